@@ -1,0 +1,210 @@
+"""Pins of the COD layout, visibility predicate and masked attention.
+
+* Brute force on every tiny layout: the label predicate equals the key sets
+  obtained from a prefix range plus a parent walk (the form the kernels use),
+  and the generator's depth-major layout equals the oracle's own loop-built
+  row labels.
+* One depth reduces to plain causal attention (torch SDPA, is_causal=True).
+* Attention through a dense T x T mask equals attention over the index sets.
+* Chunked == unchunked, bit for bit; a chunking that drops cross-chunk keys
+  does not.
+* Position counts: T = N*K and the visible-pair count in closed form at keep
+  1.0; the mean of T over seeds against N * sum_{n<D} p^n; the page's
+  rounded 2.73 against the exact 2.7731; (N*K)^2 > 4e9 at N=8192, K=8.
+* Q = 0 gives the mean of the visible V rows.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import cod as oc
+from synth import inputs as si
+
+
+def _layout(N, D, keep, loss_rate, seed, heads=(4, 2, 8), dtype="f32"):
+    return si.cod_case(N, D, keep, loss_rate, seed, heads=heads, dtype=dtype)
+
+
+def _index_sets(L):
+    """Keys by prefix range over group 0 plus a walk up the parent links."""
+    sets = []
+    for t in range(L["T"]):
+        s, d = int(L["start"][t]), int(L["depth"][t])
+        keys = set(range(0, s + 1))            # group 0 row j holds start j
+        r = t
+        for _ in range(d):
+            keys.add(r)
+            r = int(L["parent"][r])
+        assert r == -1 or d == 0
+        sets.append(keys)
+    return sets
+
+
+def test_predicate_vs_index_sets_all_tiny_layouts():
+    n_cases = 0
+    for N in range(1, 6):
+        for D in range(1, 5):
+            for bits in itertools.product([False, True], repeat=N):
+                for keep in (0.5, 1.0):
+                    L = _layout(N, D, keep, 0.0, 11)
+                    # overwrite the drawn loss mask with every pattern
+                    L = _relayout(np.array(bits), L["U"], keep, D)
+                    sets = _index_sets(L)
+                    for t in range(L["T"]):
+                        vis = oc.visible(L["start"][t], L["depth"][t], L["start"], L["depth"])
+                        assert set(np.nonzero(vis)[0].tolist()) == sets[t]
+                    n_cases += 1
+    assert n_cases > 400
+
+
+def _relayout(loss_mask, U, keep, D):
+    """Rebuild a generator-format layout for a given loss mask, reusing U."""
+    N = len(loss_mask)
+    starts = [np.arange(N)]
+    alive = loss_mask.copy()
+    for e in range(1, D):
+        alive = alive & (U[:, e - 1] < keep)
+        starts.append(np.nonzero(alive)[0])
+    off = np.concatenate([[0], np.cumsum([len(s) for s in starts])])
+    start = np.concatenate(starts)
+    depth = np.concatenate([np.full(len(s), e) for e, s in enumerate(starts)])
+    parent = np.full(len(start), -1)
+    for e in range(2, D):
+        parent[off[e]:off[e + 1]] = off[e - 1] + np.searchsorted(starts[e - 1], starts[e])
+    return dict(start=start, depth=depth, parent=parent, T=len(start))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_generator_layout_matches_oracle_rows(seed):
+    L = _layout(40, 5, 0.7, 0.5, seed)
+    rows = oc.cod_rows(L["loss_mask"], L["U"], 0.7, 5)
+    assert list(zip(L["start"].tolist(), L["depth"].tolist())) == rows
+    sets = _index_sets(L)
+    for t in range(L["T"]):
+        vis = oc.visible(L["start"][t], L["depth"][t], L["start"], L["depth"])
+        assert set(np.nonzero(vis)[0].tolist()) == sets[t]
+
+
+def test_count_closed_form_per_query():
+    L = _layout(300, 6, 0.6, 0.5, 9)
+    cnt, _ = oc.index_stats(L["start"], L["depth"])
+    np.testing.assert_array_equal(cnt, L["start"] + 1 + L["depth"])
+
+
+def test_single_depth_is_causal_attention():
+    g = np.random.default_rng(2)
+    N, Hq, Hkv, Dh = 37, 4, 2, 16
+    q = g.standard_normal((N, Hq, Dh))
+    k = g.standard_normal((N, Hkv, Dh))
+    v = g.standard_normal((N, Hkv, Dh))
+    start = np.arange(N)
+    depth = np.zeros(N, int)
+    out, _ = oc.attention(q, k, v, start, depth)
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2)[None], torch.from_numpy(k).permute(1, 0, 2)[None],
+        torch.from_numpy(v).permute(1, 0, 2)[None], is_causal=True, enable_gqa=True)
+    np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_dense_mask_attention_equals_index_attention():
+    L = _layout(23, 4, 0.7, 0.6, 5)
+    T = L["T"]
+    g = np.random.default_rng(3)
+    q = g.standard_normal((T, 4, 8))
+    k = g.standard_normal((T, 2, 8))
+    v = g.standard_normal((T, 2, 8))
+    out, lse = oc.attention(q, k, v, L["start"], L["depth"])
+    # dense T x T boolean mask built from the parent-walk sets, then SDPA
+    sets = _index_sets(L)
+    M = np.zeros((T, T), bool)
+    for t, s in enumerate(sets):
+        M[t, list(s)] = True
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2)[None], torch.from_numpy(k).permute(1, 0, 2)[None],
+        torch.from_numpy(v).permute(1, 0, 2)[None], attn_mask=torch.from_numpy(M)[None, None],
+        enable_gqa=True)
+    np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-14)
+    # lse: log sum_k exp(s) from the dense scores
+    s = np.einsum("thd,khd->thk", q, np.repeat(k, 2, axis=1)) / np.sqrt(8)
+    s = np.where(M[:, None, :], s, -np.inf)
+    np.testing.assert_allclose(lse, np.log(np.exp(s).sum(-1)), rtol=1e-12)
+
+
+def test_chunked_equals_unchunked_bitwise():
+    L = _layout(32, 4, 1.0, 1.0, 1)   # 4 groups of 32 rows, 8 chunks of 16
+    T = L["T"]
+    g = np.random.default_rng(8)
+    q = g.standard_normal((T, 4, 8))
+    k = g.standard_normal((T, 2, 8))
+    v = g.standard_normal((T, 2, 8))
+    a, la = oc.attention(q, k, v, L["start"], L["depth"])
+    b, lb = oc.attention_chunked(q, k, v, L["start"], L["depth"], 16)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    # a partition that loses the keys of earlier chunks is not the same
+    wrong = []
+    for c0 in range(0, T, 16):
+        sl = slice(c0, c0 + 16)
+        o, _ = oc.attention(q[sl], k[sl], v[sl], L["start"][sl], L["depth"][sl])
+        wrong.append(o)
+    assert not np.allclose(np.concatenate(wrong), a)
+
+
+def test_keep_one_counts_exact():
+    N, K = 64, 8
+    L = _layout(N, K, 1.0, 1.0, 0)
+    assert L["T"] == N * K
+    cnt, _ = oc.index_stats(L["start"], L["depth"])
+    assert int(cnt.sum()) == K * N * (N + 1) // 2 + N * K * (K - 1) // 2
+
+
+def test_long_sequence_counts():
+    L = si.cod_config(4, draw_qkv=False)
+    N, K = 8192, 8
+    assert L["T"] == 65536
+    assert (N * K) ** 2 == 4294967296 > 4e9
+    # visible pairs from the per-query closed form (start + 1 + depth),
+    # itself pinned by brute force above, against the summed formula
+    pairs = int(np.sum(L["start"].astype(np.int64) + 1 + L["depth"]))
+    assert pairs == K * N * (N + 1) // 2 + N * K * (K - 1) // 2 == 268697600
+
+
+def test_position_count_statistics():
+    p, D, N = 0.7, 5, 4096
+    exact = sum(p ** n for n in range(D))
+    assert abs(exact - 2.7731) < 1e-12
+    assert abs(exact - 2.73) / exact < 0.016              # the page's rounded figure
+    EL = sum(p ** e for e in range(1, D))
+    EL2 = sum((2 * e - 1) * p ** e for e in range(1, D))
+    var = EL2 - EL ** 2
+    assert abs(var - 2.4218) < 1e-4
+    Ts = [si.cod_case(N, D, p, 1.0, 1000 + s, draw_qkv=False)["T"] for s in range(200)]
+    sigma = np.sqrt(N * var)
+    assert abs(np.mean(Ts) - N * exact) < 4 * sigma / np.sqrt(200)
+    # loss-mask-0.5 rule of the training-shaped case
+    c3 = si.cod_config(3, draw_qkv=False)
+    mean3 = N * (1 + 0.5 * EL)
+    var3 = 0.5 * EL2 - (0.5 * EL) ** 2
+    assert abs(mean3 - 7727.3) < 0.1
+    assert abs(c3["T"] - mean3) < 4 * np.sqrt(N * var3)
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    L = _layout(19, 3, 0.7, 0.7, 4)
+    T = L["T"]
+    g = np.random.default_rng(1)
+    k = g.standard_normal((T, 2, 8))
+    v = g.standard_normal((T, 2, 8))
+    out, _ = oc.attention(np.zeros((T, 4, 8)), k, v, L["start"], L["depth"])
+    for t in range(T):
+        vis = oc.visible(L["start"][t], L["depth"][t], L["start"], L["depth"])
+        mv = v[vis].mean(axis=0)
+        np.testing.assert_allclose(out[t], np.repeat(mv, 2, axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_mix64_reference_values():
+    # SplitMix64 seeded with 0 yields these first outputs (states gamma, 2*gamma, ...)
+    outs = oc.mix64(np.arange(3, dtype=np.uint64) * oc.GOLDEN_GAMMA)
+    assert [hex(int(x)) for x in outs] == ["0xe220a8397b1dcdaf", "0x6e789e6aa1b965f4", "0x6c45d188009454f"]

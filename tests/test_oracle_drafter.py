@@ -1,0 +1,141 @@
+"""Pins of the oracle's RMSNorm, fc fusion, decoder layer and LM-head argmax.
+
+RMSNorm: its closed form (unit-gain output has RMS sqrt(ms/(ms+eps))), scale
+invariance, and torch.nn.functional.rms_norm in fp64.  Layer: a composition
+of torch fp64 CPU ops (rms_norm, linear, scaled_dot_product_attention with a
+boolean mask and GQA, silu).  Argmax: numpy's first maximum, including ties
+across the oracle's vocabulary slices.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import batch as ob
+from oracle import drafter as od
+from synth import inputs as si
+
+
+def test_rmsnorm_closed_form_and_scale_invariance():
+    g = np.random.default_rng(0)
+    x = g.standard_normal((5, 96)) * 0.7
+    eps = 1e-6
+    y = od.rmsnorm(x, np.ones(96), eps)
+    ms = np.mean(x * x, axis=1)
+    rms_y = np.sqrt(np.mean(y * y, axis=1))
+    np.testing.assert_allclose(rms_y, np.sqrt(ms / (ms + eps)), rtol=1e-12)
+    y3 = od.rmsnorm(3.0 * x, np.ones(96), eps)
+    assert np.max(np.abs(y3 - y)) < 1e-5
+
+
+def test_rmsnorm_matches_torch():
+    g = np.random.default_rng(1)
+    x = g.standard_normal((7, 128))
+    w = g.uniform(0.5, 1.5, 128)
+    ref = F.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(w), eps=1e-6).numpy()
+    np.testing.assert_allclose(od.rmsnorm(x, w, 1e-6), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_bf16_decode_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0001, 0x7F7F, 0x4049], np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(od.bf16_to_f64(bits), ref)
+
+
+def _tiny_case(seed=3, R=3, K=3, dtype="f32"):
+    dims = si.DrafterDims(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, ffn=96,
+                          vocab=300, dtype=dtype)
+    W = si.drafter_weights(dims, seed, random_gains=True)
+    c = si.decode_case(dims, seed, R, K, W=[4, 0, 5][:R], kv_len=[3, 7, 0][:R], n_rej=[1, 0, 2][:R])
+    b = ob.build_draft_batch(K, dims.mask_token_id, c["cu_window"], c["n_rej"], c["kv_len"],
+                             c["kv_base"], c["window_ids"], c["window_pos"], c["window_hrow"],
+                             c["new_token"], c["ctx_hrow"], c["target_hidden"], W["h_shared"])
+    return dims, W, c, b
+
+
+def _torch_layer_reference(dims, W, c, b):
+    """The same layer assembled from torch fp64 ops, one request at a time."""
+    T = torch.float64
+    d, Hq, Hkv, Dh = dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    w = {k: torch.from_numpy(od.to_f64(W[k], dims.dtype)) for k in
+         ("w_fc", "w_qkv", "w_o", "w_gate", "w_up", "w_down", "embed", "w_lm")}
+    g = {k: torch.from_numpy(np.asarray(W[k], np.float64)) for k in
+         ("stream_gain", "attn_gain", "mlp_gain", "final_gain")}
+    hid = torch.from_numpy(od.to_f64(b["draft_hidden"], dims.dtype))
+    u = torch.cat([F.rms_norm(hid[:, s], (d,), g["stream_gain"][s], eps=dims.eps) for s in range(3)], 1)
+    x0 = F.embedding(torch.from_numpy(b["draft_ids"].astype(np.int64)), w["embed"]) + F.linear(u, w["w_fc"])
+    kc = torch.from_numpy(od.to_f64(c["k_cache"].view(np.uint16) if dims.dtype == "bf16" else c["k_cache"], dims.dtype)).clone()
+    vc = torch.from_numpy(od.to_f64(c["v_cache"].view(np.uint16) if dims.dtype == "bf16" else c["v_cache"], dims.dtype)).clone()
+    live = torch.from_numpy(b["rejected"] == 0)
+    a = F.rms_norm(x0, (d,), g["attn_gain"], eps=dims.eps)
+    qkv = F.linear(a, w["w_qkv"])
+    q = qkv[:, :Hq * Dh].reshape(-1, Hq, Dh)
+    k = qkv[:, Hq * Dh:(Hq + Hkv) * Dh].reshape(-1, Hkv, Dh)
+    v = qkv[:, (Hq + Hkv) * Dh:].reshape(-1, Hkv, Dh)
+    sl = torch.from_numpy(b["slot_mapping"].astype(np.int64))
+    kc[sl[live]] = k[live]
+    vc[sl[live]] = v[live]
+    kc = torch.nan_to_num(kc, nan=0.0)   # unwritten rows are masked out below
+    vc = torch.nan_to_num(vc, nan=0.0)
+    o = torch.zeros(len(x0), Hq, Dh, dtype=T)
+    for r in range(c["R"]):
+        rows = [t for t in range(b["T"]) if b["req_of_row"][t] == r and b["rejected"][t] == 0]
+        base = int(c["kv_base"][r])
+        cap = (int(c["kv_base"][r + 1]) if r + 1 < c["R"] else c["kv_rows"]) - base
+        pos = torch.tensor([int(b["draft_pos"][t]) for t in rows])
+        mask = torch.arange(cap)[None, :] <= pos[:, None]
+        qq = q[rows].permute(1, 0, 2)[None]
+        kk = kc[base:base + cap].permute(1, 0, 2)[None]
+        vv = vc[base:base + cap].permute(1, 0, 2)[None]
+        oo = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask[None, None], enable_gqa=True)
+        o[rows] = oo[0].permute(1, 0, 2)
+    x1 = x0 + F.linear(o.reshape(-1, Hq * Dh), w["w_o"])
+    bb = F.rms_norm(x1, (d,), g["mlp_gain"], eps=dims.eps)
+    x2 = x1 + F.linear(F.silu(F.linear(bb, w["w_gate"])) * F.linear(bb, w["w_up"]), w["w_down"])
+    qr = torch.from_numpy(b["query_rows"].astype(np.int64))
+    f = F.rms_norm(x2[qr], (d,), g["final_gain"], eps=dims.eps)
+    z = F.linear(f, w["w_lm"])
+    return x0.numpy(), x2.numpy(), z.numpy(), kc.numpy(), live.numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_matches_torch_composition(dtype):
+    dims, W, c, b = _tiny_case(dtype=dtype)
+    res = od.drafter_forward(dims, W, b, c["kv_base"], c["k_cache"], c["v_cache"])
+    x0, x2, z, kc, live = _torch_layer_reference(dims, W, c, b)
+    np.testing.assert_allclose(res["x0"][live], x0[live], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(res["x_query"], x2[b["query_rows"]], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(res["logits"], z, rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(res["tokens"], np.argmax(z, axis=1))
+    written = b["slot_mapping"][live]
+    np.testing.assert_allclose(res["k_cache"][written], kc[written], rtol=1e-12, atol=1e-13)
+
+
+def test_sentinel_rows_untouched_and_unread():
+    dims, W, c, b = _tiny_case(dtype="bf16")
+    res = od.drafter_forward(dims, W, b, c["kv_base"], c["k_cache"], c["v_cache"])
+    assert np.all(np.isfinite(res["x_query"]))   # no query read a sentinel row
+    live = b["slot_mapping"][b["rejected"] == 0]
+    untouched = np.setdiff1d(np.arange(c["kv_rows"]), live)
+    cached = np.concatenate([np.arange(c["kv_base"][r], c["kv_base"][r] + c["kv_len"][r]) for r in range(c["R"])])
+    sentinel_rows = np.setdiff1d(untouched, cached)
+    assert len(sentinel_rows) == int(np.sum(c["n_rej"]))
+    assert np.all(np.isnan(res["k_cache"][sentinel_rows]))
+
+
+def test_argmax_ties_and_slices():
+    """Integer logits (x = +-1 so RMSNorm with eps=0 is exact, integer W_lm)
+    give exact ties, many of them across the oracle's vocabulary slices."""
+    g = np.random.default_rng(4)
+    d, V = 8, 700
+    w = g.integers(-3, 4, (V, d)).astype(np.float64)
+    x = g.choice([-1.0, 1.0], (6, d))
+    tok, gap, logits = od.lm_head_argmax(x, np.ones(d), w, 0.0, dtype="f64", chunk=128)
+    z = x @ w.T
+    np.testing.assert_array_equal(logits, z)
+    np.testing.assert_array_equal(tok, np.argmax(z, axis=1))     # first maximum
+    srt = np.sort(z, axis=1)
+    np.testing.assert_array_equal(gap, srt[:, -1] - srt[:, -2])
+    assert np.any(gap == 0.0)
+    for i in range(len(x)):
+        assert tok[i] == np.nonzero(z[i] == z[i].max())[0][0]
