@@ -1,0 +1,227 @@
+"""Benchmark of the parallel-drafting hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+A step is one drafter forward predicting all K=7 draft tokens of the decode
+step with c=1 (2,048-position KV cache, d=2880, 64 q / 8 kv heads x 64,
+SwiGLU 8192, vocab 201,088, bf16): pe_build_draft_batch -> pe_fuse_hidden ->
+pe_draft_layer -> pe_lm_head_argmax, inputs resident in HBM.  The headline
+value is draft positions per second (7 per step).  The JSON line also
+carries the roofline of the dominant kernel (the LM-head weight stream),
+the fp64 oracle's CPU rate on the same workload, and secondary measurements:
+the c=64 decode step and the training-shaped COD / parallel-group attention.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the c=64 decode and attention measurements")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_loop(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms
+
+
+def decode_bytes(dims, case, T, RK):
+    """Algorithmic HBM bytes of one decode step: every weight once, the KV
+    rows the queries read, the K/V rows written, the hidden rows read and
+    copied, the embedding rows, and the activations in and out."""
+    import numpy as np
+    e = 2 if dims.dtype == "bf16" else 4
+    d, F, V = dims.hidden, dims.ffn, dims.vocab
+    qc = dims.n_q_heads * dims.head_dim
+    kvc = dims.n_kv_heads * dims.head_dim
+    weights = (d * 3 * d + dims.qkv_rows * d + d * qc + 2 * F * d + d * F + V * d) * e
+    W = np.diff(case["cu_window"])
+    n_acc = W - case["n_rej"]
+    keys = int(np.sum(case["kv_len"].astype(np.int64) + n_acc + case["K"]))   # rows read per kv head
+    live = int(np.sum(n_acc)) + RK
+    kv = keys * 2 * kvc * e + live * 2 * kvc * e
+    hidden = T * 3 * d * e * 3                     # target rows read, draft rows written, read by the norm
+    emb = T * d * e
+    act = T * d * 4 + RK * d * 4 + RK * 4
+    return weights + kv + hidden + emb + act, weights
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from drafter_pe_build_amd import _lib as L
+    from drafter_pe_build_amd.step import DraftStep, GraphStep, to_device
+    from synth import inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    dims = si.GPTOSS_DIMS
+    log("generating the c=1 decode inputs and the drafter weights")
+    t0 = time.time()
+    W = si.drafter_weights(dims, 1)
+    _, _, case1 = si.decode_config(1, with_weights=False)
+    log("  %.1f s" % (time.time() - t0))
+    st = DraftStep(dims, W, case1)
+    RK = st.R * st.K
+    ms_eager = time_loop(st.run, args.steps, args.warmup, stream)
+    log("c=1 step, eager launches: %.1f us" % (ms_eager * 1e3))
+    gs = GraphStep(st)
+    ms = time_loop(gs.replay, args.steps, args.warmup, stream)
+    step_bytes, weight_bytes = decode_bytes(dims, case1, st.T, RK)
+    log("c=1 step, one graph replay: %.1f us" % (ms * 1e3))
+
+    # dominant kernel: the LM-head stage (final RMSNorm rows, then the W_lm
+    # stream with the fused argmax), replayed from its own graph
+    lm_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(lm_graph):
+        st.lm_head(False)
+    lm_ms = time_loop(lm_graph.replay, args.steps, args.warmup, stream)
+    lm_bytes = dims.vocab * dims.hidden * 2 + RK * dims.hidden * (4 + 2 + 2)
+    lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
+    log("LM head stage: %.1f us, %.0f GB/s" % (lm_ms * 1e3, lm_gbs))
+
+    result = {
+        "metric": "draft positions/sec per drafter fwd",
+        "value": RK / (ms * 1e-3),
+        "unit": "draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "eager_ms_per_step": ms_eager,
+        "launch": "one HIP graph replay of the four stage calls (eager launches reported beside)",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) cache, scaled hidden streams)",
+        "config": {"workload": "decode step c=1, K=7 draft slots, 2048-position KV cache, d=2880, "
+                               "64q/8kv x 64, SwiGLU 8192, vocab 201088",
+                   "requests": 1, "draft_slots": 7, "cache_positions": 2048},
+        "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
+        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "kernel": "LM head stage (final RMSNorm + W_lm stream with fused argmax)",
+                     "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "launch_us": lm_ms * 1e3, "algorithmic_bytes": lm_bytes},
+    }
+    del gs, lm_graph, st
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra = {}
+        log("c=64 decode step")
+        _, _, case2 = si.decode_config(2, with_weights=False)
+        st2 = DraftStep(dims, W, case2)
+        RK2 = st2.R * st2.K
+        gs2 = GraphStep(st2)
+        ms2 = time_loop(gs2.replay, max(5, args.steps // 5), 3, stream)
+        b2, _ = decode_bytes(dims, case2, st2.T, RK2)
+        live2 = int(np.sum(np.diff(case2["cu_window"]) - case2["n_rej"])) + RK2
+        fl2 = 2.0 * (live2 * (3 * dims.hidden * dims.hidden + dims.qkv_rows * dims.hidden)
+                     + RK2 * (dims.hidden * dims.n_q_heads * dims.head_dim + 3 * dims.ffn * dims.hidden
+                              + dims.vocab * dims.hidden))
+        extra["decode_c64"] = {"ms_per_step": ms2, "draft_positions_per_s": RK2 / (ms2 * 1e-3),
+                               "hbm_gbs": b2 / (ms2 * 1e-3) / 1e9, "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "gemm_tflops": fl2 / (ms2 * 1e-3) / 1e12,
+                               "mfma_frac": fl2 / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        log("  %.1f us" % (ms2 * 1e3))
+        del gs2, st2
+        torch.cuda.empty_cache()
+        for cfg, name in ((3, "cod_attention_n4096"), (4, "group_attention_n8192_chunked")):
+            log("attention config %d" % cfg)
+            Lay = si.cod_config(cfg)
+            T = Lay["T"]
+            Hq, Hkv, Dh = Lay["heads"]
+            q, k, v = (to_device(Lay[n], "cuda") for n in ("q", "k", "v"))
+            start = to_device(Lay["start"].astype(np.int32), "cuda")
+            depth = to_device(Lay["depth"].astype(np.int32), "cuda")
+            parent = to_device(Lay["parent"].astype(np.int32), "cuda")
+            selfr = to_device(np.arange(T, dtype=np.int32), "cuda")
+            base = torch.zeros(1, dtype=torch.int32, device="cuda")
+            out = torch.empty((T, Hq, Dh), dtype=torch.bfloat16, device="cuda")
+            chunks = [(0, T)] if cfg == 3 else [(8192 * c, 8192 * (c + 1)) for c in range(8)]
+            arglist = [L.attn_args(num_q=c1 - c0, num_seg=1, q_per_seg=c1 - c0, num_kv_rows=T, n_q_heads=Hq,
+                                   n_kv_heads=Hkv, head_dim=Dh, scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16,
+                                   q=q[c0:c1], q_row_stride=Hq * Dh, k=k, v=v, seg_kv_base=base,
+                                   q_start=start[c0:c1], q_depth=depth[c0:c1], q_self_row=selfr[c0:c1],
+                                   kv_parent=parent, max_prefix=Lay["N"], out=out[c0:c1]) for c0, c1 in chunks]
+            ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+            def run_attn():
+                for a in arglist:
+                    L.pe_draft_attention(a, "cuda", workspace=ws)
+
+            msa = time_loop(run_attn, max(5, args.steps // 5), 2, stream)
+            pairs = int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
+            fl = pairs * Hq * 4 * Dh
+            extra[name] = {"T": T, "ms": msa, "positions_per_s": T / (msa * 1e-3), "visible_pairs": pairs,
+                           "tflops": fl / (msa * 1e-3) / 1e12,
+                           "mfma_frac": fl / (msa * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "launches": len(chunks)}
+            log("  %.1f us, %.0f TFLOP/s" % (msa * 1e3, fl / (msa * 1e-3) / 1e12))
+            del q, k, v, out
+            torch.cuda.empty_cache()
+        result["secondary"] = extra
+
+    if not args.no_cpu:
+        log("oracle CPU baseline (one full c=1 step in fp64)")
+        ncores = len(os.sched_getaffinity(0))
+        try:
+            from threadpoolctl import threadpool_info
+            blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+            if blas:
+                ncores = max(blas)
+        except Exception:
+            pass
+        from oracle import batch as ob
+        from oracle import drafter as od
+        t0 = time.time()
+        b = ob.build_draft_batch(case1["K"], dims.mask_token_id, case1["cu_window"], case1["n_rej"],
+                                 case1["kv_len"], case1["kv_base"], case1["window_ids"], case1["window_pos"],
+                                 case1["window_hrow"], case1["new_token"], case1["ctx_hrow"],
+                                 case1["target_hidden"], W["h_shared"])
+        od.drafter_forward(dims, W, b, case1["kv_base"], case1["k_cache"], case1["v_cache"], keep_logits=False)
+        tc = time.time() - t0
+        result["cpu_baseline"] = {"value": RK / tc, "unit": "draft positions/s", "cores": ncores, "kind": "oracle",
+                                  "sample": "one full c=1 decode step (7 draft positions), fp64 numpy, %.1f s" % tc}
+        log("  %.1f s" % tc)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,76 @@
+// Stage 1: draft-batch construction in one pass.
+//
+// "P-EAGLE: parallel speculative decoding in vLLM", sections "fused Triton
+// kernel" and "hidden-state management": one kernel copies the previous ids
+// and positions, inserts the new token, MASK-fills the parallel slots, emits
+// the rejected / masked flags and the hidden-state mapping, and copies the
+// hidden rows (target rows to their new positions, h_shared into every MASK
+// slot).  Section "KV cache": rejected rows get PADDING_SLOT_ID (-1).
+//
+// One workgroup per draft row: thread 0 finds the row's request by binary
+// search over cu_window (row r's request segment starts at cu_window[r] + r*K),
+// writes the integer metadata, and the whole workgroup streams the row's
+// 3*hidden hidden values with 16-byte loads and stores.
+#include "kernels.h"
+
+namespace pe {
+
+__global__ __launch_bounds__(256) void build_draft_batch_kernel(BatchParams p) {
+  __shared__ int s_src;   // hidden source row, -1 = h_shared, -2 = none
+  const int t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    // largest r with cu_window[r] + r*K <= t
+    int lo = 0, hi = p.R - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.cu_window[mid] + mid * p.K <= t) lo = mid; else hi = mid - 1;
+    }
+    const int r = lo;
+    const int w0 = p.cu_window[r];
+    const int W = p.cu_window[r + 1] - w0;
+    const int first = w0 + r * p.K;
+    const int j = t - first;
+    const int nrej = min(max(p.n_rej[r], 0), max(W, 0));
+    const int n_acc = W - nrej;
+    const int base = p.kv_base[r];
+    int id, pos, slot, src;
+    uint8_t rej = 0, msk = 0;
+    if (j < W) {
+      const int w = w0 + j;
+      id = p.window_ids[w];
+      pos = p.window_pos[w];
+      src = p.window_hrow[w];
+      if (j >= n_acc) { rej = 1; slot = -1; } else { slot = base + pos; }
+    } else {
+      const int k = j - W;
+      pos = p.kv_len[r] + n_acc + k;
+      slot = base + pos;
+      if (k == 0) { id = p.new_token[r]; src = p.ctx_hrow[r]; }
+      else { id = p.mask_token_id; src = -1; msk = 1; }
+      if (k < p.K) p.query_rows[r * p.K + k] = t;
+    }
+    if (j == 0) p.cu_draft[r] = t;
+    if (t == p.T - 1) p.cu_draft[p.R] = p.T;
+    p.draft_ids[t] = id;
+    p.draft_pos[t] = pos;
+    p.slot_mapping[t] = slot;
+    p.hidden_src[t] = src;
+    p.req_of_row[t] = r;
+    p.rejected[t] = rej;
+    p.masked[t] = msk;
+    s_src = (src >= p.target_rows) ? -2 : (src < -1 ? -2 : src);
+  }
+  __syncthreads();
+  const int src = s_src;
+  if (src == -2) return;
+  const char* from = (src < 0) ? reinterpret_cast<const char*>(p.h_shared)
+                               : reinterpret_cast<const char*>(p.target_hidden) + (int64_t)src * p.row_bytes;
+  char* to = reinterpret_cast<char*>(p.draft_hidden) + (int64_t)t * p.row_bytes;
+  for (int c = threadIdx.x; c < p.row_bytes / 16; c += blockDim.x) st16(to + 16 * c, ld16(from + 16 * c));
+}
+
+void launch_build_draft_batch(const BatchParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(build_draft_batch_kernel, dim3(p.T), dim3(256), 0, s, p);
+}
+
+}  // namespace pe

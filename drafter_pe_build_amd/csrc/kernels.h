@@ -1,0 +1,111 @@
+// Parameter blocks and launchers of the gfx950 kernels (internal to libpe).
+#pragma once
+#include "common.h"
+
+namespace pe {
+
+struct BatchParams {
+  int R, K, T, target_rows, mask_token_id;
+  int row_bytes;  // 3 * hidden * element size (multiple of 16)
+  const int32_t *cu_window, *n_rej, *kv_len, *kv_base, *window_ids, *window_pos,
+      *window_hrow, *new_token, *ctx_hrow;
+  const void *target_hidden, *h_shared;
+  int32_t *draft_ids, *draft_pos, *slot_mapping, *hidden_src, *req_of_row, *query_rows, *cu_draft;
+  uint8_t *rejected, *masked;
+  void* draft_hidden;
+};
+void launch_build_draft_batch(const BatchParams& p, hipStream_t s);
+
+struct NormParams {
+  const void* in;
+  int64_t ld_in;         // elements between input rows
+  const int32_t* rows;   // [n] source rows or nullptr (identity)
+  const uint8_t* skip;   // flags indexed by source row, or nullptr
+  int n, segs, d;        // rows, segments per row, segment length
+  const float* gain;     // [segs * d]
+  float eps;
+  void* out;
+  int64_t ld_out;
+  int* zero;             // counters cleared by the launch (block 0), or nullptr
+  int nzero;
+};
+// Row count limit of one segment: 8 x 256 sixteen-byte chunks per row.
+constexpr int kNormMaxChunks = 8;
+void launch_rmsnorm_rows(const NormParams& p, int in_bf16, int out_bf16, hipStream_t s);
+
+// GEMM epilogues.  The product Y[m][n] = sum_k X[m][k] W[n][k] of output row m
+// (an X row) and feature n (a W row) is finished by one of these.
+enum EpiKind {
+  EPI_FC = 0,      // out_f32[m][n] = y + embed[ids[m]][n]; rows with rejected[m] skipped
+  EPI_QKV = 1,     // n < q_cols: q_out[m][n] = y; then k, v columns go to the
+                   // caches at slots[m] (skipped when slots[m] < 0)
+  EPI_RESID = 2,   // out_f32[m][n] = y + res[res_rows ? res_rows[m] : m][n]
+  EPI_SWIGLU = 3,  // out_s[m][n] = silu(y_gate) * y_up
+  EPI_ARGMAX = 4   // running (max, lowest index) per row; optional logits
+};
+
+struct Epi {
+  int kind;
+  float* out_f32;
+  int64_t ld_out;
+  void* out_s;
+  const void* embed;
+  const int32_t* ids;
+  const uint8_t* rejected;
+  const float* res;
+  const int32_t* res_rows;
+  int64_t ld_res;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slots;
+  int q_cols, kv_cols, kv_rows;
+  int embed_rows;
+  float* logits;         // argmax: optional [M, N]
+  float* part_val;       // argmax: [P, M] partial maxima
+  int32_t* part_idx;     // argmax: [P, M] their indices
+};
+
+struct GemmParams {
+  const void* X;
+  int64_t ldx;
+  const void* W;
+  const void* W2;  // second weight matrix of EPI_SWIGLU (up), else nullptr
+  int M, N, K;
+  const void* xzero;  // M <= 16: >= K zeroed elements, 16-byte aligned (padding rows of X)
+  Epi epi;
+};
+
+// Packs a row-major [N, row_bytes] matrix into the matrix-core-ready layout
+// streamed by the GEMM kernels (see gemm.hip).
+void launch_pack(const void* src, void* dst, int N, int row_bytes, hipStream_t s);
+// Chooses the weight-streaming kernel (M <= 16) or the LDS-tiled kernel.
+// W (and W2) are packed weights.
+// EPI_ARGMAX returns the number of partial rows P to reduce with
+// launch_argmax_reduce; every other kind returns 0.
+int launch_gemm(const GemmParams& p, int bf16, hipStream_t s);
+// Upper bound of P for an argmax GEMM of this shape.
+int gemm_argmax_partials(int M, int N);
+
+void launch_argmax_reduce(const float* pv, const int32_t* pi, int P, int M, int32_t* tokens, hipStream_t s);
+
+struct AttnParams {
+  const void* q;
+  int64_t q_stride;
+  const int32_t* q_rows;
+  int meta_by_row;  // per-query metadata indexed by q_rows[i] instead of i
+  const void *k, *v;
+  int num_q, num_seg, q_per_seg, num_kv_rows, Hq, Hkv;
+  float scale, scale_log2;
+  const int32_t *seg_kv_base, *q_start, *q_depth, *q_self_row, *kv_parent;
+  int n_splits, split_len;
+  void* out;
+  float* lse;
+  int64_t* dbg_count;
+  uint64_t* dbg_hash;
+  float* part_o;       // [n_splits, num_q*Hq, Dh]
+  float* part_ml;      // [n_splits, num_q*Hq, 2]
+  uint64_t* part_dbg;  // [n_splits, num_q*Hkv, 2]
+};
+void launch_attention(const AttnParams& p, int bf16, int head_dim, hipStream_t s);
+
+}  // namespace pe

@@ -1,0 +1,110 @@
+"""Host-only checks of libpe.so: it loads, exports every function include/pe.h
+declares, and rejects bad arguments before launching anything (no GPU needed:
+every call below fails validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from drafter_pe_build_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libpe.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"pe_build_draft_batch", "pe_fuse_hidden", "pe_draft_attention", "pe_draft_layer",
+            "pe_lm_head_argmax"} <= set(names)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(L.EXPORTS)
+
+
+def test_version_and_status_strings():
+    lib = L.lib()
+    assert lib.pe_version().decode().startswith("pe ")
+    assert lib.pe_status_string(1) == b"PE_ERR_INVALID_ARG"
+    assert lib.pe_status_string(2) == b"PE_ERR_UNSUPPORTED"
+
+
+def _dims(**kw):
+    base = dict(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=512, vocab=4096, mask_token_id=4095,
+                eps=1e-6, dtype="f32")
+    base.update(kw)
+    return L.dims_struct(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def test_dims_validation_codes():
+    lib = L.lib()
+    n = ctypes.c_size_t()
+    ok = _dims()
+    assert lib.pe_fuse_hidden_workspace(ctypes.byref(ok), 10, ctypes.byref(n)) == 0
+    assert n.value >= 10 * 3 * 256 * 4
+    cases = [(dict(head_dim=96), 2), (dict(n_kv_heads=3), 1), (dict(hidden=200), 2),
+             (dict(mask_token_id=4096), 1), (dict(eps=-1.0), 1), (dict(vocab=0), 1),
+             (dict(n_q_heads=128, n_kv_heads=1), 2), (dict(hidden=272, dtype="bf16"), 2)]
+    for kw, code in cases:
+        d = _dims(**kw)
+        assert lib.pe_fuse_hidden_workspace(ctypes.byref(d), 10, ctypes.byref(n)) == code, kw
+    assert lib.pe_fuse_hidden_workspace(ctypes.byref(ok), -1, ctypes.byref(n)) == 1
+
+
+def test_entry_points_reject_before_launch():
+    lib = L.lib()
+    d = _dims()
+    w = L.PeWeights()
+    b = L.PeBatchOut()
+    # batch build: R = 0, then a NULL output buffer
+    args = [ctypes.byref(d), 0, 4, 0, 1] + [FAKE] * 11 + [ctypes.byref(b), None]
+    assert lib.pe_build_draft_batch(*args) == 1
+    args = [ctypes.byref(d), 1, 4, 0, 1] + [FAKE] * 11 + [ctypes.byref(b), None]
+    assert lib.pe_build_draft_batch(*args) == 1
+    # misaligned hidden pointer
+    b2 = L.PeBatchOut(*([FAKE] * 9 + [ctypes.c_void_p(0x1004)]))
+    args = [ctypes.byref(d), 1, 4, 0, 1] + [FAKE] * 11 + [ctypes.byref(b2), None]
+    assert lib.pe_build_draft_batch(*args) == 1
+    # fuse: missing weights, then workspace too small
+    assert lib.pe_fuse_hidden(ctypes.byref(d), ctypes.byref(w), 8, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    w2 = L.PeWeights(*([FAKE] * 12))
+    assert lib.pe_fuse_hidden(ctypes.byref(d), ctypes.byref(w2), 8, FAKE, None, FAKE, FAKE, FAKE, 16, None) == 1
+    # layer: more queries than rows
+    assert lib.pe_draft_layer(ctypes.byref(d), ctypes.byref(w2), 3, 1, 4, FAKE, ctypes.byref(b2), FAKE, FAKE, FAKE,
+                              10, 10, FAKE, FAKE, 1 << 30, None) == 1
+    # lm head: workspace too small
+    assert lib.pe_lm_head_argmax(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, FAKE, None, FAKE, 16, None) == 1
+    # empty inputs are valid no-ops
+    assert lib.pe_fuse_hidden(ctypes.byref(d), ctypes.byref(w), 0, None, None, None, None, None, 0, None) == 0
+    assert lib.pe_lm_head_argmax(ctypes.byref(d), ctypes.byref(w), 0, None, None, None, None, 0, None) == 0
+
+
+def test_attention_validation_and_workspace():
+    lib = L.lib()
+    n = ctypes.c_size_t()
+    a = L.attn_args(num_q=7, num_seg=1, q_per_seg=7, num_kv_rows=2055, n_q_heads=64, n_kv_heads=8, head_dim=64,
+                    scale=0.125, dtype=L.PE_BF16, q=FAKE, q_row_stride=4096, k=FAKE, v=FAKE, seg_kv_base=FAKE,
+                    q_start=FAKE, out=FAKE, max_prefix=2055)
+    assert lib.pe_draft_attention_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value > 7 * 64 * 64 * 4            # decode shape is split over the cache
+    bad = [dict(num_q=8), dict(head_dim=80), dict(n_kv_heads=7), dict(q_row_stride=100), dict(scale=0.0),
+           dict(q=ctypes.c_void_p(0x1002)), dict(q_depth=FAKE)]
+    for kw in bad:
+        a2 = L.attn_args(**{**dict(num_q=7, num_seg=1, q_per_seg=7, num_kv_rows=2055, n_q_heads=64, n_kv_heads=8,
+                                    head_dim=64, scale=0.125, dtype=L.PE_BF16, q=FAKE, q_row_stride=4096, k=FAKE,
+                                    v=FAKE, seg_kv_base=FAKE, q_start=FAKE, out=FAKE, max_prefix=2055), **kw})
+        assert lib.pe_draft_attention(ctypes.byref(a2), None, 0, None) in (1, 2), kw
+    # split path without workspace is refused
+    assert lib.pe_draft_attention(ctypes.byref(a), None, 0, None) == 1

@@ -1,0 +1,235 @@
+"""GPU parity of pe_draft_attention (COD layout and decode regions) against the oracle.
+
+* Outputs and LSE within the tolerance of oracle.cod.attention.
+* Visible-key counts and SplitMix64 hashes bit-exact against
+  oracle.cod.index_stats (they come from the kernel's own masking loop).
+* Chunked (query chunks) == unchunked, bit for bit, on small layouts and on
+  the N=8192, K=8 long-sequence case.
+* The training-shaped N=4096 COD case with every query's index stats, and
+  values on a sample of queries (every depth's first and last rows).
+* Decode-shaped segments with ragged lengths through the split-KV path,
+  plus empty queries and num_q = 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+from drafter_pe_build_amd import _lib as L
+from drafter_pe_build_amd.step import to_device
+from helpers import TOL, bits, dev_to_f64, say
+from oracle import cod as oc
+from oracle import drafter as od
+from oracle import metrics as om
+from synth import inputs as si
+
+pytestmark = pytest.mark.gpu
+
+
+class LazyRows:
+    """fp64 view of selected rows of a storage array (the oracle indexes q[t])."""
+
+    def __init__(self, arr, dtype):
+        self.arr, self.dtype, self.shape = arr, dtype, arr.shape
+
+    def __getitem__(self, t):
+        return od.to_f64(self.arr[t], self.dtype)
+
+
+def upload_layout(Lay):
+    dt = Lay["dtype"]
+    return dict(q=to_device(Lay["q"], "cuda"), k=to_device(Lay["k"], "cuda"), v=to_device(Lay["v"], "cuda"),
+                start=to_device(Lay["start"].astype(np.int32), "cuda"),
+                depth=to_device(Lay["depth"].astype(np.int32), "cuda"),
+                parent=to_device(Lay["parent"].astype(np.int32), "cuda"),
+                self_row=to_device(np.arange(Lay["T"], dtype=np.int32), "cuda"),
+                base=torch.zeros(1, dtype=torch.int32, device="cuda"), dtype=dt)
+
+
+def run_cod(D, Lay, c0=0, c1=None, out=None, lse=None, dbg=True, split_len=0):
+    T = Lay["T"]
+    c1 = T if c1 is None else c1
+    nq = c1 - c0
+    Hq, Hkv, Dh = Lay["heads"]
+    sdt = torch.bfloat16 if D["dtype"] == "bf16" else torch.float32
+    if out is None:
+        out = torch.empty((nq, Hq, Dh), dtype=sdt, device="cuda")
+    if lse is None:
+        lse = torch.empty((nq, Hq), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros((nq, Hkv), dtype=torch.int64, device="cuda") if dbg else None
+    hsh = torch.zeros((nq, Hkv), dtype=torch.int64, device="cuda") if dbg else None
+    a = L.attn_args(num_q=nq, num_seg=1, q_per_seg=nq, num_kv_rows=T, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=Dh,
+                    scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16 if D["dtype"] == "bf16" else L.PE_F32,
+                    q=D["q"][c0:c1], q_row_stride=Hq * Dh, k=D["k"], v=D["v"], seg_kv_base=D["base"],
+                    q_start=D["start"][c0:c1], q_depth=D["depth"][c0:c1], q_self_row=D["self_row"][c0:c1],
+                    kv_parent=D["parent"], max_prefix=Lay["N"], split_len=split_len, out=out, lse=lse,
+                    dbg_count=cnt, dbg_hash=hsh)
+    L.pe_draft_attention(a, "cuda")
+    return out, lse, cnt, hsh
+
+
+def check_against_oracle(Lay, out, lse, cnt, hsh, queries, name):
+    dt = Lay["dtype"]
+    tol = TOL[dt]
+    q64 = LazyRows(Lay["q"], dt)
+    k64 = od.to_f64(Lay["k"], dt)
+    v64 = od.to_f64(Lay["v"], dt)
+    ref_o, ref_l = oc.attention(q64, k64, v64, Lay["start"], Lay["depth"], queries)
+    o = dev_to_f64(out)[queries]
+    e = om.relerr(o, ref_o)
+    el = om.relerr(lse.cpu().numpy()[queries], ref_l)
+    say("  [%s] out relerr %.3g  lse relerr %.3g  (%d queries)" % (name, e, el, len(queries)))
+    assert e <= tol and el <= tol
+    if cnt is not None:
+        rc, rh = oc.index_stats(Lay["start"], Lay["depth"], queries)
+        gc = cnt.cpu().numpy()[queries]
+        gh = hsh.cpu().numpy().view(np.uint64)[queries]
+        for j in range(gc.shape[1]):
+            np.testing.assert_array_equal(gc[:, j], rc)
+            np.testing.assert_array_equal(gh[:, j], rh)
+
+
+@pytest.mark.parametrize("dtype,heads,N,D,keep,loss", [
+    ("bf16", (8, 2, 128), 150, 5, 0.7, 0.5),
+    ("bf16", (16, 4, 64), 97, 4, 0.6, 1.0),
+    ("f32", (8, 2, 128), 130, 5, 0.7, 0.5),
+    ("f32", (4, 4, 64), 70, 3, 1.0, 1.0),
+    ("bf16", (32, 8, 128), 257, 8, 1.0, 1.0),
+])
+def test_cod_small_layouts(dtype, heads, N, D, keep, loss):
+    Lay = si.cod_case(N, D, keep, loss, 21, heads=heads, dtype=dtype)
+    name = "COD %s N=%d D=%d heads=%s T=%d" % (dtype, N, D, heads, Lay["T"])
+    say(name)
+    Dv = upload_layout(Lay)
+    out, lse, cnt, hsh = run_cod(Dv, Lay)
+    torch.cuda.synchronize()
+    check_against_oracle(Lay, out, lse, cnt, hsh, np.arange(Lay["T"]), name)
+    # chunked == unchunked, bit for bit (chunks of 64 rows and a ragged tail), with a
+    # fixed split of the prefix range so that several splits and the combine are active
+    out1, lse1, _, _ = run_cod(Dv, Lay, dbg=False, split_len=64)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    for c0 in range(0, Lay["T"], 64):
+        c1 = min(Lay["T"], c0 + 64)
+        run_cod(Dv, Lay, c0, c1, out=out2[c0:c1], lse=lse2[c0:c1], dbg=False, split_len=64)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out2), bits(out1)) and np.array_equal(bits(lse2), bits(lse1))
+    check_against_oracle(Lay, out1, lse1, None, None, np.arange(Lay["T"]), name + " split 64")
+
+
+def test_cod_training_shape_n4096():
+    Lay = si.cod_config(3)
+    say("COD N=4096 T=%d" % Lay["T"])
+    Dv = upload_layout(Lay)
+    out, lse, cnt, hsh = run_cod(Dv, Lay)
+    torch.cuda.synchronize()
+    go = Lay["group_off"]
+    sample = set()
+    for e in range(len(go) - 1):
+        sample.update(range(go[e], min(go[e] + 8, go[e + 1])))
+        sample.update(range(max(go[e], go[e + 1] - 8), go[e + 1]))
+    sample.update(np.random.default_rng(0).choice(Lay["T"], 64, replace=False).tolist())
+    check_against_oracle(Lay, out, lse, None, None, np.array(sorted(sample)), "N=4096 values")
+    # index stats of every query
+    rc, rh = oc.index_stats(Lay["start"], Lay["depth"])
+    gc = cnt.cpu().numpy()
+    gh = hsh.cpu().numpy().view(np.uint64)
+    for j in range(gc.shape[1]):
+        np.testing.assert_array_equal(gc[:, j], rc)
+        np.testing.assert_array_equal(gh[:, j], rh)
+    assert int(rc.sum()) == int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
+
+
+def test_long_sequence_chunked_n8192():
+    Lay = si.cod_config(4)
+    T = Lay["T"]
+    assert T == 65536
+    Hq, Hkv, Dh = Lay["heads"]
+    Dv = upload_layout(Lay)
+    out = torch.empty((T, Hq, Dh), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    say("parallel groups N=8192 K=8 T=%d: unchunked" % T)
+    run_cod(Dv, Lay, out=out, lse=lse, dbg=False)
+    torch.cuda.synchronize()
+    say("  8 chunks of 8192")
+    for c in range(8):
+        run_cod(Dv, Lay, 8192 * c, 8192 * (c + 1), out=out2[8192 * c:8192 * (c + 1)],
+                lse=lse2[8192 * c:8192 * (c + 1)], dbg=False)
+    torch.cuda.synchronize()
+    # nothing near the size of a dense mask (T^2 = 4.3e9 elements) was allocated
+    assert free0 - torch.cuda.mem_get_info()[0] < (64 << 20)
+    assert np.array_equal(bits(out2), bits(out)) and np.array_equal(bits(lse2), bits(lse))
+    say("  index statistics run")
+    out3, lse3, cnt, hsh = run_cod(Dv, Lay, dbg=True)
+    torch.cuda.synchronize()
+    # visible-pair closed form through the kernel's own counters
+    assert int(cnt[:, 0].sum().item()) == 268697600
+    g = np.random.default_rng(1)
+    sample = set()
+    for c in range(8):
+        sample.update([8192 * c, 8192 * c + 1, 8192 * c + 8190, 8192 * c + 8191])
+    sample.update(g.choice(T, 24, replace=False).tolist())
+    check_against_oracle(Lay, out, lse, cnt, hsh, np.array(sorted(sample)), "N=8192 sampled")
+
+
+def test_decode_segments_split_kv():
+    """Ragged decode regions: query k of segment s sits at position len_s-K+k and
+    sees region rows 0..its position; several splits plus a combine."""
+    g = np.random.default_rng(5)
+    Hq, Hkv, Dh, K = 16, 2, 64, 7
+    lens = np.array([100, 900, 37, 2000, 71, 7])
+    base = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    rows = int(lens.sum())
+    for dtype in ("bf16", "f32"):
+        q = si.to_storage(g.standard_normal((rows, Hq, Dh)).astype(np.float32), dtype)
+        k = si.to_storage(g.standard_normal((rows, Hkv, Dh)).astype(np.float32), dtype)
+        v = si.to_storage(g.standard_normal((rows, Hkv, Dh)).astype(np.float32), dtype)
+        R = len(lens)
+        pos = np.concatenate([np.arange(l - K, l) for l in lens]).astype(np.int32)
+        pos[5] = -1                                      # a query that sees nothing
+        qrows = np.concatenate([b + np.arange(l - K, l) for b, l in zip(base, lens)]).astype(np.int32)
+        sdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        for split_len in (0, 64, 4096):
+            out = torch.empty((R * K, Hq, Dh), dtype=sdt, device="cuda")
+            lse = torch.empty((R * K, Hq), dtype=torch.float32, device="cuda")
+            cnt = torch.zeros((R * K, Hkv), dtype=torch.int64, device="cuda")
+            hsh = torch.zeros((R * K, Hkv), dtype=torch.int64, device="cuda")
+            a = L.attn_args(num_q=R * K, num_seg=R, q_per_seg=K, num_kv_rows=rows, n_q_heads=Hq, n_kv_heads=Hkv,
+                            head_dim=Dh, scale=0.125, dtype=L.PE_BF16 if dtype == "bf16" else L.PE_F32,
+                            q=to_device(q, "cuda"), q_row_stride=Hq * Dh, q_rows=to_device(qrows, "cuda"),
+                            k=to_device(k, "cuda"), v=to_device(v, "cuda"), seg_kv_base=to_device(base, "cuda"),
+                            q_start=to_device(pos, "cuda"), max_prefix=int(lens.max()), split_len=split_len,
+                            out=out, lse=lse, dbg_count=cnt, dbg_hash=hsh)
+            say("decode segments %s split_len=%d" % (dtype, split_len))
+            L.pe_draft_attention(a, "cuda")
+            torch.cuda.synchronize()
+            o = dev_to_f64(out)
+            for s in range(R):
+                b, l = int(base[s]), int(lens[s])
+                lab = np.arange(l)
+                for j in range(K):
+                    i = s * K + j
+                    if pos[i] < 0:
+                        assert np.all(o[i] == 0) and np.all(np.isneginf(lse.cpu().numpy()[i]))
+                        assert int(cnt[i, 0]) == 0
+                        continue
+                    qq = np.zeros((l, Hq, Dh))
+                    qq[pos[i]] = od.to_f64(q[b + pos[i]], dtype)
+                    ro, rl = oc.attention(qq, od.to_f64(k[b:b + l], dtype), od.to_f64(v[b:b + l], dtype), lab,
+                                          np.zeros(l, int), [pos[i]], 0.125)
+                    assert om.relerr(o[i], ro[0]) <= TOL[dtype]
+                    assert om.relerr(lse.cpu().numpy()[i], rl[0]) <= TOL[dtype]
+                    c, h = oc.region_index_stats(b, int(pos[i]))
+                    assert int(cnt[i, 0]) == c and int(cnt[i, 1]) == c
+                    assert np.uint64(hsh[i, 0].item() & 0xFFFFFFFFFFFFFFFF) == h
+
+
+def test_empty_query_set_is_noop():
+    out = torch.empty(0, device="cuda")
+    a = L.attn_args(num_q=0, num_seg=0, q_per_seg=0, num_kv_rows=0, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                    scale=0.125, dtype=L.PE_BF16, q_row_stride=512, out=out)
+    L.pe_draft_attention(a, "cuda")
+    torch.cuda.synchronize()

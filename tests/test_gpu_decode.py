@@ -1,0 +1,149 @@
+"""GPU parity of the decode-step stages against the fp64 oracle.
+
+Each case runs the four stage calls through the C ABI (via DraftStep) and
+checks, stage by stage: the draft batch bit for bit; x0; the layer output of
+the query rows, the K/V rows written, and that rejected / unwritten cache
+rows keep their sentinel bits; logits and greedy tokens.  Cases cover both
+storage dtypes, both GEMM kernels (M <= 16 and M > 16), ragged windows,
+fully rejected windows, K = 1, and the full-size c=1 and c=64 decode steps.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import GAP, TOL, bits, dev_to_f64, gptoss_weights, say
+from oracle import batch as ob
+from oracle import drafter as od
+from oracle import metrics as om
+from synth import inputs as si
+
+pytestmark = pytest.mark.gpu
+
+BATCH_KEYS = ("draft_ids", "draft_pos", "slot_mapping", "hidden_src", "req_of_row", "rejected", "masked",
+              "query_rows", "cu_draft")
+
+
+def oracle_batch(dims, W, c):
+    return ob.build_draft_batch(c["K"], dims.mask_token_id, c["cu_window"], c["n_rej"], c["kv_len"], c["kv_base"],
+                                c["window_ids"], c["window_pos"], c["window_hrow"], c["new_token"], c["ctx_hrow"],
+                                c["target_hidden"], W["h_shared"])
+
+
+def check_case(name, dims, W, c, logits=True):
+    from drafter_pe_build_amd.step import DraftStep
+    tol = TOL[dims.dtype]
+    say("[%s] upload" % name)
+    st = DraftStep(dims, W, c)
+    rb = oracle_batch(dims, W, c)
+
+    say("[%s] pe_build_draft_batch" % name)
+    st.build_batch()
+    torch.cuda.synchronize()
+    for k in BATCH_KEYS:
+        np.testing.assert_array_equal(st.batch[k].cpu().numpy(), rb[k], err_msg=k)
+    hid = bits(st.batch["draft_hidden"])
+    np.testing.assert_array_equal(hid, rb["draft_hidden"].view(hid.dtype))
+
+    say("[%s] oracle forward" % name)
+    ref = od.drafter_forward(dims, W, rb, c["kv_base"], c["k_cache"], c["v_cache"], keep_logits=logits)
+    live = rb["rejected"] == 0
+
+    say("[%s] pe_fuse_hidden" % name)
+    st.fuse()
+    torch.cuda.synchronize()
+    e = om.relerr(st.x0.cpu().numpy()[live], ref["x0"][live])
+    say("  x0 relerr %.3g" % e)
+    assert e <= tol
+
+    say("[%s] pe_draft_layer" % name)
+    k_before = bits(st.k_cache)
+    st.layer()
+    torch.cuda.synchronize()
+    e = om.relerr(st.x_out.cpu().numpy(), ref["x_query"])
+    say("  layer out relerr %.3g" % e)
+    assert e <= tol
+    slots = rb["slot_mapping"][live]
+    for gpu, refc in ((st.k_cache, ref["k_cache"]), (st.v_cache, ref["v_cache"])):
+        g = dev_to_f64(gpu)
+        ek = om.relerr(g[slots], refc[slots])
+        say("  written kv relerr %.3g" % ek)
+        assert ek <= tol
+    k_after = bits(st.k_cache)
+    untouched = np.ones(c["kv_rows"], bool)
+    untouched[slots] = False
+    np.testing.assert_array_equal(k_after[untouched], k_before[untouched])   # cache + sentinel rows keep their bits
+    n_sentinel = int(np.sum(c["n_rej"]))
+    cached = np.zeros(c["kv_rows"], bool)
+    for r in range(c["R"]):
+        cached[c["kv_base"][r]:c["kv_base"][r] + c["kv_len"][r]] = True
+    assert int(np.sum(untouched & ~cached)) == n_sentinel
+
+    say("[%s] pe_lm_head_argmax" % name)
+    st.lm_head(with_logits=logits)
+    torch.cuda.synchronize()
+    tok = st.tokens.cpu().numpy()
+    ok, n = om.tokens_agree(tok, ref["tokens"], ref["gap"], GAP)
+    say("  tokens compared %d of %d, equal %s" % (n, len(tok), ok))
+    assert ok and n > 0
+    if logits:
+        e = om.relerr(st.logits.cpu().numpy(), ref["logits"])
+        say("  logits relerr %.3g" % e)
+        assert e <= tol
+
+    say("[%s] full step again (stage outputs must repeat bit for bit)" % name)
+    t1 = st.tokens.clone()
+    x1 = st.x_out.clone()
+    st.run(with_logits=False)
+    torch.cuda.synchronize()
+    assert torch.equal(t1, st.tokens) and torch.equal(x1, st.x_out)
+    return st
+
+
+def small_dims(dtype, head_dim=64, hq=8, hkv=2):
+    return si.DrafterDims(hidden=128, n_q_heads=hq, n_kv_heads=hkv, head_dim=head_dim, ffn=256, vocab=1000,
+                          dtype=dtype)
+
+
+def test_tiny_config_fp32():
+    dims, W, c = si.decode_config(0)
+    check_case("tiny fp32 N=128 K=4", dims, W, c)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_ragged_stream_and_tiled(dtype):
+    # R*K = 15 query rows (weight-streaming GEMMs); T > 16 rows (tiled fc / qkv)
+    dims = small_dims(dtype)
+    W = si.drafter_weights(dims, 11, random_gains=True)
+    c = si.decode_case(dims, 11, R=3, K=5, W=[6, 0, 9], kv_len=[40, 3, 130], n_rej=[2, 0, 9])
+    check_case("small %s ragged R=3 K=5" % dtype, dims, W, c)
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 64), ("bf16", 128), ("f32", 128)])
+def test_small_many_queries(dtype, head_dim):
+    dims = small_dims(dtype, head_dim=head_dim, hq=4, hkv=4)
+    W = si.drafter_weights(dims, 12, random_gains=True)
+    g = np.random.default_rng(12)
+    R = 9
+    Wn = g.integers(0, 8, R)
+    n_rej = np.array([g.integers(0, w + 1) for w in Wn])
+    c = si.decode_case(dims, 12, R=R, K=7, W=Wn, kv_len=g.integers(0, 300, R), n_rej=n_rej)
+    check_case("small %s Dh=%d R=9 K=7" % (dtype, head_dim), dims, W, c)
+
+
+def test_single_draft_slot():
+    dims = small_dims("bf16", hq=16, hkv=2)
+    W = si.drafter_weights(dims, 13)
+    c = si.decode_case(dims, 13, R=4, K=1, W=[3, 1, 0, 5], kv_len=[10, 0, 70, 1], n_rej=[1, 1, 0, 0])
+    check_case("K=1", dims, W, c)
+
+
+def test_decode_c1_full_size():
+    dims = si.GPTOSS_DIMS
+    _, _, c = si.decode_config(1, with_weights=False)
+    check_case("decode c=1 d=2880 V=201088", dims, gptoss_weights(), c)
+
+
+def test_decode_c64_full_size():
+    dims = si.GPTOSS_DIMS
+    _, _, c = si.decode_config(2, with_weights=False)
+    check_case("decode c=64 d=2880 V=201088", dims, gptoss_weights(), c)
