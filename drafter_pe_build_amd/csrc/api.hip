@@ -205,6 +205,7 @@ FuseWs fuse_ws(const pe_drafter_dims* d, int T, void* base) {
   w.nzero = zero_ints((size_t)3 * d->hidden * esize(d->dtype));
   w.u = c.take((size_t)T * 3 * d->hidden * esize(d->dtype));
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
+
   w.total = c.off;
   return w;
 }
@@ -482,7 +483,7 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   st = run_attention(&aa, lw.attn, lw.attn_bytes, 1, stream);
   if (st != PE_OK) return st;
 
-  // x1 = x0[query rows] + W_o o
+  // x1 = x0[query rows] + W_o o;  b = RMSNorm(x1)
   gp = GemmParams{};
   gp.X = lw.o;
   gp.ldx = qcols;
@@ -498,8 +499,6 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.epi.res_rows = batch->query_rows;
   gp.epi.ld_res = d;
   launch_gemm(gp, bf, stream);
-
-  // b = RMSNorm(x1); h = silu(W_gate b) * (W_up b)
   np = NormParams{};
   np.in = lw.x1;
   np.ld_in = d;
@@ -511,6 +510,8 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   np.out = lw.b;
   np.ld_out = d;
   launch_rmsnorm_rows(np, 0, bf, stream);
+
+  // h = silu(W_gate b) * (W_up b)
   gp = GemmParams{};
   gp.X = lw.b;
   gp.ldx = d;

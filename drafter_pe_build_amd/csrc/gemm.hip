@@ -163,44 +163,60 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmParams p) {
   }
 }
 
-// LM head for M <= 16: grid-stride over groups of NFB weight blocks, one wave
-// per block, full K per wave.  Each lane keeps the best (logit, lowest index)
-// of its activation row; the workgroup's best per row goes to partial slot
-// [blockIdx][row], reduced by argmax_reduce_kernel.
-template <typename S, int NFB, int U>
-__global__ __launch_bounds__(64 * NFB) void lm_argmax_stream_kernel(GemmParams p) {
+// LM head for M <= 16: grid-stride over groups of NFB weight blocks; KS waves
+// per block split K and sum through LDS in ks order.  Each lane of the
+// block's first wave keeps the best (logit, lowest index) of its activation
+// row; the workgroup's best per row goes to partial slot [blockIdx][row],
+// reduced by argmax_reduce_kernel.
+template <typename S, int NFB, int KS, int U>
+__global__ __launch_bounds__(64 * NFB * KS) void lm_argmax_stream_kernel(GemmParams p) {
   constexpr int CH = Storage<S>::CH;
   constexpr int STEP = 4 * CH;
+  constexpr int NW = NFB * KS;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int fbl = wave / KS, ks = wave % KS;
   const int r = lane & 15, g = lane >> 4;
   const int M = p.M, N = p.N, K = p.K;
   const int nsteps = K / STEP;
+  const int s0 = nsteps * ks / KS, s1 = nsteps * (ks + 1) / KS;
   const int nfb = (N + 15) >> 4;
   const int ntiles = (nfb + NFB - 1) / NFB;
   const bool xr = r < M;
   const S* xrow = (xr ? reinterpret_cast<const S*>(p.X) + (int64_t)r * p.ldx : reinterpret_cast<const S*>(p.xzero)) + g * CH;
   const char* W = reinterpret_cast<const char*>(p.W) + lane * 16;
+  __shared__ f32x4 red[KS > 1 ? NFB * (KS - 1) * 64 : 1];
   float best = -INFINITY;
   int bidx = 0x7fffffff;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int fb = tile * NFB + wave;
-    if (fb >= nfb) continue;
-    const char* wb = W + (int64_t)fb * nsteps * 1024;
+    const int fb = tile * NFB + fbl;
+    const bool active = fb < nfb;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsteps; s += U) {
-      u32x4 wv[U], xv[U];
+    if (active) {
+      const char* wb = W + (int64_t)fb * nsteps * 1024;
+      for (int s = s0; s < s1; s += U) {
+        u32x4 wv[U], xv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int su = min(s + u, nsteps - 1);
-        wv[u] = ld16(wb + (int64_t)su * 1024);
-        xv[u] = ld16(xrow + su * STEP);
+        for (int u = 0; u < U; ++u) {
+          const int su = min(s + u, s1 - 1);
+          wv[u] = ld16(wb + (int64_t)su * 1024);
+          xv[u] = ld16(xrow + su * STEP);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (s + u < s1) mma16(acc, wv[u], xv[u], S());
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (s + u < nsteps) mma16(acc, wv[u], xv[u], S());
     }
-    if (xr) {
+    if constexpr (KS > 1) {
+      if (ks > 0 && active) red[(fbl * (KS - 1) + ks - 1) * 64 + lane] = acc;
+      __syncthreads();
+      if (ks == 0 && active) {
+#pragma unroll
+        for (int k = 0; k < KS - 1; ++k) acc += red[(fbl * (KS - 1) + k) * 64 + lane];
+      }
+      __syncthreads();
+    }
+    if (ks == 0 && active && xr) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = fb * 16 + 4 * g + j;
@@ -215,14 +231,14 @@ __global__ __launch_bounds__(64 * NFB) void lm_argmax_stream_kernel(GemmParams p
     const int oi = __shfl_xor(bidx, o, 64);
     if (better(ov, oi, best, bidx)) { best = ov; bidx = oi; }
   }
-  __shared__ float sbv[NFB][16];
-  __shared__ int sbi[NFB][16];
+  __shared__ float sbv[NW][16];
+  __shared__ int sbi[NW][16];
   if (g == 0) { sbv[wave][r] = best; sbi[wave][r] = bidx; }
   __syncthreads();
   if ((int)threadIdx.x < M) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int w = 0; w < NFB; ++w)
+    for (int w = 0; w < NW; ++w)
       if (better(sbv[w][threadIdx.x], sbi[w][threadIdx.x], bv, bi)) { bv = sbv[w][threadIdx.x]; bi = sbi[w][threadIdx.x]; }
     p.epi.part_val[(int64_t)blockIdx.x * M + threadIdx.x] = bv;
     p.epi.part_idx[(int64_t)blockIdx.x * M + threadIdx.x] = bi;
@@ -423,7 +439,17 @@ void launch_argmax_reduce(const float* pv, const int32_t* pi, int P, int M, int3
 // ---------------------------------------------------------------------------
 // Dispatch
 static constexpr int kStreamU = 8;     // 1 KB steps in flight per wave
-static constexpr int kLmGrid = 2048;   // LM-head workgroups (grid-stride)
+// LM-head launch shape: NFB blocks x KS waves per workgroup, grid capped at kLmGrid.
+#ifndef PE_LM_NFB
+#define PE_LM_NFB 4
+#endif
+#ifndef PE_LM_KS
+#define PE_LM_KS 2
+#endif
+#ifndef PE_LM_GRID
+#define PE_LM_GRID 4096
+#endif
+static constexpr int kLmNFB = PE_LM_NFB, kLmKS = PE_LM_KS, kLmGrid = PE_LM_GRID;
 
 // Waves per 16-row block: the most (up to 16) that still leave every wave at
 // least one full batch of kStreamU steps.
@@ -435,7 +461,7 @@ static int stream_ks(int nsteps) {
 
 int gemm_argmax_partials(int M, int N) {
   if (M <= 16) {
-    const int ntiles = ((N + 15) / 16 + 3) / 4;
+    const int ntiles = ((N + 15) / 16 + kLmNFB - 1) / kLmNFB;
     return ntiles < kLmGrid ? ntiles : kLmGrid;
   }
   return (N + 63) / 64;  // largest count over the tiled configurations (BN >= 64)
@@ -468,7 +494,8 @@ static int launch_gemm_t(const GemmParams& p, hipStream_t s) {
   if (p.M <= 16) {
     if (am) {
       const int grid = gemm_argmax_partials(p.M, p.N);
-      hipLaunchKernelGGL((lm_argmax_stream_kernel<S, 4, kStreamU>), dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kStreamU>), dim3(grid), dim3(64 * kLmNFB * kLmKS),
+                         0, s, p);
       return grid;
     }
     if (dual) launch_stream<S, true>(p, s); else launch_stream<S, false>(p, s);

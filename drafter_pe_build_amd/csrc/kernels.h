@@ -75,6 +75,7 @@ struct GemmParams {
   Epi epi;
 };
 
+
 // Packs a row-major [N, row_bytes] matrix into the matrix-core-ready layout
 // streamed by the GEMM kernels (see gemm.hip).
 void launch_pack(const void* src, void* dst, int N, int row_bytes, hipStream_t s);
