@@ -215,7 +215,8 @@ def main():
                                    q=q[c0:c1], q_row_stride=Hq * Dh, k=k, v=v, seg_kv_base=base,
                                    q_start=start[c0:c1], q_depth=depth[c0:c1], q_self_row=selfr[c0:c1],
                                    kv_parent=parent, max_prefix=Lay["N"], out=out[c0:c1]) for c0, c1 in chunks]
-            ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+            wsb = max(L.pe_draft_attention_workspace(a) for a in arglist)
+            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
 
             def run_attn():
                 for a in arglist:

@@ -101,7 +101,7 @@ size_t attn_ws_bytes(int num_q, int Hq, int Hkv, int Dh, int n_splits) {
 
 void attn_split_for(const pe_attn_args* a, int* n_splits, int* split_len) {
   const int G = a->n_q_heads / a->n_kv_heads;
-  const int QPW = 64 / G;
+  const int QPW = attn_queries_per_workgroup(G, a->head_dim);
   const int tps = (a->q_per_seg + QPW - 1) / QPW;
   int base = a->num_seg * tps * a->n_kv_heads;
   if (base < 1) base = 1;
@@ -182,7 +182,7 @@ LayerWs layer_ws(const pe_drafter_dims* d, int T, int R, int K, int max_pos, voi
   w.h = c.take((size_t)RK * d->ffn * e);
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
   const int G = d->n_q_heads / d->n_kv_heads;
-  const int QPW = 64 / G;
+  const int QPW = attn_queries_per_workgroup(G, d->head_dim);
   int n_splits, split_len;
   choose_split(R * ((K + QPW - 1) / QPW) * d->n_kv_heads, max_pos, 0, &n_splits, &split_len);
   w.attn_bytes = attn_ws_bytes(RK, d->n_q_heads, d->n_kv_heads, d->head_dim, n_splits);

@@ -9,29 +9,48 @@
 // exists, and key tiles beyond the largest prefix of a workgroup's queries
 // are never touched.
 //
-// Work unit: one workgroup = one kv head x up to 64 query columns, a column
-// being a (query, q-head) pair of that kv head's GQA group (64/G queries of
-// G heads), optionally restricted to one split of the prefix range (decode
-// shapes: few queries, long regions).  4 waves x 16 columns.  Per 64-key tile:
-//   * keys are staged in LDS: K row-major, V transposed (V^T[dh][key]) so
-//     that both MFMA operands read contiguous 8/16-byte runs;
-//   * S^T = K Q^T on the matrix cores (A = K rows, B = Q columns, Q kept in
-//     registers for the whole kernel), giving lane (r, g) the scores of
-//     column r for keys 4g..4g+3 of each 16-key block;
-//   * masking, online softmax in fp32 (exp2 with the log2(e)-folded scale);
-//     each lane's column is fixed, so the rescale of the running output is
-//     a per-lane scalar;
+// Work unit: one workgroup = one kv head x 256 columns (128 at head_dim
+// 128), a column being a (query, q-head) pair of that kv head's GQA group
+// (256/G queries of G heads), optionally restricted to one split of the
+// prefix range (decode shapes: few queries, long regions).  4 waves x 64
+// columns (blocks of 16).  Per 64-key tile:
+//   * the tile is staged in LDS (K row-major, V transposed as V^T[dh][key] so
+//     both matrix-core operands read contiguous runs); two LDS buffers and a
+//     register prefetch of the next tile leave one barrier per tile and keep
+//     the next tile's HBM reads in flight while this one is multiplied;
+//   * S^T = K Q^T on the matrix cores (A = K rows from LDS, B = Q columns kept
+//     in registers for the whole kernel): each 1 KB operand read from LDS
+//     feeds every column block of the wave;
+//   * masking (skipped on tiles every column of the wave sees in full) and an
+//     online softmax in fp32 (exp2 with the log2(e)-folded scale); each lane's
+//     column is fixed, so the rescale of the running output is per lane;
 //   * O^T += V^T P^T on the matrix cores (P rounded to the operand type).
+// A wave skips the multiplications of tiles none of its columns can see.
 // Chain rows are gathered into extra tiles whose mask is "owner == column's
-// query"; a row shared by several chains simply appears once per owner.
-// Splits write unnormalised partials (m, l, O); a combine kernel merges them.
+// query"; a row shared by several chains appears once per owner.  Splits
+// write unnormalised partials (m, l, O); a combine kernel merges them.
+//
+// Every column's result depends only on its own key set and the fixed tile
+// order (prefix tiles aligned to multiples of 64 from the split start, then
+// the chain tiles), so a query gives the same bits whether it is attended in
+// one launch or in a chunk of queries (for the same split length and the
+// same grouping of chain tiles, i.e. chunks that start at multiples of the
+// workgroup's query count).
 #include <math.h>
 #include "kernels.h"
 
 namespace pe {
 
-constexpr int KT = 64;     // keys per tile
-constexpr int MAXD = 16;   // deepest chain walked per query
+constexpr int KT = 64;          // keys per tile
+constexpr int NWAVE = 4;        // waves per workgroup
+constexpr int MAXD = 16;        // deepest chain walked per query
+constexpr int ANC_MAX = 2048;   // chain rows gathered per workgroup
+
+// 16-column blocks per wave: four at head_dim 64; two at 128, where four
+// would not fit the register file.
+__host__ __device__ constexpr int attn_col_blocks(int DH) { return DH >= 128 ? 2 : 4; }
+
+int attn_queries_per_workgroup(int G, int head_dim) { return NWAVE * attn_col_blocks(head_dim) * 16 / G; }
 
 template <typename S, int DH, bool DBG>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps) {
@@ -42,17 +61,23 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
   constexpr int DC = DH / CH;                    // 16-byte chunks per head row
   constexpr int KPITCH = DC + 1;                 // Ks row pitch, 16-byte units
   constexpr int VPB = KT * (int)sizeof(S) + 16;  // Vt row pitch, bytes
-  __shared__ u32x4 Ks[KT * KPITCH];
-  __shared__ __attribute__((aligned(16))) char Vt[DH * VPB];
-  __shared__ int s_keyrow[KT];
-  __shared__ int s_start[64], s_depth[64], s_self[64], s_cnt[64], s_off[65];
-  __shared__ int s_anc_row[64 * MAXD], s_anc_own[64 * MAXD];
-  __shared__ int s_maxstart;
+  constexpr int KLD = (KT * DC + 255) / 256;     // K chunks each thread moves per tile
+  constexpr int VTS = (16 * DC + 255) / 256;     // V tasks (4 keys x CH dims) per thread per tile
+  constexpr int CBLK = attn_col_blocks(DH);
+  constexpr int QMAX = NWAVE * CBLK * 16;        // columns (queries at G = 1) per workgroup
+  __shared__ u32x4 Ks[2][KT * KPITCH];
+  __shared__ __attribute__((aligned(16))) char Vt[2][DH * VPB];
+  __shared__ int s_start[QMAX], s_cnt[QMAX], s_self[QMAX], s_off[QMAX + 1];
+  __shared__ int s_anc_row[ANC_MAX];
+  __shared__ __attribute__((aligned(16))) int s_anc_own[ANC_MAX];  // -1 past the last entry of a tile
+  __shared__ int s_red[8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int Hkv = p.Hkv, Hq = p.Hq;
-  const int QPW = 64 / G;
+  const int QPW = QMAX / G;
+  const int maxd = min(MAXD, ANC_MAX / QPW);
 
   int bid = blockIdx.x;
   const int kvh = bid % Hkv;
@@ -64,53 +89,59 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
   const int qbase = seg * p.q_per_seg + tile * QPW;
   const int nq = min(QPW, p.q_per_seg - tile * QPW);
 
-  // ---- per-query metadata and chain walk
-  if (tid < 64) {
-    int st = -1, dp = 0, self = -1;
-    if (tid < nq) {
-      const int qi = qbase + tid;
-      const int mi = (p.meta_by_row && p.q_rows) ? p.q_rows[qi] : qi;
-      st = p.q_start[mi];
-      if (p.q_depth) {
-        dp = min(max(p.q_depth[mi], 0), MAXD);
-        self = p.q_self_row[mi];
+  // ---- per-query metadata, chain lengths, exclusive scan of the lengths
+  int st = -1, cnt = 0, self = -1;
+  if (tid < nq) {
+    const int qi = qbase + tid;
+    const int mi = (p.meta_by_row && p.q_rows) ? p.q_rows[qi] : qi;
+    st = p.q_start[mi];
+    if (p.q_depth) {
+      const int dp = min(max(p.q_depth[mi], 0), maxd);
+      self = p.q_self_row[mi];
+      int row = self;
+      for (int e = 0; e < dp; ++e) {
+        if (row < 0 || row >= p.num_kv_rows) break;
+        ++cnt;
+        row = p.kv_parent[row];
       }
     }
-    int cnt = 0, row = self;
-    for (int e = 0; e < dp; ++e) {
-      if (row < 0 || row >= p.num_kv_rows) break;
-      ++cnt;
-      row = p.kv_parent[row];
-    }
+  }
+  if (tid < QMAX) {
     s_start[tid] = st;
-    s_depth[tid] = cnt;
-    s_self[tid] = self;
     s_cnt[tid] = cnt;
+    s_self[tid] = self;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int o = 0, mx = -1;
-    for (int i = 0; i < 64; ++i) {
-      s_off[i] = o;
-      o += s_cnt[i];
-      mx = max(mx, s_start[i]);
-    }
-    s_off[64] = o;
-    s_maxstart = mx;
+  int incl = cnt;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
   }
+  int mx = st;
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+  if (lane == 63) s_red[wave] = incl;
+  if (lane == 0) s_red[4 + wave] = mx;
   __syncthreads();
-  if (tid < nq && s_cnt[tid] > 0) {
-    int row = s_self[tid];
-    const int o = s_off[tid];
-    for (int e = 0; e < s_cnt[tid]; ++e) {
+  int wofs = 0;
+  for (int w = 0; w < wave; ++w) wofs += s_red[w];
+  const int n_anc_all = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  const int max_start = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
+  if (tid < QMAX) s_off[tid] = wofs + incl - cnt;
+  if (tid == 0) s_off[QMAX] = n_anc_all;
+  if (cnt > 0) {
+    int row = self;
+    const int o = wofs + incl - cnt;
+    for (int e = 0; e < cnt; ++e) {
       s_anc_row[o + e] = row;
       s_anc_own[o + e] = tid;
       row = p.kv_parent[row];
     }
   }
+  if (tid < KT) {  // pad the last chain tile (ANC_MAX is a multiple of KT)
+    const int e = n_anc_all + tid;
+    if (e < ((n_anc_all + KT - 1) / KT) * KT) s_anc_own[e] = -1;
+  }
   __syncthreads();
-  const int n_anc = (sp == 0) ? s_off[64] : 0;
-  const int max_start = s_maxstart;
+  const int n_anc = (sp == 0) ? n_anc_all : 0;
   const int seg_base = p.seg_kv_base[seg];
 
   // ---- this split's prefix range [kbeg, kend]
@@ -119,65 +150,108 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
   const int n_pref = (kend >= kbeg) ? (kend - kbeg + KT) / KT : 0;
   const int n_tiles = n_pref + (n_anc + KT - 1) / KT;
 
-  // ---- this lane's column
-  const int col = wave * 16 + r;
-  const int cq = col / G, cg = col % G;
-  const bool cact = cq < nq;
-  const int cstart = cact ? s_start[cq] : -1;
-  const int h = kvh * G + cg;
-
+  // ---- this lane's columns, one per column block
   const S* Q = reinterpret_cast<const S*>(p.q);
   const S* Kg = reinterpret_cast<const S*>(p.k);
   const S* Vg = reinterpret_cast<const S*>(p.v);
-  u32x4 qreg[NST];
-  {
-    int qrow = -1;
-    if (cact) qrow = p.q_rows ? p.q_rows[qbase + cq] : qbase + cq;
+  int cq[CBLK], climit[CBLK], hh[CBLK];
+  bool cact[CBLK];
+  u32x4 qreg[CBLK][NST];
+  int lo = 0x7fffffff, hi = -1;
 #pragma unroll
-    for (int st = 0; st < NST; ++st)
-      qreg[st] = (qrow >= 0) ? ld16(Q + (int64_t)qrow * p.q_stride + (int64_t)h * DH + st * STEP + g * CH)
-                             : u32x4{0u, 0u, 0u, 0u};
+  for (int cb = 0; cb < CBLK; ++cb) {
+    const int col = wave * (CBLK * 16) + cb * 16 + r;
+    cq[cb] = col / G;
+    hh[cb] = kvh * G + col % G;
+    cact[cb] = cq[cb] < nq;
+    climit[cb] = cact[cb] ? min(s_start[cq[cb]], kend) : -1;
+    if (cact[cb]) {
+      lo = min(lo, climit[cb]);
+      hi = max(hi, climit[cb]);
+    }
+    const int qrow = cact[cb] ? (p.q_rows ? p.q_rows[qbase + cq[cb]] : qbase + cq[cb]) : -1;
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+      qreg[cb][t] = (qrow >= 0) ? ld16(Q + (int64_t)qrow * p.q_stride + (int64_t)hh[cb] * DH + t * STEP + g * CH)
+                                : u32x4{0u, 0u, 0u, 0u};
   }
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o, 64));
+    hi = max(hi, __shfl_xor(hi, o, 64));
+  }
+  const int wmin = __builtin_amdgcn_readfirstlane(lo);   // every active column sees keys <= wmin
+  const int wmax = __builtin_amdgcn_readfirstlane(hi);   // no column sees keys > wmax
+  // chain entries owned by this wave's queries (a query's G columns may
+  // straddle two waves when G exceeds a wave's 16 * CBLK columns)
+  const int wq0 = min(wave * CBLK * 16 / G, nq), wq1 = min(((wave + 1) * CBLK * 16 + G - 1) / G, nq);
+  const int wa0 = s_off[wq0], wa1 = s_off[wq1];
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[NMB];
+  float m_run[CBLK], l_run[CBLK];
+  f32x4 acc[CBLK][NMB];
+  int64_t dcnt[CBLK];
+  uint64_t dhsh[CBLK];
 #pragma unroll
-  for (int i = 0; i < NMB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int64_t dcnt = 0;
-  uint64_t dhsh = 0;
+  for (int cb = 0; cb < CBLK; ++cb) {
+    m_run[cb] = -INFINITY;
+    l_run[cb] = 0.f;
+    dcnt[cb] = 0;
+    dhsh[cb] = 0;
+#pragma unroll
+    for (int i = 0; i < NMB; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const float sl2 = p.scale_log2;
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const bool anc = it >= n_pref;
-    const int k0 = anc ? (it - n_pref) * KT : kbeg + it * KT;
-    if (tid < KT) {
-      int row = -1;
-      if (anc) {
-        const int ai = k0 + tid;
-        if (ai < n_anc) row = s_anc_row[ai];
-      } else {
-        const int pos = k0 + tid;
-        if (pos <= kend) row = seg_base + pos;
+  // ---- tile staging: key rows by arithmetic (prefix) or from the chain list.
+  // Branch-free: every thread loads from a clamped row and zeroes invalid
+  // rows when it writes LDS (a zero V row keeps 0 * V finite).
+  const bool have_rows = p.num_kv_rows > 0;
+  auto tile_row = [&](int it, int key) -> int {
+    const int pos = kbeg + it * KT + key;
+    const int ai = (it - n_pref) * KT + key;
+    const int arow = s_anc_row[min(max(ai, 0), ANC_MAX - 1)];
+    const int row = (it < n_pref) ? (pos <= kend ? seg_base + pos : -1) : (ai < n_anc ? arow : -1);
+    return (row >= 0 && row < p.num_kv_rows) ? row : -1;
+  };
+  u32x4 kreg[KLD], vreg[VTS][4];
+  uint32_t kok = 0, vok = 0;  // valid-row bits of the staged chunks
+  auto load_tile = [&](int it) {
+    kok = 0;
+    vok = 0;
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int c = tid + i * 256;
+      const int key = (c / DC) & (KT - 1), ch = c % DC;
+      const int row = tile_row(it, key);
+      kok |= (uint32_t)(row >= 0) << i;
+      kreg[i] = ld16(Kg + ((int64_t)max(row, 0) * Hkv + kvh) * DH + ch * CH);
+    }
+#pragma unroll
+    for (int i = 0; i < VTS; ++i) {
+      const int t = tid + i * 256;
+      const int kg = t & 15, dc = (t >> 4) % DC;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = tile_row(it, kg * 4 + q);
+        vok |= (uint32_t)(row >= 0) << (4 * i + q);
+        vreg[i][q] = ld16(Vg + ((int64_t)max(row, 0) * Hkv + kvh) * DH + dc * CH);
       }
-      if (row < 0 || row >= p.num_kv_rows) row = -1;
-      s_keyrow[tid] = row;
     }
-    __syncthreads();
-    // K tile, row-major
-    for (int c = tid; c < KT * DC; c += 256) {
-      const int key = c / DC, ch = c % DC;
-      const int row = s_keyrow[key];
-      Ks[key * KPITCH + ch] = (row >= 0) ? ld16(Kg + ((int64_t)row * Hkv + kvh) * DH + ch * CH) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto store_tile = [&](int buf) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int c = tid + i * 256;
+      if (c < KT * DC) Ks[buf][(c / DC) * KPITCH + c % DC] = ((kok >> i) & 1) ? kreg[i] : z;
     }
-    // V tile, transposed: each task moves 4 keys x CH head dims
-    for (int t = tid; t < 16 * DC; t += 256) {
+#pragma unroll
+    for (int i = 0; i < VTS; ++i) {
+      const int t = tid + i * 256;
+      if (t >= 16 * DC) continue;
       const int kg = t & 15, dc = t >> 4;
       u32x4 v4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = s_keyrow[kg * 4 + i];
-        v4[i] = (row >= 0) ? ld16(Vg + ((int64_t)row * Hkv + kvh) * DH + dc * CH) : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int q = 0; q < 4; ++q) v4[q] = ((vok >> (4 * i + q)) & 1) ? vreg[i][q] : z;
       if constexpr (sizeof(S) == 2) {
 #pragma unroll
         for (int e = 0; e < CH; ++e) {
@@ -185,141 +259,215 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
           const uint32_t a0 = (v4[0][e >> 1] >> sh) & 0xffffu, a1 = (v4[1][e >> 1] >> sh) & 0xffffu;
           const uint32_t a2 = (v4[2][e >> 1] >> sh) & 0xffffu, a3 = (v4[3][e >> 1] >> sh) & 0xffffu;
           u32x2 w = {a0 | (a1 << 16), a2 | (a3 << 16)};
-          *reinterpret_cast<u32x2*>(Vt + (dc * CH + e) * VPB + kg * 8) = w;
+          *reinterpret_cast<u32x2*>(&Vt[buf][(dc * CH + e) * VPB + kg * 8]) = w;
         }
       } else {
 #pragma unroll
         for (int e = 0; e < CH; ++e) {
           u32x4 w = {v4[0][e], v4[1][e], v4[2][e], v4[3][e]};
-          *reinterpret_cast<u32x4*>(Vt + (dc * CH + e) * VPB + kg * 16) = w;
+          *reinterpret_cast<u32x4*>(&Vt[buf][(dc * CH + e) * VPB + kg * 16]) = w;
         }
       }
     }
-    __syncthreads();
+  };
 
-    // S^T = K Q^T
-    f32x4 sacc[4];
+  const int n_iter = have_rows ? n_tiles : 0;
+  if (n_iter > 0) load_tile(0);
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (it + 1 < n_iter) load_tile(it + 1);
+
+    const bool anc = it >= n_pref;
+    const int k0 = anc ? (it - n_pref) * KT : kbeg + it * KT;
+    const bool skip = anc ? (k0 + KT <= wa0 || k0 >= wa1) : (k0 > wmax);
+    if (skip) continue;
+    const bool full = !DBG && !anc && (k0 + KT - 1 <= wmin);
+
+    // S^T = K Q^T: each K operand read once, used for every column block
+    f32x4 sacc[CBLK][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      sacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CBLK; ++cb)
 #pragma unroll
-      for (int st = 0; st < NST; ++st) mma16(sacc[b], Ks[(16 * b + r) * KPITCH + st * 4 + g], qreg[st], S());
-    }
-    // mask + online softmax
-    float sv[16];
-    float tmax = -INFINITY;
+      for (int b = 0; b < 4; ++b) sacc[cb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kk = 16 * b + 4 * g + j;
-        const int row = s_keyrow[kk];
-        bool vis;
-        if (anc) vis = cact && row >= 0 && s_anc_own[k0 + kk] == cq;
-        else vis = row >= 0 && (k0 + kk) <= cstart;
-        const float s = vis ? sacc[b][j] : -INFINITY;
-        sv[4 * b + j] = s;
-        tmax = fmaxf(tmax, s);
-        if constexpr (DBG) {
-          if (vis) { ++dcnt; dhsh += mix64((uint64_t)(uint32_t)row); }
+      for (int t = 0; t < NST; ++t) {
+        const u32x4 a = Ks[buf][(16 * b + r) * KPITCH + t * 4 + g];
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) mma16(sacc[cb][b], a, qreg[cb][t], S());
+      }
+
+    // Mask in place.  This lane holds keys 16b + 4g + j (b, j < 4) of its
+    // columns.  Chain keys are visible to the column whose query owns them
+    // (the owner list is padded with -1); a prefix key k0 + 16b + 4g + j is
+    // visible while it is <= the column's limit.  Tiles that every column of
+    // the wave sees in full are left unmasked.
+    if (anc) {
+      int own[16];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const u32x4 o4 = *reinterpret_cast<const u32x4*>(&s_anc_own[k0 + 16 * b + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) own[4 * b + j] = (int)o4[j];
+      }
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sacc[cb][b][j] = (own[4 * b + j] == cq[cb]) ? sacc[cb][b][j] : -INFINITY;
+    } else if (!full) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) {
+        const int d = climit[cb] - k0 - 4 * g;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sacc[cb][b][j] = (16 * b + j <= d) ? sacc[cb][b][j] : -INFINITY;
+      }
+    }
+    if constexpr (DBG) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) {
+        const int d = climit[cb] - k0 - 4 * g;
+        for (int i = 0; i < 16; ++i) {
+          const int kk = 16 * (i >> 2) + 4 * g + (i & 3);
+          const bool vis = anc ? (s_anc_own[k0 + kk] == cq[cb]) : (16 * (i >> 2) + (i & 3) <= d);
+          if (vis) {
+            const int row = anc ? s_anc_row[k0 + kk] : seg_base + k0 + kk;
+            ++dcnt[cb];
+            dhsh[cb] += mix64((uint64_t)(uint32_t)row);
+          }
         }
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    float pv[16];
-    float psum = 0.f;
-    if (m_new == -INFINITY) {
+    }
+
+    // online softmax per column block; P^T packed for the next product
+    u32x4 bop[CBLK][sizeof(S) == 2 ? 2 : 4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pv[i] = 0.f;
-    } else {
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
-      const float mb = m_new * sl2;
+    for (int cb = 0; cb < CBLK; ++cb) {
+      float sv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = sacc[cb][i >> 2][i & 3];
+      float tmax = sv[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sv[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // The running maximum m is moved only when a column's maximum grows by
+      // more than 2^8 in exp2 units (then P <= 2^8 between moves; the final
+      // division by l removes m exactly), so the rescale of O and l is rare.
+      const bool grow = (tmax - m_run[cb]) * sl2 > 8.0f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        // alpha is 1 on lanes that keep m (m may still be -inf there)
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[cb] - tmax) * sl2) : 1.0f;
+        l_run[cb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NMB; ++i) acc[cb][i] *= alpha;
+        m_run[cb] = grow ? tmax : m_run[cb];
+      }
+      const float mb = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb] * sl2;
+      float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         pv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -mb));
-        psum += pv[i];
+        l_run[cb] += pv[i];
       }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
+      if constexpr (sizeof(S) == 2) {
 #pragma unroll
-      for (int i = 0; i < NMB; ++i) acc[i] *= alpha;
-      m_run = m_new;
+        for (int pr = 0; pr < 2; ++pr) {
+          const int b0 = 2 * pr;
+          bop[cb][pr] = u32x4{pack_bf16x2(pv[4 * b0 + 0], pv[4 * b0 + 1]), pack_bf16x2(pv[4 * b0 + 2], pv[4 * b0 + 3]),
+                              pack_bf16x2(pv[4 * b0 + 4], pv[4 * b0 + 5]), pack_bf16x2(pv[4 * b0 + 6], pv[4 * b0 + 7])};
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          bop[cb][b] = u32x4{__float_as_uint(pv[4 * b]), __float_as_uint(pv[4 * b + 1]), __float_as_uint(pv[4 * b + 2]),
+                             __float_as_uint(pv[4 * b + 3])};
+      }
     }
-    // O^T += V^T P^T
+
+    // O^T += V^T P^T: each V^T operand read once, used for every column block
     if constexpr (sizeof(S) == 2) {
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int b0 = 2 * pr;
-        u32x4 bop = {pack_bf16x2(pv[4 * b0 + 0], pv[4 * b0 + 1]), pack_bf16x2(pv[4 * b0 + 2], pv[4 * b0 + 3]),
-                     pack_bf16x2(pv[4 * b0 + 4], pv[4 * b0 + 5]), pack_bf16x2(pv[4 * b0 + 6], pv[4 * b0 + 7])};
+      for (int mbk = 0; mbk < NMB; ++mbk)
 #pragma unroll
-        for (int mbk = 0; mbk < NMB; ++mbk) {
-          const char* vrow = Vt + (16 * mbk + r) * VPB;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + (32 * pr + 4 * g) * 2);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (32 * pr + 16 + 4 * g) * 2);
-          u32x4 aop = {lo.x, lo.y, hi.x, hi.y};
-          mma16(acc[mbk], aop, bop, S());
+        for (int pr = 0; pr < 2; ++pr) {
+          const char* vrow = &Vt[buf][(16 * mbk + r) * VPB];
+          const u32x2 vlo = *reinterpret_cast<const u32x2*>(vrow + (32 * pr + 4 * g) * 2);
+          const u32x2 vhi = *reinterpret_cast<const u32x2*>(vrow + (32 * pr + 16 + 4 * g) * 2);
+          const u32x4 aop = {vlo.x, vlo.y, vhi.x, vhi.y};
+#pragma unroll
+          for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][pr], S());
         }
-      }
     } else {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        u32x4 bop = {__float_as_uint(pv[4 * b]), __float_as_uint(pv[4 * b + 1]), __float_as_uint(pv[4 * b + 2]),
-                     __float_as_uint(pv[4 * b + 3])};
+      for (int mbk = 0; mbk < NMB; ++mbk)
 #pragma unroll
-        for (int mbk = 0; mbk < NMB; ++mbk) {
-          const u32x4 aop = *reinterpret_cast<const u32x4*>(Vt + (16 * mbk + r) * VPB + (16 * b + 4 * g) * 4);
-          mma16(acc[mbk], aop, bop, S());
+        for (int b = 0; b < 4; ++b) {
+          const u32x4 aop = *reinterpret_cast<const u32x4*>(&Vt[buf][(16 * mbk + r) * VPB + (16 * b + 4 * g) * 4]);
+#pragma unroll
+          for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][b], S());
         }
-      }
     }
-    __syncthreads();
   }
 
-  // ---- epilogue
-  const int qo = qbase + cq;
-  if (p.n_splits == 1) {
-    if (cact) {
-      const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  // ---- epilogue (l_run holds this lane's share of the row sum)
+#pragma unroll
+  for (int cb = 0; cb < CBLK; ++cb) {
+    l_run[cb] += __shfl_xor(l_run[cb], 16, 64);
+    l_run[cb] += __shfl_xor(l_run[cb], 32, 64);
+    if constexpr (DBG) {
+      for (int o = 16; o < 64; o <<= 1) {
+        dcnt[cb] += __shfl_xor(dcnt[cb], o, 64);
+        dhsh[cb] += __shfl_xor(dhsh[cb], o, 64);
+      }
+    }
+    if (!cact[cb]) continue;
+    const int qo = qbase + cq[cb];
+    const int h = hh[cb];
+    if (p.n_splits == 1) {
+      const float inv = l_run[cb] > 0.f ? 1.0f / l_run[cb] : 0.f;
       S* o = reinterpret_cast<S*>(p.out) + ((int64_t)qo * Hq + h) * DH;
 #pragma unroll
       for (int mbk = 0; mbk < NMB; ++mbk) {
         const int dh = 16 * mbk + 4 * g;
         if constexpr (sizeof(S) == 2) {
-          u32x2 w = {pack_bf16x2(acc[mbk][0] * inv, acc[mbk][1] * inv), pack_bf16x2(acc[mbk][2] * inv, acc[mbk][3] * inv)};
+          u32x2 w = {pack_bf16x2(acc[cb][mbk][0] * inv, acc[cb][mbk][1] * inv),
+                     pack_bf16x2(acc[cb][mbk][2] * inv, acc[cb][mbk][3] * inv)};
           *reinterpret_cast<u32x2*>(o + dh) = w;
         } else {
-          f32x4 w = acc[mbk] * inv;
+          f32x4 w = acc[cb][mbk] * inv;
           *reinterpret_cast<f32x4*>(o + dh) = w;
         }
       }
-      if (p.lse && g == 0) p.lse[(int64_t)qo * Hq + h] = l_run > 0.f ? m_run * p.scale + logf(l_run) : -INFINITY;
-    }
-  } else if (cact) {
-    const int64_t qh = ((int64_t)sp * p.num_q + qo) * Hq + h;
+      if (p.lse && g == 0)
+        p.lse[(int64_t)qo * Hq + h] = l_run[cb] > 0.f ? m_run[cb] * p.scale + logf(l_run[cb]) : -INFINITY;
+    } else {
+      const int64_t qh = ((int64_t)sp * p.num_q + qo) * Hq + h;
 #pragma unroll
-    for (int mbk = 0; mbk < NMB; ++mbk)
-      *reinterpret_cast<f32x4*>(p.part_o + qh * DH + 16 * mbk + 4 * g) = acc[mbk];
-    if (g == 0) {
-      p.part_ml[qh * 2 + 0] = m_run;
-      p.part_ml[qh * 2 + 1] = l_run;
+      for (int mbk = 0; mbk < NMB; ++mbk)
+        *reinterpret_cast<f32x4*>(p.part_o + qh * DH + 16 * mbk + 4 * g) = acc[cb][mbk];
+      if (g == 0) {
+        p.part_ml[qh * 2 + 0] = m_run[cb];
+        p.part_ml[qh * 2 + 1] = l_run[cb];
+      }
     }
-  }
-  if constexpr (DBG) {
-    for (int o = 16; o < 64; o <<= 1) {
-      dcnt += __shfl_xor(dcnt, o, 64);
-      dhsh += __shfl_xor(dhsh, o, 64);
-    }
-    if (cact && cg == 0 && g == 0) {
-      if (p.n_splits == 1) {
-        p.dbg_count[(int64_t)qo * Hkv + kvh] = dcnt;
-        p.dbg_hash[(int64_t)qo * Hkv + kvh] = dhsh;
-      } else {
-        const int64_t qk = ((int64_t)sp * p.num_q + qo) * Hkv + kvh;
-        p.part_dbg[qk * 2 + 0] = (uint64_t)dcnt;
-        p.part_dbg[qk * 2 + 1] = dhsh;
+    if constexpr (DBG) {
+      if (h % G == 0 && g == 0) {
+        if (p.n_splits == 1) {
+          p.dbg_count[(int64_t)qo * Hkv + kvh] = dcnt[cb];
+          p.dbg_hash[(int64_t)qo * Hkv + kvh] = dhsh[cb];
+        } else {
+          const int64_t qk = ((int64_t)sp * p.num_q + qo) * Hkv + kvh;
+          p.part_dbg[qk * 2 + 0] = (uint64_t)dcnt[cb];
+          p.part_dbg[qk * 2 + 1] = dhsh[cb];
+        }
       }
     }
   }
@@ -377,7 +525,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 template <typename S, int DH>
 static void launch_attn_t(const AttnParams& p, hipStream_t s) {
   const int G = p.Hq / p.Hkv;
-  const int QPW = 64 / G;
+  const int QPW = attn_queries_per_workgroup(G, DH);
   const int tps = (p.q_per_seg + QPW - 1) / QPW;
   const int grid = p.num_seg * tps * p.n_splits * p.Hkv;
   if (p.dbg_count) hipLaunchKernelGGL((attn_kernel<S, DH, true>), dim3(grid), dim3(256), 0, s, p, G, tps);

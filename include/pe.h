@@ -250,7 +250,9 @@ typedef struct {
     const void* v;          /* [num_kv_rows, Hkv, Dh]                          */
     const int32_t* seg_kv_base;  /* [num_seg]                                  */
     const int32_t* q_start;      /* [num_q] last prefix offset (-1 = none)     */
-    const int32_t* q_depth;      /* [num_q] or NULL (all 0); at most 64        */
+    const int32_t* q_depth;      /* [num_q] or NULL (all 0); at most 16 (8 when
+                                    n_q_heads == n_kv_heads); deeper chains
+                                    are cut at that depth                      */
     const int32_t* q_self_row;   /* [num_q] or NULL when q_depth is NULL       */
     const int32_t* kv_parent;    /* [num_kv_rows] or NULL when q_depth is NULL */
     int32_t max_prefix;     /* host bound on 1 + max q_start (work split only;
@@ -273,8 +275,12 @@ typedef struct {
  * keep every dependency across chunk boundaries.  Here the mask is evaluated
  * from indices inside the kernel and never stored; a chunk of queries is a
  * call on a subset of queries (slice q, q_start, q_depth, q_self_row, q_rows)
- * with the full key arrays.  dbg_count/dbg_hash are accumulated by the same
- * loop that skips and masks keys.  Alignment: q, k, v, out 16 bytes.
+ * with the full key arrays.  A query's outputs are bitwise the same in a
+ * chunk that starts at a multiple of 256 queries (of its segment) as in one
+ * call over all queries, for the same nonzero split_len (split_len 0 picks
+ * the split from the launch size, which may change the summation order).
+ * dbg_count/dbg_hash are accumulated by the same loop that skips and masks
+ * keys.  Alignment: q, k, v, out 16 bytes.
  * Workspace: pe_draft_attention_workspace (256-byte aligned).
  */
 pe_status pe_draft_attention(const pe_attn_args* args, void* workspace,

@@ -107,9 +107,11 @@ def lm_head_argmax(x, final_gain, w_lm, eps, dtype="f64", chunk=16384, keep_logi
     """f = RMSNorm(x); z = W_lm f; token = lowest index of the maximum.
 
     ``w_lm`` may be in storage dtype ("bf16" bits or "f32"); it is upcast to
-    float64 one vocabulary slice at a time.  Returns (tokens, gap, logits)
-    where gap is the difference between the largest and second-largest
-    logit of each row (0 on ties) and logits is None unless kept.
+    float64 one vocabulary slice at a time.  Returns (tokens, gap, logits,
+    rms) where gap is the difference between the largest and second-largest
+    logit of each row (0 on ties), logits is None unless kept and rms is the
+    root mean square of each row's logits (the scale a tolerance on them is
+    stated in).
     """
     f = rmsnorm(np.asarray(x, dtype=np.float64), final_gain, eps)
     V = w_lm.shape[0]
@@ -118,10 +120,12 @@ def lm_head_argmax(x, final_gain, w_lm, eps, dtype="f64", chunk=16384, keep_logi
     best = np.full(n, -np.inf)
     second = np.full(n, -np.inf)
     tok = np.zeros(n, np.int64)
+    ss = np.zeros(n)
     for s in range(0, V, chunk):
         w = w_lm[s:s + chunk]
         w = bf16_to_f64(w) if dtype == "bf16" else np.asarray(w, dtype=np.float64)
         z = f @ w.T
+        ss += np.sum(z * z, axis=1)
         if keep_logits:
             logits[:, s:s + chunk] = z
         # running top-2; the first maximum wins ties, so an equal maximum in a
@@ -135,7 +139,7 @@ def lm_head_argmax(x, final_gain, w_lm, eps, dtype="f64", chunk=16384, keep_logi
         second = np.where(better, np.maximum(best, m2), np.maximum(second, m1))
         tok = np.where(better, s + j, tok)
         best = np.where(better, m1, best)
-    return tok, best - second, logits
+    return tok, best - second, logits, np.sqrt(ss / V)
 
 
 def drafter_forward(dims, weights, batch, kv_base, k_cache, v_cache, keep_logits=True):
@@ -144,7 +148,8 @@ def drafter_forward(dims, weights, batch, kv_base, k_cache, v_cache, keep_logits
     ``weights`` holds storage arrays as drawn (bf16 bits or float32), gains
     float32; ``k_cache``/``v_cache`` are storage arrays and are not modified
     (float64 copies are updated and returned).  Returns a dict with x0, the
-    written caches, x2 of the query rows, tokens, gaps and logits.
+    written caches, x2 of the query rows, tokens, gaps, logits and the rms of
+    each query row's logits.
     """
     dt = dims.dtype
     T = batch["T"]
@@ -162,7 +167,7 @@ def drafter_forward(dims, weights, batch, kv_base, k_cache, v_cache, keep_logits
     x2, o = decoder_layer(x0, batch, kv_base, kc, vc, W, dims.n_q_heads, dims.n_kv_heads,
                           dims.head_dim, dims.eps)
     xq = x2[batch["query_rows"]]
-    tok, gap, logits = lm_head_argmax(xq, np.asarray(weights["final_gain"], np.float64),
-                                      weights["w_lm"], dims.eps, dtype=dt, keep_logits=keep_logits)
+    tok, gap, logits, rms = lm_head_argmax(xq, np.asarray(weights["final_gain"], np.float64),
+                                           weights["w_lm"], dims.eps, dtype=dt, keep_logits=keep_logits)
     return dict(x0=x0, k_cache=kc, v_cache=vc, x_query=xq, attn_out=o, tokens=tok,
-                gap=gap, logits=logits)
+                gap=gap, logits=logits, logit_rms=rms)

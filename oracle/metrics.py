@@ -2,8 +2,9 @@
 
 Relative error of a tensor is max|x - ref| / max|ref| (an elementwise ratio
 is unbounded near zero).  Greedy tokens are compared only where the
-reference's top-2 logit gap exceeds the threshold: below it, rounding in a
-lower precision may legitimately pick the other token.
+reference's top-2 logit gap exceeds the threshold (a scalar or one value per
+row): below it, rounding in a lower precision may legitimately pick the
+other token.
 """
 import numpy as np
 

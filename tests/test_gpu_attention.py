@@ -90,10 +90,12 @@ def check_against_oracle(Lay, out, lse, cnt, hsh, queries, name):
 
 @pytest.mark.parametrize("dtype,heads,N,D,keep,loss", [
     ("bf16", (8, 2, 128), 150, 5, 0.7, 0.5),
-    ("bf16", (16, 4, 64), 97, 4, 0.6, 1.0),
-    ("f32", (8, 2, 128), 130, 5, 0.7, 0.5),
-    ("f32", (4, 4, 64), 70, 3, 1.0, 1.0),
+    ("bf16", (16, 4, 64), 150, 4, 0.6, 1.0),
+    ("f32", (8, 2, 128), 160, 5, 0.7, 0.5),
+    ("f32", (4, 4, 64), 140, 3, 1.0, 1.0),
     ("bf16", (32, 8, 128), 257, 8, 1.0, 1.0),
+    ("bf16", (64, 1, 128), 90, 4, 0.8, 1.0),
+    ("bf16", (8, 8, 128), 120, 5, 0.9, 0.7),
 ])
 def test_cod_small_layouts(dtype, heads, N, D, keep, loss):
     Lay = si.cod_case(N, D, keep, loss, 21, heads=heads, dtype=dtype)
@@ -103,13 +105,14 @@ def test_cod_small_layouts(dtype, heads, N, D, keep, loss):
     out, lse, cnt, hsh = run_cod(Dv, Lay)
     torch.cuda.synchronize()
     check_against_oracle(Lay, out, lse, cnt, hsh, np.arange(Lay["T"]), name)
-    # chunked == unchunked, bit for bit (chunks of 64 rows and a ragged tail), with a
+    # chunked == unchunked, bit for bit (chunks of 256 rows and a ragged tail), with a
     # fixed split of the prefix range so that several splits and the combine are active
+    assert Lay["T"] > 256
     out1, lse1, _, _ = run_cod(Dv, Lay, dbg=False, split_len=64)
     out2 = torch.empty_like(out)
     lse2 = torch.empty_like(lse)
-    for c0 in range(0, Lay["T"], 64):
-        c1 = min(Lay["T"], c0 + 64)
+    for c0 in range(0, Lay["T"], 256):
+        c1 = min(Lay["T"], c0 + 256)
         run_cod(Dv, Lay, c0, c1, out=out2[c0:c1], lse=lse2[c0:c1], dbg=False, split_len=64)
     torch.cuda.synchronize()
     assert np.array_equal(bits(out2), bits(out1)) and np.array_equal(bits(lse2), bits(lse1))

@@ -130,9 +130,10 @@ def test_argmax_ties_and_slices():
     d, V = 8, 700
     w = g.integers(-3, 4, (V, d)).astype(np.float64)
     x = g.choice([-1.0, 1.0], (6, d))
-    tok, gap, logits = od.lm_head_argmax(x, np.ones(d), w, 0.0, dtype="f64", chunk=128)
+    tok, gap, logits, rms = od.lm_head_argmax(x, np.ones(d), w, 0.0, dtype="f64", chunk=128)
     z = x @ w.T
     np.testing.assert_array_equal(logits, z)
+    np.testing.assert_allclose(rms, np.sqrt(np.mean(z * z, axis=1)), rtol=1e-14)
     np.testing.assert_array_equal(tok, np.argmax(z, axis=1))     # first maximum
     srt = np.sort(z, axis=1)
     np.testing.assert_array_equal(gap, srt[:, -1] - srt[:, -2])
