@@ -9,22 +9,26 @@
 // exists, and key tiles beyond the largest prefix of a workgroup's queries
 // are never touched.
 //
-// Work unit: one workgroup = one kv head x 256 columns (128 at head_dim
-// 128), a column being a (query, q-head) pair of that kv head's GQA group
-// (256/G queries of G heads), optionally restricted to one split of the
-// prefix range (decode shapes: few queries, long regions).  4 waves x 64
-// columns (blocks of 16).  Per 64-key tile:
+// Work unit: one workgroup = one kv head x 128 columns, a column being a
+// (query, q-head) pair of that kv head's GQA group (128/G queries of G
+// heads), optionally restricted to one split of the prefix range (decode
+// shapes: few queries, long regions).  4 waves x 32 columns (two blocks of
+// 16); two workgroups share a CU, so each SIMD interleaves two waves' matrix
+// and vector work.  Per 64-key tile:
 //   * the tile is staged in LDS (K row-major, V transposed as V^T[dh][key] so
 //     both matrix-core operands read contiguous runs); two LDS buffers and a
 //     register prefetch of the next tile leave one barrier per tile and keep
 //     the next tile's HBM reads in flight while this one is multiplied;
 //   * S^T = K Q^T on the matrix cores (A = K rows from LDS, B = Q columns kept
-//     in registers for the whole kernel): each 1 KB operand read from LDS
-//     feeds every column block of the wave;
+//     in registers for the whole kernel), each LDS operand feeding both
+//     column blocks;
 //   * masking (skipped on tiles every column of the wave sees in full) and an
 //     online softmax in fp32 (exp2 with the log2(e)-folded scale); each lane's
-//     column is fixed, so the rescale of the running output is per lane;
-//   * O^T += V^T P^T on the matrix cores (P rounded to the operand type).
+//     column is fixed, so the rescale of the running output is per lane, and
+//     the running maximum moves only when it grows by more than 2^8;
+//   * O^T += V^T P^T on the matrix cores (P rounded to the operand type); the
+//     row sums l come from the same products, through a V^T block whose first
+//     row is all ones, so l sums exactly the rounded P that weights V.
 // A wave skips the multiplications of tiles none of its columns can see.
 // Chain rows are gathered into extra tiles whose mask is "owner == column's
 // query"; a row shared by several chains appears once per owner.  Splits
@@ -39,37 +43,71 @@
 #include <math.h>
 #include "kernels.h"
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
 namespace pe {
 
 constexpr int KT = 64;          // keys per tile
 constexpr int NWAVE = 4;        // waves per workgroup
+constexpr int CBLK = 2;         // 16-column blocks per wave
+constexpr int QMAX = NWAVE * CBLK * 16;  // columns per workgroup
 constexpr int MAXD = 16;        // deepest chain walked per query
-constexpr int ANC_MAX = 2048;   // chain rows gathered per workgroup
+constexpr int ANC_MAX = 1024;   // chain rows gathered per workgroup
 
-// 16-column blocks per wave: four at head_dim 64; two at 128, where four
-// would not fit the register file.
-__host__ __device__ constexpr int attn_col_blocks(int DH) { return DH >= 128 ? 2 : 4; }
+int attn_queries_per_workgroup(int G, int) { return QMAX / G; }
 
-int attn_queries_per_workgroup(int G, int head_dim) { return NWAVE * attn_col_blocks(head_dim) * 16 / G; }
+// Maxima of scores, which are products or -inf and never signalling NaNs:
+// the plain instructions, without the quieting copies the compiler adds to
+// fmaxf operands.
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Max and sum over the four lanes r, r+16, r+32, r+48 (one matrix-core
+// column), with the gfx950 lane-swap instructions: after a swap of the two
+// 32-lane halves (then of the 16-lane rows within them) every lane holds its
+// own value and its partner's.
+__device__ __forceinline__ float colgroup_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float colgroup_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <typename S, int DH, bool DBG>
-__global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps) {
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int tps) {
+  constexpr bool BF = sizeof(S) == 2;
   constexpr int CH = Storage<S>::CH;
   constexpr int STEP = 4 * CH;
   constexpr int NST = DH / STEP;
   constexpr int NMB = DH / 16;
   constexpr int DC = DH / CH;                    // 16-byte chunks per head row
-  constexpr int KPITCH = DC + 1;                 // Ks row pitch, 16-byte units
-  constexpr int VPB = KT * (int)sizeof(S) + 16;  // Vt row pitch, bytes
-  constexpr int KLD = (KT * DC + 255) / 256;     // K chunks each thread moves per tile
-  constexpr int VTS = (16 * DC + 255) / 256;     // V tasks (4 keys x CH dims) per thread per tile
-  constexpr int CBLK = attn_col_blocks(DH);
-  constexpr int QMAX = NWAVE * CBLK * 16;        // columns (queries at G = 1) per workgroup
-  __shared__ u32x4 Ks[2][KT * KPITCH];
-  __shared__ __attribute__((aligned(16))) char Vt[2][DH * VPB];
-  __shared__ int s_start[QMAX], s_cnt[QMAX], s_self[QMAX], s_off[QMAX + 1];
-  __shared__ int s_anc_row[ANC_MAX];
-  __shared__ __attribute__((aligned(16))) int s_anc_own[ANC_MAX];  // -1 past the last entry of a tile
+  constexpr int KPB = DH * (int)sizeof(S) + 16;  // K row pitch, bytes
+  // bf16: V row-major (pitch DH*2 + 32), read transposed by ds_read_b64_tr_b16;
+  // f32: V^T[dh][key] (pitch KT*4 + 16), written transposed
+  constexpr int VPB = BF ? DH * 2 + 32 : KT * 4 + 16;
+  constexpr int VBYTES = BF ? KT * VPB : DH * VPB;
+  constexpr int NCH = (KT * DC + 255) / 256;     // 16-byte chunks of K (and of V) per thread per tile
+  constexpr int NB = BF ? 1 : 2;                 // 16-key blocks per P^T operand of one half tile
+  static_assert(2 * NCH <= 32, "valid-row bits");
+  __shared__ __attribute__((aligned(16))) char Ks[2][KT * KPB];
+  __shared__ __attribute__((aligned(16))) char Vs[2][VBYTES];
+  __shared__ int s_start[QMAX], s_off[QMAX + 1];
+  __shared__ int s_anc_row[ANC_MAX];                               // chain rows, then
+  __shared__ __attribute__((aligned(16))) int s_anc_own[ANC_MAX];  // -1 to the end of the tile
   __shared__ int s_red[8];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -106,11 +144,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
       }
     }
   }
-  if (tid < QMAX) {
-    s_start[tid] = st;
-    s_cnt[tid] = cnt;
-    s_self[tid] = self;
-  }
+  if (tid < QMAX) s_start[tid] = st;
   int incl = cnt;
   for (int o = 1; o < 64; o <<= 1) {
     const int v = __shfl_up(incl, o, 64);
@@ -138,7 +172,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
   }
   if (tid < KT) {  // pad the last chain tile (ANC_MAX is a multiple of KT)
     const int e = n_anc_all + tid;
-    if (e < ((n_anc_all + KT - 1) / KT) * KT) s_anc_own[e] = -1;
+    if (e < ((n_anc_all + KT - 1) / KT) * KT) {
+      s_anc_own[e] = -1;
+      s_anc_row[e] = -1;
+    }
   }
   __syncthreads();
   const int n_anc = (sp == 0) ? n_anc_all : 0;
@@ -175,6 +212,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
       qreg[cb][t] = (qrow >= 0) ? ld16(Q + (int64_t)qrow * p.q_stride + (int64_t)hh[cb] * DH + t * STEP + g * CH)
                                 : u32x4{0u, 0u, 0u, 0u};
   }
+  // the Q operands are complete before the tile loop, whose global loads
+  // are then only the next tile's
+#pragma unroll
+  for (int cb = 0; cb < CBLK; ++cb)
+#pragma unroll
+    for (int t = 0; t < NST; ++t) asm volatile("" : : "v"(qreg[cb][t]));
   for (int o = 32; o > 0; o >>= 1) {
     lo = min(lo, __shfl_xor(lo, o, 64));
     hi = max(hi, __shfl_xor(hi, o, 64));
@@ -186,87 +229,71 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
   const int wq0 = min(wave * CBLK * 16 / G, nq), wq1 = min(((wave + 1) * CBLK * 16 + G - 1) / G, nq);
   const int wa0 = s_off[wq0], wa1 = s_off[wq1];
 
-  float m_run[CBLK], l_run[CBLK];
-  f32x4 acc[CBLK][NMB];
+  float m_run[CBLK];
+  f32x4 acc[CBLK][NMB], lsum[CBLK];
   int64_t dcnt[CBLK];
   uint64_t dhsh[CBLK];
 #pragma unroll
   for (int cb = 0; cb < CBLK; ++cb) {
     m_run[cb] = -INFINITY;
-    l_run[cb] = 0.f;
+    lsum[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     dcnt[cb] = 0;
     dhsh[cb] = 0;
 #pragma unroll
     for (int i = 0; i < NMB; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sl2 = p.scale_log2;
+  // A operand whose row 0 is all ones: its product with P^T is the column sum
+  const uint32_t one = BF ? 0x3F803F80u : 0x3F800000u;
+  const u32x4 ones = (r == 0) ? u32x4{one, one, one, one} : u32x4{0u, 0u, 0u, 0u};
 
-  // ---- tile staging: key rows by arithmetic (prefix) or from the chain list.
-  // Branch-free: every thread loads from a clamped row and zeroes invalid
-  // rows when it writes LDS (a zero V row keeps 0 * V finite).
+  // ---- tile staging.  Thread chunk i covers key (tid + 256 i) / DC, 16-byte
+  // chunk (tid + 256 i) % DC of both K and V.  Key rows come by arithmetic
+  // (prefix tiles) or from the chain list (one uniform branch per tile);
+  // every thread loads from a clamped row and zeroes invalid rows when it
+  // writes LDS (a zero V row keeps 0 * V finite).
   const bool have_rows = p.num_kv_rows > 0;
-  auto tile_row = [&](int it, int key) -> int {
-    const int pos = kbeg + it * KT + key;
-    const int ai = (it - n_pref) * KT + key;
-    const int arow = s_anc_row[min(max(ai, 0), ANC_MAX - 1)];
-    const int row = (it < n_pref) ? (pos <= kend ? seg_base + pos : -1) : (ai < n_anc ? arow : -1);
-    return (row >= 0 && row < p.num_kv_rows) ? row : -1;
-  };
-  u32x4 kreg[KLD], vreg[VTS][4];
-  uint32_t kok = 0, vok = 0;  // valid-row bits of the staged chunks
+  u32x4 kreg[NCH], vreg[NCH];
+  uint32_t ok_bits = 0;
   auto load_tile = [&](int it) {
-    kok = 0;
-    vok = 0;
+    int row[NCH];
+    if (it < n_pref) {
+      const int p0 = kbeg + it * KT;
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int c = tid + i * 256;
-      const int key = (c / DC) & (KT - 1), ch = c % DC;
-      const int row = tile_row(it, key);
-      kok |= (uint32_t)(row >= 0) << i;
-      kreg[i] = ld16(Kg + ((int64_t)max(row, 0) * Hkv + kvh) * DH + ch * CH);
-    }
-#pragma unroll
-    for (int i = 0; i < VTS; ++i) {
-      const int t = tid + i * 256;
-      const int kg = t & 15, dc = (t >> 4) % DC;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = tile_row(it, kg * 4 + q);
-        vok |= (uint32_t)(row >= 0) << (4 * i + q);
-        vreg[i][q] = ld16(Vg + ((int64_t)max(row, 0) * Hkv + kvh) * DH + dc * CH);
+      for (int i = 0; i < NCH; ++i) {
+        const int key = ((tid + i * 256) / DC) & (KT - 1);
+        row[i] = (p0 + key <= kend) ? seg_base + p0 + key : -1;
       }
+    } else {
+      const int a0 = (it - n_pref) * KT;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) row[i] = s_anc_row[a0 + (((tid + i * 256) / DC) & (KT - 1))];
+    }
+    ok_bits = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const bool ok = row[i] >= 0 && row[i] < p.num_kv_rows;
+      ok_bits |= (uint32_t)ok << i;
+      const int64_t off = ((int64_t)(ok ? row[i] : 0) * Hkv + kvh) * DH + ((tid + i * 256) % DC) * CH;
+      kreg[i] = ld16(Kg + off);
+      vreg[i] = ld16(Vg + off);
     }
   };
   auto store_tile = [&](int buf) {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * 256;
-      if (c < KT * DC) Ks[buf][(c / DC) * KPITCH + c % DC] = ((kok >> i) & 1) ? kreg[i] : z;
-    }
-#pragma unroll
-    for (int i = 0; i < VTS; ++i) {
-      const int t = tid + i * 256;
-      if (t >= 16 * DC) continue;
-      const int kg = t & 15, dc = t >> 4;
-      u32x4 v4[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v4[q] = ((vok >> (4 * i + q)) & 1) ? vreg[i][q] : z;
-      if constexpr (sizeof(S) == 2) {
-#pragma unroll
-        for (int e = 0; e < CH; ++e) {
-          const int sh = 16 * (e & 1);
-          const uint32_t a0 = (v4[0][e >> 1] >> sh) & 0xffffu, a1 = (v4[1][e >> 1] >> sh) & 0xffffu;
-          const uint32_t a2 = (v4[2][e >> 1] >> sh) & 0xffffu, a3 = (v4[3][e >> 1] >> sh) & 0xffffu;
-          u32x2 w = {a0 | (a1 << 16), a2 | (a3 << 16)};
-          *reinterpret_cast<u32x2*>(&Vt[buf][(dc * CH + e) * VPB + kg * 8]) = w;
-        }
+      if (c >= KT * DC) continue;
+      const int key = c / DC, ch = c % DC;
+      const bool ok = (ok_bits >> i) & 1;
+      *reinterpret_cast<u32x4*>(&Ks[buf][key * KPB + ch * 16]) = ok ? kreg[i] : z;
+      const u32x4 v = ok ? vreg[i] : z;
+      if constexpr (BF) {
+        *reinterpret_cast<u32x4*>(&Vs[buf][key * VPB + ch * 16]) = v;
       } else {
 #pragma unroll
-        for (int e = 0; e < CH; ++e) {
-          u32x4 w = {v4[0][e], v4[1][e], v4[2][e], v4[3][e]};
-          *reinterpret_cast<u32x4*>(&Vt[buf][(dc * CH + e) * VPB + kg * 16]) = w;
-        }
+        for (int e = 0; e < CH; ++e) *reinterpret_cast<uint32_t*>(&Vs[buf][(ch * CH + e) * VPB + key * 4]) = v[e];
       }
     }
   };
@@ -284,144 +311,146 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
     const bool skip = anc ? (k0 + KT <= wa0 || k0 >= wa1) : (k0 > wmax);
     if (skip) continue;
     const bool full = !DBG && !anc && (k0 + KT - 1 <= wmin);
+    const char* Kb = Ks[buf];
+    const char* Vb = Vs[buf];
 
-    // S^T = K Q^T: each K operand read once, used for every column block
-    f32x4 sacc[CBLK][4];
+    // Two halves of 32 keys: S^T = K Q^T, mask, online softmax, then
+    // O^T += V^T P^T and l += 1^T P^T.  This lane holds keys
+    // k0 + 16b + 4g + j (b = 2h, 2h+1; j < 4) of its columns.
 #pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb)
+    for (int h = 0; h < 2; ++h) {
+      f32x4 sacc[CBLK][2];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) sacc[cb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < CBLK; ++cb) sacc[cb][0] = sacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int t = 0; t < NST; ++t) {
-        const u32x4 a = Ks[buf][(16 * b + r) * KPITCH + t * 4 + g];
+        for (int t = 0; t < NST; ++t) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(Kb + (16 * (2 * h + bb) + r) * KPB + (4 * t + g) * 16);
 #pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) mma16(sacc[cb][b], a, qreg[cb][t], S());
+          for (int cb = 0; cb < CBLK; ++cb) mma16(sacc[cb][bb], a, qreg[cb][t], S());
+        }
+
+      // Mask in place: chain keys are visible to the column whose query owns
+      // them (the owner list is padded with -1); a prefix key is visible
+      // while it is <= the column's limit.  Tiles every column of the wave
+      // sees in full are left unmasked.
+      if (anc) {
+        int own[8];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const u32x4 o4 = *reinterpret_cast<const u32x4*>(&s_anc_own[k0 + 16 * (2 * h + bb) + 4 * g]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) own[4 * bb + j] = (int)o4[j];
+        }
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb)
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              sacc[cb][bb][j] = (own[4 * bb + j] == cq[cb]) ? sacc[cb][bb][j] : -INFINITY;
+      } else if (!full) {
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) {
+          const int d = climit[cb] - k0 - 4 * g;
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              sacc[cb][bb][j] = (16 * (2 * h + bb) + j <= d) ? sacc[cb][bb][j] : -INFINITY;
+        }
+      }
+      if constexpr (DBG) {
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) {
+          const int d = climit[cb] - k0 - 4 * g;
+          for (int i = 0; i < 8; ++i) {
+            const int bq = 2 * h + (i >> 2), j = i & 3;
+            const int kk = 16 * bq + 4 * g + j;
+            const bool vis = anc ? (s_anc_own[k0 + kk] == cq[cb]) : (16 * bq + j <= d);
+            if (vis) {
+              const int row = anc ? s_anc_row[k0 + kk] : seg_base + k0 + kk;
+              ++dcnt[cb];
+              dhsh[cb] += mix64((uint64_t)(uint32_t)row);
+            }
+          }
+        }
       }
 
-    // Mask in place.  This lane holds keys 16b + 4g + j (b, j < 4) of its
-    // columns.  Chain keys are visible to the column whose query owns them
-    // (the owner list is padded with -1); a prefix key k0 + 16b + 4g + j is
-    // visible while it is <= the column's limit.  Tiles that every column of
-    // the wave sees in full are left unmasked.
-    if (anc) {
-      int own[16];
+      // online softmax per column block; P^T packed for the next product
+      u32x4 bop[CBLK][NB];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const u32x4 o4 = *reinterpret_cast<const u32x4*>(&s_anc_own[k0 + 16 * b + 4 * g]);
+      for (int cb = 0; cb < CBLK; ++cb) {
+        const f32x4* sc = sacc[cb];
+        float tmax = max3(max3(sc[0][0], sc[0][1], sc[0][2]), max3(sc[0][3], sc[1][0], sc[1][1]),
+                          max3(sc[1][2], sc[1][3], -INFINITY));
+        tmax = colgroup_max(tmax);
+        // The running maximum m moves only when a column's maximum grows by
+        // more than 2^8 in exp2 units (so P <= 2^8 between moves; the final
+        // division by l removes m exactly), which makes the rescale rare.
+        const bool grow = (tmax - m_run[cb]) * sl2 > 8.0f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          // alpha is 1 on lanes that keep m (m may still be -inf there)
+          const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[cb] - tmax) * sl2) : 1.0f;
+          lsum[cb] *= alpha;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) own[4 * b + j] = (int)o4[j];
+          for (int i = 0; i < NMB; ++i) acc[cb][i] *= alpha;
+          m_run[cb] = grow ? tmax : m_run[cb];
+        }
+        const float mb = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb] * sl2;
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 2][i & 3], sl2, -mb));
+        if constexpr (BF) {
+          bop[cb][0] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                             pack_bf16x2(pv[6], pv[7])};
+        } else {
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+            bop[cb][bb] = u32x4{__float_as_uint(pv[4 * bb]), __float_as_uint(pv[4 * bb + 1]),
+                                __float_as_uint(pv[4 * bb + 2]), __float_as_uint(pv[4 * bb + 3])};
+        }
+      }
+
+      // O^T += V^T P^T: each V^T operand read once, used for every column block
+#pragma unroll
+      for (int mbk = 0; mbk < NMB; ++mbk) {
+        if constexpr (BF) {
+          // Lane 4c + m of a 16-lane group addresses dims 16 mbk + 4m .. +3 of
+          // key 32h + 16s + 4g + c; lane r then receives dim 16 mbk + r of the
+          // four keys c = 0..3 (slots 4s + c of the operand).
+          typedef __attribute__((address_space(3))) short4_t lds_s4;
+          const int kr = 32 * h + 4 * g + (r >> 2);
+          const char* vp = Vb + kr * VPB + (16 * mbk + 4 * (r & 3)) * 2;
+          const auto lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp));
+          const auto hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp + 16 * VPB));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
+          const u32x4 aop = {l2.x, l2.y, h2.x, h2.y};
+#pragma unroll
+          for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][0], S());
+        } else {
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            const u32x4 aop =
+                *reinterpret_cast<const u32x4*>(Vb + (16 * mbk + r) * VPB + (16 * (2 * h + bb) + 4 * g) * 4);
+#pragma unroll
+            for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][bb], S());
+          }
+        }
       }
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            sacc[cb][b][j] = (own[4 * b + j] == cq[cb]) ? sacc[cb][b][j] : -INFINITY;
-    } else if (!full) {
-#pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) {
-        const int d = climit[cb] - k0 - 4 * g;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sacc[cb][b][j] = (16 * b + j <= d) ? sacc[cb][b][j] : -INFINITY;
-      }
-    }
-    if constexpr (DBG) {
-#pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) {
-        const int d = climit[cb] - k0 - 4 * g;
-        for (int i = 0; i < 16; ++i) {
-          const int kk = 16 * (i >> 2) + 4 * g + (i & 3);
-          const bool vis = anc ? (s_anc_own[k0 + kk] == cq[cb]) : (16 * (i >> 2) + (i & 3) <= d);
-          if (vis) {
-            const int row = anc ? s_anc_row[k0 + kk] : seg_base + k0 + kk;
-            ++dcnt[cb];
-            dhsh[cb] += mix64((uint64_t)(uint32_t)row);
-          }
-        }
-      }
-    }
-
-    // online softmax per column block; P^T packed for the next product
-    u32x4 bop[CBLK][sizeof(S) == 2 ? 2 : 4];
-#pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb) {
-      float sv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sv[i] = sacc[cb][i >> 2][i & 3];
-      float tmax = sv[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sv[i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      // The running maximum m is moved only when a column's maximum grows by
-      // more than 2^8 in exp2 units (then P <= 2^8 between moves; the final
-      // division by l removes m exactly), so the rescale of O and l is rare.
-      const bool grow = (tmax - m_run[cb]) * sl2 > 8.0f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        // alpha is 1 on lanes that keep m (m may still be -inf there)
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[cb] - tmax) * sl2) : 1.0f;
-        l_run[cb] *= alpha;
-#pragma unroll
-        for (int i = 0; i < NMB; ++i) acc[cb][i] *= alpha;
-        m_run[cb] = grow ? tmax : m_run[cb];
-      }
-      const float mb = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb] * sl2;
-      float pv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, -mb));
-        l_run[cb] += pv[i];
-      }
-      if constexpr (sizeof(S) == 2) {
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const int b0 = 2 * pr;
-          bop[cb][pr] = u32x4{pack_bf16x2(pv[4 * b0 + 0], pv[4 * b0 + 1]), pack_bf16x2(pv[4 * b0 + 2], pv[4 * b0 + 3]),
-                              pack_bf16x2(pv[4 * b0 + 4], pv[4 * b0 + 5]), pack_bf16x2(pv[4 * b0 + 6], pv[4 * b0 + 7])};
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          bop[cb][b] = u32x4{__float_as_uint(pv[4 * b]), __float_as_uint(pv[4 * b + 1]), __float_as_uint(pv[4 * b + 2]),
-                             __float_as_uint(pv[4 * b + 3])};
-      }
-    }
-
-    // O^T += V^T P^T: each V^T operand read once, used for every column block
-    if constexpr (sizeof(S) == 2) {
-#pragma unroll
-      for (int mbk = 0; mbk < NMB; ++mbk)
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const char* vrow = &Vt[buf][(16 * mbk + r) * VPB];
-          const u32x2 vlo = *reinterpret_cast<const u32x2*>(vrow + (32 * pr + 4 * g) * 2);
-          const u32x2 vhi = *reinterpret_cast<const u32x2*>(vrow + (32 * pr + 16 + 4 * g) * 2);
-          const u32x4 aop = {vlo.x, vlo.y, vhi.x, vhi.y};
-#pragma unroll
-          for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][pr], S());
-        }
-    } else {
-#pragma unroll
-      for (int mbk = 0; mbk < NMB; ++mbk)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const u32x4 aop = *reinterpret_cast<const u32x4*>(&Vt[buf][(16 * mbk + r) * VPB + (16 * b + 4 * g) * 4]);
-#pragma unroll
-          for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][b], S());
-        }
+        for (int bb = 0; bb < NB; ++bb) mma16(lsum[cb], ones, bop[cb][bb], S());
     }
   }
 
-  // ---- epilogue (l_run holds this lane's share of the row sum)
+  // ---- epilogue.  l of column r is row 0 of lsum (lane g = 0, element 0;
+  // the other lanes of the column hold 0 there).
 #pragma unroll
   for (int cb = 0; cb < CBLK; ++cb) {
-    l_run[cb] += __shfl_xor(l_run[cb], 16, 64);
-    l_run[cb] += __shfl_xor(l_run[cb], 32, 64);
+    const float l_run = colgroup_sum(lsum[cb][0]);
     if constexpr (DBG) {
       for (int o = 16; o < 64; o <<= 1) {
         dcnt[cb] += __shfl_xor(dcnt[cb], o, 64);
@@ -432,12 +461,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
     const int qo = qbase + cq[cb];
     const int h = hh[cb];
     if (p.n_splits == 1) {
-      const float inv = l_run[cb] > 0.f ? 1.0f / l_run[cb] : 0.f;
+      const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
       S* o = reinterpret_cast<S*>(p.out) + ((int64_t)qo * Hq + h) * DH;
 #pragma unroll
       for (int mbk = 0; mbk < NMB; ++mbk) {
         const int dh = 16 * mbk + 4 * g;
-        if constexpr (sizeof(S) == 2) {
+        if constexpr (BF) {
           u32x2 w = {pack_bf16x2(acc[cb][mbk][0] * inv, acc[cb][mbk][1] * inv),
                      pack_bf16x2(acc[cb][mbk][2] * inv, acc[cb][mbk][3] * inv)};
           *reinterpret_cast<u32x2*>(o + dh) = w;
@@ -447,7 +476,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
         }
       }
       if (p.lse && g == 0)
-        p.lse[(int64_t)qo * Hq + h] = l_run[cb] > 0.f ? m_run[cb] * p.scale + logf(l_run[cb]) : -INFINITY;
+        p.lse[(int64_t)qo * Hq + h] = l_run > 0.f ? m_run[cb] * p.scale + logf(l_run) : -INFINITY;
     } else {
       const int64_t qh = ((int64_t)sp * p.num_q + qo) * Hq + h;
 #pragma unroll
@@ -455,7 +484,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p, int G, int tps)
         *reinterpret_cast<f32x4*>(p.part_o + qh * DH + 16 * mbk + 4 * g) = acc[cb][mbk];
       if (g == 0) {
         p.part_ml[qh * 2 + 0] = m_run[cb];
-        p.part_ml[qh * 2 + 1] = l_run[cb];
+        p.part_ml[qh * 2 + 1] = l_run;
       }
     }
     if constexpr (DBG) {

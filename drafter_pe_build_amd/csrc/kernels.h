@@ -108,8 +108,8 @@ struct AttnParams {
   uint64_t* part_dbg;  // [n_splits, num_q*Hkv, 2]
 };
 void launch_attention(const AttnParams& p, int bf16, int head_dim, hipStream_t s);
-// Queries one attention workgroup takes: 256 (query, head) columns of one kv
-// head at head_dim 64, 128 at head_dim 128.
+// Queries one attention workgroup takes: 128 (query, head) columns of one kv
+// head, i.e. 128 / (n_q_heads / n_kv_heads) queries.
 int attn_queries_per_workgroup(int G, int head_dim);
 
 }  // namespace pe
