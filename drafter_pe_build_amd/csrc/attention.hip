@@ -229,13 +229,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   const int wq0 = min(wave * CBLK * 16 / G, nq), wq1 = min(((wave + 1) * CBLK * 16 + G - 1) / G, nq);
   const int wa0 = s_off[wq0], wa1 = s_off[wq1];
 
-  float m_run[CBLK];
+  // m_run: running maximum (raw score units); thr = m_run + thr_gap; mb =
+  // m_run * scale * log2 e (0 while no score has been seen, m_run = -inf)
+  float m_run[CBLK], thr[CBLK], mb[CBLK];
   f32x4 acc[CBLK][NMB], lsum[CBLK];
   int64_t dcnt[CBLK];
   uint64_t dhsh[CBLK];
 #pragma unroll
   for (int cb = 0; cb < CBLK; ++cb) {
     m_run[cb] = -INFINITY;
+    thr[cb] = -INFINITY;
+    mb[cb] = 0.f;
     lsum[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     dcnt[cb] = 0;
     dhsh[cb] = 0;
@@ -243,57 +247,62 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
     for (int i = 0; i < NMB; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sl2 = p.scale_log2;
+  const float thr_gap = 8.0f / sl2;
   // A operand whose row 0 is all ones: its product with P^T is the column sum
   const uint32_t one = BF ? 0x3F803F80u : 0x3F800000u;
   const u32x4 ones = (r == 0) ? u32x4{one, one, one, one} : u32x4{0u, 0u, 0u, 0u};
 
   // ---- tile staging.  Thread chunk i covers key (tid + 256 i) / DC, 16-byte
-  // chunk (tid + 256 i) % DC of both K and V.  Key rows come by arithmetic
-  // (prefix tiles) or from the chain list (one uniform branch per tile);
-  // every thread loads from a clamped row and zeroes invalid rows when it
-  // writes LDS (a zero V row keeps 0 * V finite).
+  // chunk (tid + 256 i) % DC of both K and V.  Keys a tile does not hold for
+  // anyone (past the prefix end, padding of the last chain tile) load a row
+  // the tile does hold - the prefix end, the tile's first chain row - so
+  // every staged value is one some column attends (finite for meaningful
+  // inputs) and the mask gives it P = 0.  Prefix tiles address from a
+  // uniform base; chain tiles per row.  Rows stay inside [0, num_kv_rows).
   const bool have_rows = p.num_kv_rows > 0;
+  const int last_row = p.num_kv_rows - 1;
+  const int64_t rstride = (int64_t)Hkv * DH;  // elements between K (V) rows
   u32x4 kreg[NCH], vreg[NCH];
-  uint32_t ok_bits = 0;
   auto load_tile = [&](int it) {
-    int row[NCH];
     if (it < n_pref) {
       const int p0 = kbeg + it * KT;
+      const int row0 = max(min(seg_base + p0, last_row), 0);
+      const int room = max(min(kend - p0, last_row - row0), 0);  // keys past it repeat the last held row
+      const S* kb = Kg + (int64_t)row0 * rstride + kvh * DH;
+      const S* vb = Vg + (int64_t)row0 * rstride + kvh * DH;
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int key = ((tid + i * 256) / DC) & (KT - 1);
-        row[i] = (p0 + key <= kend) ? seg_base + p0 + key : -1;
+        const int c = tid + i * 256;
+        const uint32_t off = (uint32_t)min(c / DC, room) * (uint32_t)rstride + (uint32_t)((c % DC) * CH);
+        kreg[i] = ld16(kb + off);
+        vreg[i] = ld16(vb + off);
       }
     } else {
       const int a0 = (it - n_pref) * KT;
+      const int first = s_anc_row[a0];
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) row[i] = s_anc_row[a0 + (((tid + i * 256) / DC) & (KT - 1))];
-    }
-    ok_bits = 0;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const bool ok = row[i] >= 0 && row[i] < p.num_kv_rows;
-      ok_bits |= (uint32_t)ok << i;
-      const int64_t off = ((int64_t)(ok ? row[i] : 0) * Hkv + kvh) * DH + ((tid + i * 256) % DC) * CH;
-      kreg[i] = ld16(Kg + off);
-      vreg[i] = ld16(Vg + off);
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + i * 256;
+        const int rw = s_anc_row[a0 + c / DC];
+        const int64_t off = (int64_t)(rw < 0 ? first : rw) * rstride + kvh * DH + (c % DC) * CH;
+        kreg[i] = ld16(Kg + off);
+        vreg[i] = ld16(Vg + off);
+      }
     }
   };
   auto store_tile = [&](int buf) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * 256;
       if (c >= KT * DC) continue;
       const int key = c / DC, ch = c % DC;
-      const bool ok = (ok_bits >> i) & 1;
-      *reinterpret_cast<u32x4*>(&Ks[buf][key * KPB + ch * 16]) = ok ? kreg[i] : z;
-      const u32x4 v = ok ? vreg[i] : z;
+      *reinterpret_cast<u32x4*>(&Ks[buf][key * KPB + ch * 16]) = kreg[i];
       if constexpr (BF) {
-        *reinterpret_cast<u32x4*>(&Vs[buf][key * VPB + ch * 16]) = v;
+        *reinterpret_cast<u32x4*>(&Vs[buf][key * VPB + ch * 16]) = vreg[i];
       } else {
 #pragma unroll
-        for (int e = 0; e < CH; ++e) *reinterpret_cast<uint32_t*>(&Vs[buf][(ch * CH + e) * VPB + key * 4]) = v[e];
+        for (int e = 0; e < CH; ++e)
+          *reinterpret_cast<uint32_t*>(&Vs[buf][(ch * CH + e) * VPB + key * 4]) = vreg[i][e];
       }
     }
   };
@@ -378,30 +387,33 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
         }
       }
 
-      // online softmax per column block; P^T packed for the next product
+      // online softmax per column block; P^T packed for the next product.
+      // The running maximum m of a column moves only when one of its scores
+      // exceeds thr = m + 8 / (scale log2 e), i.e. when P would pass 2^8 (the
+      // final division by l removes m exactly).  Each lane tests its own
+      // scores; the column maximum and the rescale run only when some lane
+      // of the wave is over.
       u32x4 bop[CBLK][NB];
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb) {
         const f32x4* sc = sacc[cb];
-        float tmax = max3(max3(sc[0][0], sc[0][1], sc[0][2]), max3(sc[0][3], sc[1][0], sc[1][1]),
-                          max3(sc[1][2], sc[1][3], -INFINITY));
-        tmax = colgroup_max(tmax);
-        // The running maximum m moves only when a column's maximum grows by
-        // more than 2^8 in exp2 units (so P <= 2^8 between moves; the final
-        // division by l removes m exactly), which makes the rescale rare.
-        const bool grow = (tmax - m_run[cb]) * sl2 > 8.0f;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          // alpha is 1 on lanes that keep m (m may still be -inf there)
-          const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[cb] - tmax) * sl2) : 1.0f;
+        const float lmax = max3(max3(sc[0][0], sc[0][1], sc[0][2]), max3(sc[0][3], sc[1][0], sc[1][1]),
+                                max3(sc[1][2], sc[1][3], -INFINITY));
+        if (__builtin_amdgcn_ballot_w64(lmax > thr[cb])) {
+          const float cmax = colgroup_max(lmax);
+          const bool grow = cmax > thr[cb];  // the same on the column's four lanes
+          // alpha is 1 on columns that keep m (m may still be -inf there)
+          const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[cb] - cmax) * sl2) : 1.0f;
           lsum[cb] *= alpha;
 #pragma unroll
           for (int i = 0; i < NMB; ++i) acc[cb][i] *= alpha;
-          m_run[cb] = grow ? tmax : m_run[cb];
+          m_run[cb] = grow ? cmax : m_run[cb];
+          thr[cb] = m_run[cb] + thr_gap;
+          mb[cb] = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb] * sl2;
         }
-        const float mb = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb] * sl2;
         float pv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 2][i & 3], sl2, -mb));
+        for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 2][i & 3], sl2, -mb[cb]));
         if constexpr (BF) {
           bop[cb][0] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                              pack_bf16x2(pv[6], pv[7])};
