@@ -38,6 +38,12 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + errs)
     if verbose and errs.strip():
         print(errs)
+    # every symbol must resolve (a kernel whose host stub was dropped links
+    # but cannot be loaded)
+    probe = subprocess.run([sys.executable, "-c", "import ctypes, os, sys; "
+                            "ctypes.CDLL(sys.argv[1], mode=os.RTLD_NOW)", tmp], capture_output=True, text=True)
+    if probe.returncode != 0:
+        raise RuntimeError("built library does not load:\n" + probe.stderr[-2000:])
     os.replace(tmp, LIB)
     return LIB
 

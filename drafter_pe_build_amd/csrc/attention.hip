@@ -70,6 +70,12 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return r;
 }
 
+// One 16-byte copy per lane from global memory straight into LDS: lane l
+// writes bytes [16 l, 16 l + 16) after the wave-uniform LDS address dst.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
 // Max and sum over the four lanes r, r+16, r+32, r+48 (one matrix-core
 // column), with the gfx950 lane-swap instructions: after a swap of the two
 // 32-lane halves (then of the 16-lane rows within them) every lane holds its
@@ -262,8 +268,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   const bool have_rows = p.num_kv_rows > 0;
   const int last_row = p.num_kv_rows - 1;
   const int64_t rstride = (int64_t)Hkv * DH;  // elements between K (V) rows
-  u32x4 kreg[NCH], vreg[NCH];
+  u32x4 kreg[BF ? 1 : NCH], vreg[BF ? 1 : NCH];  // f32: register staging
   auto load_tile = [&](int it) {
+    if constexpr (BF) return;
     if (it < n_pref) {
       const int p0 = kbeg + it * KT;
       const int row0 = max(min(seg_base + p0, last_row), 0);
@@ -291,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
     }
   };
   auto store_tile = [&](int buf) {
+    if constexpr (BF) return;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * 256;
@@ -307,155 +315,282 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
     }
   };
 
-  const int n_iter = have_rows ? n_tiles : 0;
-  if (n_iter > 0) load_tile(0);
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (it + 1 < n_iter) load_tile(it + 1);
-
-    const bool anc = it >= n_pref;
-    const int k0 = anc ? (it - n_pref) * KT : kbeg + it * KT;
-    const bool skip = anc ? (k0 + KT <= wa0 || k0 >= wa1) : (k0 > wmax);
-    if (skip) continue;
-    const bool full = !DBG && !anc && (k0 + KT - 1 <= wmin);
-    const char* Kb = Ks[buf];
-    const char* Vb = Vs[buf];
-
-    // Two halves of 32 keys: S^T = K Q^T, mask, online softmax, then
-    // O^T += V^T P^T and l += 1^T P^T.  This lane holds keys
-    // k0 + 16b + 4g + j (b = 2h, 2h+1; j < 4) of its columns.
+  // bf16: tiles are copied from global memory straight into LDS.  One
+  // 64-lane instruction fills 64 consecutive 16-byte slots of the padded
+  // layout (lane l -> slot l); a tile of K takes KPB / 16 of them, one of V
+  // VPB / 16, spread round-robin over the waves.  Lanes whose slot is row
+  // padding load chunk 0 of their row (never read back).  Each lane's slots
+  // are fixed, so a full prefix tile loads from a uniform base plus
+  // precomputed offsets; partial prefix tiles clamp the key, chain tiles look
+  // their rows up.
+  constexpr int KPS = KPB / 16, VPS = VPB / 16;       // 16-byte slots per padded row
+  constexpr int NDMA = BF ? KPS + VPS : 0;             // 1 KB copies per tile
+  constexpr int NDW = (NDMA + NWAVE - 1) / NWAVE;      // per wave
+  // key and 16-byte chunk (0 for padding) of copy q of this lane
+  auto dslot = [&](int q, int& key, int& ch) {
+    const int j = wave + NWAVE * q;
+    const bool isv = j >= KPS;
+    const int ps = isv ? VPS : KPS;
+    const int slot = (isv ? j - KPS : j) * 64 + lane;
+    key = slot / ps;
+    ch = (slot % ps < DC) ? slot % ps : 0;
+  };
+  uint32_t doff[BF ? NDW : 1];  // element offset of copy q within a full prefix tile
+  if constexpr (BF) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 sacc[CBLK][2];
+    for (int q = 0; q < NDW; ++q) {
+      int key, ch;
+      dslot(q, key, ch);
+      doff[q] = (uint32_t)key * (uint32_t)rstride + (uint32_t)(ch * CH);
+    }
+  }
+  auto dma_tile = [&](int it, int buf) {
+    if constexpr (BF) {
+      if (it < n_pref) {
+        const int p0 = kbeg + it * KT;
+        const int row0 = max(min(seg_base + p0, last_row), 0);
+        const int room = max(min(kend - p0, last_row - row0), 0);  // keys past it repeat the last held row
+        const bool whole = room >= KT - 1;
+        const S* kb = Kg + (int64_t)row0 * rstride + kvh * DH;
+        const S* vb = Vg + (int64_t)row0 * rstride + kvh * DH;
 #pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) sacc[cb][0] = sacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-        for (int t = 0; t < NST; ++t) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(Kb + (16 * (2 * h + bb) + r) * KPB + (4 * t + g) * 16);
-#pragma unroll
-          for (int cb = 0; cb < CBLK; ++cb) mma16(sacc[cb][bb], a, qreg[cb][t], S());
-        }
-
-      // Mask in place: chain keys are visible to the column whose query owns
-      // them (the owner list is padded with -1); a prefix key is visible
-      // while it is <= the column's limit.  Tiles every column of the wave
-      // sees in full are left unmasked.
-      if (anc) {
-        int own[8];
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          const u32x4 o4 = *reinterpret_cast<const u32x4*>(&s_anc_own[k0 + 16 * (2 * h + bb) + 4 * g]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) own[4 * bb + j] = (int)o4[j];
-        }
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb)
-#pragma unroll
-          for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              sacc[cb][bb][j] = (own[4 * bb + j] == cq[cb]) ? sacc[cb][bb][j] : -INFINITY;
-      } else if (!full) {
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) {
-          const int d = climit[cb] - k0 - 4 * g;
-#pragma unroll
-          for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              sacc[cb][bb][j] = (16 * (2 * h + bb) + j <= d) ? sacc[cb][bb][j] : -INFINITY;
-        }
-      }
-      if constexpr (DBG) {
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) {
-          const int d = climit[cb] - k0 - 4 * g;
-          for (int i = 0; i < 8; ++i) {
-            const int bq = 2 * h + (i >> 2), j = i & 3;
-            const int kk = 16 * bq + 4 * g + j;
-            const bool vis = anc ? (s_anc_own[k0 + kk] == cq[cb]) : (16 * bq + j <= d);
-            if (vis) {
-              const int row = anc ? s_anc_row[k0 + kk] : seg_base + k0 + kk;
-              ++dcnt[cb];
-              dhsh[cb] += mix64((uint64_t)(uint32_t)row);
-            }
+        for (int q = 0; q < NDW; ++q) {
+          const int j = wave + NWAVE * q;
+          if (j >= NDMA) break;
+          const bool isv = j >= KPS;
+          uint32_t off = doff[q];
+          if (!whole) {
+            int key, ch;
+            dslot(q, key, ch);
+            off = (uint32_t)min(key, room) * (uint32_t)rstride + (uint32_t)(ch * CH);
           }
+          char* dst = isv ? &Vs[buf][(j - KPS) * 1024] : &Ks[buf][j * 1024];
+          copy16_to_lds((isv ? vb : kb) + off, dst);
+        }
+      } else {
+        const int a0 = (it - n_pref) * KT;
+        const int first = s_anc_row[a0];
+#pragma unroll
+        for (int q = 0; q < NDW; ++q) {
+          const int j = wave + NWAVE * q;
+          if (j >= NDMA) break;
+          const bool isv = j >= KPS;
+          int key, ch;
+          dslot(q, key, ch);
+          const int rw = s_anc_row[a0 + key];
+          const int64_t off = (int64_t)(rw < 0 ? first : rw) * rstride + kvh * DH + ch * CH;
+          char* dst = isv ? &Vs[buf][(j - KPS) * 1024] : &Ks[buf][j * 1024];
+          copy16_to_lds((isv ? Vg : Kg) + off, dst);
         }
       }
+    }
+  };
 
-      // online softmax per column block; P^T packed for the next product.
-      // The running maximum m of a column moves only when one of its scores
-      // exceeds thr = m + 8 / (scale log2 e), i.e. when P would pass 2^8 (the
-      // final division by l removes m exactly).  Each lane tests its own
-      // scores; the column maximum and the rescale run only when some lane
-      // of the wave is over.
-      u32x4 bop[CBLK][NB];
+  // ---- per-half steps.  A half is 32 keys; this lane holds keys
+  // k0 + 16b + 4g + j (b = 2h, 2h+1; j < 4) of each of its columns.
+  typedef f32x4 HalfS[CBLK][2];
+  auto s_half = [&](const char* Kb, int h, HalfS& sacc) {  // S^T = K Q^T
 #pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) {
-        const f32x4* sc = sacc[cb];
-        const float lmax = max3(max3(sc[0][0], sc[0][1], sc[0][2]), max3(sc[0][3], sc[1][0], sc[1][1]),
-                                max3(sc[1][2], sc[1][3], -INFINITY));
-        if (__builtin_amdgcn_ballot_w64(lmax > thr[cb])) {
-          const float cmax = colgroup_max(lmax);
-          const bool grow = cmax > thr[cb];  // the same on the column's four lanes
-          // alpha is 1 on columns that keep m (m may still be -inf there)
-          const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[cb] - cmax) * sl2) : 1.0f;
-          lsum[cb] *= alpha;
+    for (int cb = 0; cb < CBLK; ++cb) sacc[cb][0] = sacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < NMB; ++i) acc[cb][i] *= alpha;
-          m_run[cb] = grow ? cmax : m_run[cb];
-          thr[cb] = m_run[cb] + thr_gap;
-          mb[cb] = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb] * sl2;
-        }
-        float pv[8];
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 2][i & 3], sl2, -mb[cb]));
-        if constexpr (BF) {
-          bop[cb][0] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                             pack_bf16x2(pv[6], pv[7])};
-        } else {
+      for (int t = 0; t < NST; ++t) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(Kb + (16 * (2 * h + bb) + r) * KPB + (4 * t + g) * 16);
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb)
-            bop[cb][bb] = u32x4{__float_as_uint(pv[4 * bb]), __float_as_uint(pv[4 * bb + 1]),
-                                __float_as_uint(pv[4 * bb + 2]), __float_as_uint(pv[4 * bb + 3])};
-        }
+        for (int cb = 0; cb < CBLK; ++cb) mma16(sacc[cb][bb], a, qreg[cb][t], S());
       }
-
-      // O^T += V^T P^T: each V^T operand read once, used for every column block
+  };
+  // Mask in place: chain keys are visible to the column whose query owns
+  // them (the owner list is padded with -1); a prefix key is visible while it
+  // is <= the column's limit; tiles every column of the wave sees in full are
+  // left unmasked.  Then the running maximum: m of a column moves only when
+  // one of its scores exceeds thr = m + 8 / (scale log2 e), i.e. when P would
+  // pass 2^8 (the final division by l removes m exactly).  Each lane tests
+  // its own scores; the column maximum runs only when some lane of the wave
+  // is over.  Returns whether any m moved; alpha then holds the factors
+  // (1 on columns that keep m) for O and l, applied by rescale().
+  float alpha[CBLK];
+  auto check_half = [&](int h, bool anc, bool full, int k0, HalfS& sacc) -> bool {
+    if (anc) {
+      int own[8];
 #pragma unroll
-      for (int mbk = 0; mbk < NMB; ++mbk) {
-        if constexpr (BF) {
-          // Lane 4c + m of a 16-lane group addresses dims 16 mbk + 4m .. +3 of
-          // key 32h + 16s + 4g + c; lane r then receives dim 16 mbk + r of the
-          // four keys c = 0..3 (slots 4s + c of the operand).
-          typedef __attribute__((address_space(3))) short4_t lds_s4;
-          const int kr = 32 * h + 4 * g + (r >> 2);
-          const char* vp = Vb + kr * VPB + (16 * mbk + 4 * (r & 3)) * 2;
-          const auto lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp));
-          const auto hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp + 16 * VPB));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
-          const u32x4 aop = {l2.x, l2.y, h2.x, h2.y};
+      for (int bb = 0; bb < 2; ++bb) {
+        const u32x4 o4 = *reinterpret_cast<const u32x4*>(&s_anc_own[k0 + 16 * (2 * h + bb) + 4 * g]);
 #pragma unroll
-          for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][0], S());
-        } else {
-#pragma unroll
-          for (int bb = 0; bb < 2; ++bb) {
-            const u32x4 aop =
-                *reinterpret_cast<const u32x4*>(Vb + (16 * mbk + r) * VPB + (16 * (2 * h + bb) + 4 * g) * 4);
-#pragma unroll
-            for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][bb], S());
-          }
-        }
+        for (int j = 0; j < 4; ++j) own[4 * bb + j] = (int)o4[j];
       }
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb)
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) mma16(lsum[cb], ones, bop[cb][bb], S());
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sacc[cb][bb][j] = (own[4 * bb + j] == cq[cb]) ? sacc[cb][bb][j] : -INFINITY;
+    } else if (!full) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) {
+        const int d = climit[cb] - k0 - 4 * g;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sacc[cb][bb][j] = (16 * (2 * h + bb) + j <= d) ? sacc[cb][bb][j] : -INFINITY;
+      }
     }
+    if constexpr (DBG) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) {
+        const int d = climit[cb] - k0 - 4 * g;
+        for (int i = 0; i < 8; ++i) {
+          const int bq = 2 * h + (i >> 2), j = i & 3;
+          const int kk = 16 * bq + 4 * g + j;
+          const bool vis = anc ? (s_anc_own[k0 + kk] == cq[cb]) : (16 * bq + j <= d);
+          if (vis) {
+            const int row = anc ? s_anc_row[k0 + kk] : seg_base + k0 + kk;
+            ++dcnt[cb];
+            dhsh[cb] += mix64((uint64_t)(uint32_t)row);
+          }
+        }
+      }
+    }
+    float lmax[CBLK];
+    bool over = false;
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) {
+      const f32x4* sc = sacc[cb];
+      lmax[cb] = max3(max3(sc[0][0], sc[0][1], sc[0][2]), max3(sc[0][3], sc[1][0], sc[1][1]),
+                      max3(sc[1][2], sc[1][3], -INFINITY));
+      over = over || lmax[cb] > thr[cb];
+    }
+    if (!__builtin_amdgcn_ballot_w64(over)) return false;
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) {
+      const float cmax = colgroup_max(lmax[cb]);
+      const bool grow = cmax > thr[cb];  // the same on the column's four lanes
+      alpha[cb] = grow ? __builtin_amdgcn_exp2f((m_run[cb] - cmax) * sl2) : 1.0f;
+      m_run[cb] = grow ? cmax : m_run[cb];
+      thr[cb] = m_run[cb] + thr_gap;
+      mb[cb] = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb] * sl2;
+    }
+    return true;
+  };
+  auto rescale = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) {
+      lsum[cb] *= alpha[cb];
+#pragma unroll
+      for (int i = 0; i < NMB; ++i) acc[cb][i] *= alpha[cb];
+    }
+  };
+  typedef u32x4 HalfP[CBLK][NB];
+  auto exp_half = [&](const HalfS& sacc, HalfP& bop) {  // P^T packed for the PV product
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[cb][i >> 2][i & 3], sl2, -mb[cb]));
+      if constexpr (BF) {
+        bop[cb][0] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                           pack_bf16x2(pv[6], pv[7])};
+      } else {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+          bop[cb][bb] = u32x4{__float_as_uint(pv[4 * bb]), __float_as_uint(pv[4 * bb + 1]),
+                              __float_as_uint(pv[4 * bb + 2]), __float_as_uint(pv[4 * bb + 3])};
+      }
+    }
+  };
+  // O^T += V^T P^T and l += 1^T P^T; each V^T operand read once, used for
+  // every column block
+  auto pv_half = [&](const char* Vb, int h, const HalfP& bop) {
+#pragma unroll
+    for (int mbk = 0; mbk < NMB; ++mbk) {
+      if constexpr (BF) {
+        // Lane 4c + m of a 16-lane group addresses dims 16 mbk + 4m .. +3 of
+        // key 32h + 16s + 4g + c; lane r then receives dim 16 mbk + r of the
+        // four keys c = 0..3 (slots 4s + c of the operand).
+        typedef __attribute__((address_space(3))) short4_t lds_s4;
+        const char* vp = Vb + (32 * h + 4 * g + (r >> 2)) * VPB + (16 * mbk + 4 * (r & 3)) * 2;
+        const auto lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp));
+        const auto hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp + 16 * VPB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
+        const u32x4 aop = {l2.x, l2.y, h2.x, h2.y};
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][0], S());
+      } else {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const u32x4 aop =
+              *reinterpret_cast<const u32x4*>(Vb + (16 * mbk + r) * VPB + (16 * (2 * h + bb) + 4 * g) * 4);
+#pragma unroll
+          for (int cb = 0; cb < CBLK; ++cb) mma16(acc[cb][mbk], aop, bop[cb][bb], S());
+        }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) mma16(lsum[cb], ones, bop[cb][bb], S());
+  };
+
+  // an empty use that makes P^T of a half complete at this point
+  auto pin = [&](const HalfP& bop) {
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) asm volatile("" : : "v"(bop[cb][bb]));
+  };
+
+  // ---- tile loop.  The next tile's global loads are issued after the
+  // barrier and written to the other LDS buffer after this tile's work (every
+  // wave has passed the barrier that follows its last read of that buffer).
+  // The last iteration reloads its own tile into the unused buffer, which
+  // keeps the loop free of branches around the staging.  Within a tile the
+  // steps are ordered so that the exponentials of one half run beside the
+  // matrix products of the other:
+  //   S0 | check0 (+rescale) | S1 + exp0 | check1 | PV0 + exp1 | (rescale) | PV1
+  const int n_iter = have_rows ? n_tiles : 0;
+  if (n_iter > 0) {
+    if constexpr (BF) {
+      dma_tile(0, 0);
+    } else {
+      load_tile(0);
+      store_tile(0);
+    }
+  }
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    if constexpr (BF) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of tile it
+    __syncthreads();
+    if constexpr (BF) {
+      if (it + 1 < n_iter) dma_tile(it + 1, buf ^ 1);  // into the buffer of tile it - 1, read by now
+    } else {
+      load_tile(min(it + 1, n_iter - 1));
+    }
+
+    const bool anc = it >= n_pref;
+    const int k0 = anc ? (it - n_pref) * KT : kbeg + it * KT;
+    const bool skip = anc ? (k0 + KT <= wa0 || k0 >= wa1) : (k0 > wmax);
+    if (!skip) {
+      const bool full = !DBG && !anc && (k0 + KT - 1 <= wmin);
+      const char* Kb = Ks[buf];
+      const char* Vb = Vs[buf];
+      HalfS s0, s1;
+      HalfP p0, p1;
+      s_half(Kb, 0, s0);
+      if (check_half(0, anc, full, k0, s0)) rescale();
+      s_half(Kb, 1, s1);
+      exp_half(s0, p0);
+      pin(p0);  // keeps exp0 beside S1 (the compiler would sink it to PV0)
+      const bool moved1 = check_half(1, anc, full, k0, s1);
+      pv_half(Vb, 0, p0);
+      exp_half(s1, p1);
+      pin(p1);  // keeps exp1 beside PV0
+      if (moved1) rescale();
+      pv_half(Vb, 1, p1);
+    }
+    if constexpr (!BF) store_tile(buf ^ 1);
   }
 
   // ---- epilogue.  l of column r is row 0 of lsum (lane g = 0, element 0;
