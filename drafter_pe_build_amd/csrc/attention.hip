@@ -26,9 +26,9 @@
 //     online softmax in fp32 (exp2 with the log2(e)-folded scale); each lane's
 //     column is fixed, so the rescale of the running output is per lane, and
 //     the running maximum moves only when it grows by more than 2^8;
-//   * O^T += V^T P^T on the matrix cores (P rounded to the operand type); the
-//     row sums l come from the same products, through a V^T block whose first
-//     row is all ones, so l sums exactly the rounded P that weights V.
+//   * O^T += V^T P^T on the matrix cores (P rounded to the operand type);
+//     each lane keeps the fp32 sum of its own P, reduced over the column's
+//     lanes at the end.
 // A wave skips the multiplications of tiles none of its columns can see.
 // Chain rows are gathered into extra tiles whose mask is "owner == column's
 // query"; a row shared by several chains appears once per owner.  Splits
@@ -237,8 +237,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
 
   // m_run: running maximum (raw score units); thr = m_run + thr_gap; mb =
   // m_run * scale * log2 e (0 while no score has been seen, m_run = -inf)
-  float m_run[CBLK], thr[CBLK], mb[CBLK];
-  f32x4 acc[CBLK][NMB], lsum[CBLK];
+  // l_run: this lane's share of the row sum (its keys); the column's l is
+  // the sum over the column's four lanes
+  float m_run[CBLK], thr[CBLK], mb[CBLK], l_run[CBLK];
+  f32x4 acc[CBLK][NMB];
   int64_t dcnt[CBLK];
   uint64_t dhsh[CBLK];
 #pragma unroll
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
     m_run[cb] = -INFINITY;
     thr[cb] = -INFINITY;
     mb[cb] = 0.f;
-    lsum[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run[cb] = 0.f;
     dcnt[cb] = 0;
     dhsh[cb] = 0;
 #pragma unroll
@@ -254,9 +256,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   }
   const float sl2 = p.scale_log2;
   const float thr_gap = 8.0f / sl2;
-  // A operand whose row 0 is all ones: its product with P^T is the column sum
-  const uint32_t one = BF ? 0x3F803F80u : 0x3F800000u;
-  const u32x4 ones = (r == 0) ? u32x4{one, one, one, one} : u32x4{0u, 0u, 0u, 0u};
 
   // ---- tile staging.  Thread chunk i covers key (tid + 256 i) / DC, 16-byte
   // chunk (tid + 256 i) % DC of both K and V.  Keys a tile does not hold for
@@ -478,18 +477,21 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   auto rescale = [&]() {
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) {
-      lsum[cb] *= alpha[cb];
+      l_run[cb] *= alpha[cb];
 #pragma unroll
       for (int i = 0; i < NMB; ++i) acc[cb][i] *= alpha[cb];
     }
   };
   typedef u32x4 HalfP[CBLK][NB];
-  auto exp_half = [&](const HalfS& sacc, HalfP& bop) {  // P^T packed for the PV product
+  // P^T packed for the PV product, and this lane's sum of the half's P (added
+  // to l together with the products, after any rescale that precedes them)
+  auto exp_half = [&](const HalfS& sacc, HalfP& bop, float (&lp)[CBLK]) {
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) {
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[cb][i >> 2][i & 3], sl2, -mb[cb]));
+      lp[cb] = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
       if constexpr (BF) {
         bop[cb][0] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                            pack_bf16x2(pv[6], pv[7])};
@@ -501,9 +503,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
       }
     }
   };
-  // O^T += V^T P^T and l += 1^T P^T; each V^T operand read once, used for
+  // O^T += V^T P^T and l += sum P; each V^T operand read once, used for
   // every column block
-  auto pv_half = [&](const char* Vb, int h, const HalfP& bop) {
+  auto pv_half = [&](const char* Vb, int h, const HalfP& bop, const float (&lp)[CBLK]) {
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) l_run[cb] += lp[cb];
 #pragma unroll
     for (int mbk = 0; mbk < NMB; ++mbk) {
       if constexpr (BF) {
@@ -528,10 +532,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
         }
       }
     }
-#pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb)
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) mma16(lsum[cb], ones, bop[cb][bb], S());
   };
 
   // an empty use that makes P^T of a half complete at this point
@@ -578,26 +578,26 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
       const char* Vb = Vs[buf];
       HalfS s0, s1;
       HalfP p0, p1;
+      float l0[CBLK], l1[CBLK];
       s_half(Kb, 0, s0);
       if (check_half(0, anc, full, k0, s0)) rescale();
       s_half(Kb, 1, s1);
-      exp_half(s0, p0);
+      exp_half(s0, p0, l0);
       pin(p0);  // keeps exp0 beside S1 (the compiler would sink it to PV0)
       const bool moved1 = check_half(1, anc, full, k0, s1);
-      pv_half(Vb, 0, p0);
-      exp_half(s1, p1);
+      pv_half(Vb, 0, p0, l0);
+      exp_half(s1, p1, l1);
       pin(p1);  // keeps exp1 beside PV0
       if (moved1) rescale();
-      pv_half(Vb, 1, p1);
+      pv_half(Vb, 1, p1, l1);
     }
     if constexpr (!BF) store_tile(buf ^ 1);
   }
 
-  // ---- epilogue.  l of column r is row 0 of lsum (lane g = 0, element 0;
-  // the other lanes of the column hold 0 there).
+  // ---- epilogue
 #pragma unroll
   for (int cb = 0; cb < CBLK; ++cb) {
-    const float l_run = colgroup_sum(lsum[cb][0]);
+    const float l_col = colgroup_sum(l_run[cb]);
     if constexpr (DBG) {
       for (int o = 16; o < 64; o <<= 1) {
         dcnt[cb] += __shfl_xor(dcnt[cb], o, 64);
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
     const int qo = qbase + cq[cb];
     const int h = hh[cb];
     if (p.n_splits == 1) {
-      const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+      const float inv = l_col > 0.f ? 1.0f / l_col : 0.f;
       S* o = reinterpret_cast<S*>(p.out) + ((int64_t)qo * Hq + h) * DH;
 #pragma unroll
       for (int mbk = 0; mbk < NMB; ++mbk) {
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
         }
       }
       if (p.lse && g == 0)
-        p.lse[(int64_t)qo * Hq + h] = l_run > 0.f ? m_run[cb] * p.scale + logf(l_run) : -INFINITY;
+        p.lse[(int64_t)qo * Hq + h] = l_col > 0.f ? m_run[cb] * p.scale + logf(l_col) : -INFINITY;
     } else {
       const int64_t qh = ((int64_t)sp * p.num_q + qo) * Hq + h;
 #pragma unroll
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
         *reinterpret_cast<f32x4*>(p.part_o + qh * DH + 16 * mbk + 4 * g) = acc[cb][mbk];
       if (g == 0) {
         p.part_ml[qh * 2 + 0] = m_run[cb];
-        p.part_ml[qh * 2 + 1] = l_run;
+        p.part_ml[qh * 2 + 1] = l_col;
       }
     }
     if constexpr (DBG) {
