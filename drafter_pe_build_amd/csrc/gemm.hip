@@ -96,6 +96,23 @@ __device__ __forceinline__ void epi_store(const Epi& e, int m, int n, float y, f
 }
 
 // ---------------------------------------------------------------------------
+// Activation rows staged in LDS by the LM-head kernel (row pitch xp bytes,
+// a zero chunk at xs + M*xp for the padding rows of the 16-row operand).
+// Ends with a workgroup barrier.
+template <typename S>
+__device__ void stage_rows(const GemmParams& p, char* xs, int xp) {
+  constexpr int CH = Storage<S>::CH;
+  const int cpr = p.K * (int)sizeof(S) / 16;  // 16-byte chunks per row
+  const S* X = reinterpret_cast<const S*>(p.X);
+  for (int c = threadIdx.x; c < p.M * cpr; c += blockDim.x) {
+    const int row = c / cpr, col = c % cpr;
+    *reinterpret_cast<u32x4*>(xs + row * xp + col * 16) = ld16(X + (int64_t)row * p.ldx + col * CH);
+  }
+  if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(xs + p.M * xp) = zero4();
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // Weight-streaming contraction for M <= 16.  Workgroup fb of KS waves owns the
 // 16-row weight block fb; wave ks takes the ks-th share of the K steps.  Each
 // wave issues U one-kilobyte weight loads (and the matching activation loads)
@@ -164,15 +181,22 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmParams p) {
 }
 
 // LM head for M <= 16: grid-stride over groups of NFB weight blocks; KS waves
-// per block split K and sum through LDS in ks order.  Each lane of the
-// block's first wave keeps the best (logit, lowest index) of its activation
-// row; the workgroup's best per row goes to partial slot [blockIdx][row],
-// reduced by argmax_reduce_kernel.
-template <typename S, int NFB, int KS, int U>
+// per block split K and sum through LDS in ks order.  With XL the M
+// activation rows are staged once per workgroup in LDS by stage_rows (row
+// pitch K + 16 bytes, so the 16 lanes of one k-chunk hit distinct banks);
+// without it (rows too wide for LDS) they are read from global memory,
+// padding rows from the zeroed buffer p.xzero.  Each wave streams its
+// weight steps in double-buffered batches of U: batch j+1 is in flight while
+// batch j is multiplied.  Each lane of the block's
+// first wave keeps the best (logit, lowest index) of its activation row; the
+// workgroup's best per row goes to partial slot [blockIdx][row], reduced by
+// argmax_reduce_kernel.
+template <typename S, int NFB, int KS, int U, bool XL>
 __global__ __launch_bounds__(64 * NFB * KS) void lm_argmax_stream_kernel(GemmParams p) {
   constexpr int CH = Storage<S>::CH;
   constexpr int STEP = 4 * CH;
   constexpr int NW = NFB * KS;
+  extern __shared__ __attribute__((aligned(16))) char xs[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int fbl = wave / KS, ks = wave % KS;
@@ -183,28 +207,47 @@ __global__ __launch_bounds__(64 * NFB * KS) void lm_argmax_stream_kernel(GemmPar
   const int nfb = (N + 15) >> 4;
   const int ntiles = (nfb + NFB - 1) / NFB;
   const bool xr = r < M;
-  const S* xrow = (xr ? reinterpret_cast<const S*>(p.X) + (int64_t)r * p.ldx : reinterpret_cast<const S*>(p.xzero)) + g * CH;
+  const char* xrow;
+  int xstep;  // bytes per step (0: padding rows stay on a zero chunk)
+  if constexpr (XL) {
+    const int xp = K * (int)sizeof(S) + 16;  // LDS row pitch, bytes
+    stage_rows<S>(p, xs, xp);
+    xrow = xr ? xs + r * xp + g * 16 : xs + M * xp;
+    xstep = xr ? STEP * (int)sizeof(S) : 0;
+  } else {
+    xrow = xr ? reinterpret_cast<const char*>(reinterpret_cast<const S*>(p.X) + (int64_t)r * p.ldx + g * CH)
+              : reinterpret_cast<const char*>(p.xzero) + g * 16;
+    xstep = STEP * (int)sizeof(S);  // p.xzero holds >= K zeroed elements
+  }
   const char* W = reinterpret_cast<const char*>(p.W) + lane * 16;
   __shared__ f32x4 red[KS > 1 ? NFB * (KS - 1) * 64 : 1];
   float best = -INFINITY;
   int bidx = 0x7fffffff;
+  const int nb = (s1 - s0 + U - 1) / U;  // batches per wave
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int fb = tile * NFB + fbl;
     const bool active = fb < nfb;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (active) {
       const char* wb = W + (int64_t)fb * nsteps * 1024;
-      for (int s = s0; s < s1; s += U) {
-        u32x4 wv[U], xv[U];
+      u32x4 wv[2][U];
+      auto wload = [&](int j, int slot) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) wv[slot][u] = ld16(wb + (int64_t)min(s0 + j * U + u, s1 - 1) * 1024);
+      };
+      auto batch = [&](int j, int slot) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int su = min(s + u, s1 - 1);
-          wv[u] = ld16(wb + (int64_t)su * 1024);
-          xv[u] = ld16(xrow + su * STEP);
+          const int su = s0 + j * U + u;
+          if (su < s1) mma16(acc, wv[slot][u], ld16(xrow + (int64_t)su * xstep), S());
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (s + u < s1) mma16(acc, wv[u], xv[u], S());
+      };
+      wload(0, 0);
+      for (int j = 0; j < nb; j += 2) {
+        if (j + 1 < nb) wload(j + 1, 1);
+        batch(j, 0);
+        if (j + 2 < nb) wload(j + 2, 0);
+        if (j + 1 < nb) batch(j + 1, 1);
       }
     }
     if constexpr (KS > 1) {
@@ -447,9 +490,15 @@ static constexpr int kStreamU = 8;     // 1 KB steps in flight per wave
 #define PE_LM_KS 2
 #endif
 #ifndef PE_LM_GRID
-#define PE_LM_GRID 4096
+#define PE_LM_GRID 1024
 #endif
-static constexpr int kLmNFB = PE_LM_NFB, kLmKS = PE_LM_KS, kLmGrid = PE_LM_GRID;
+#ifndef PE_LM_U
+#define PE_LM_U 8
+#endif
+static constexpr int kLmNFB = PE_LM_NFB, kLmKS = PE_LM_KS, kLmGrid = PE_LM_GRID, kLmU = PE_LM_U;
+// Largest activation block the LM-head kernel stages in LDS (its own arrays
+// take a few KB of the 160 KB); wider rows are read from global memory.
+static constexpr int kLmXLds = 144 * 1024;
 
 // Waves per 16-row block: the most (up to 16) that still leave every wave at
 // least one full batch of kStreamU steps.
@@ -475,6 +524,17 @@ static int launch_tiled(const GemmParams& p, hipStream_t s) {
   return n_ft;
 }
 
+// Raises kernel K's dynamic LDS limit once (the default may be below what
+// the activation block needs); one flag per kernel.
+template <auto K>
+static void allow_lds(int bytes) {
+  static bool done = false;
+  if (!done) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(K), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    done = true;
+  }
+}
+
 template <typename S, bool DUAL>
 static void launch_stream(const GemmParams& p, hipStream_t s) {
   const dim3 grid((p.N + 15) / 16);
@@ -494,8 +554,15 @@ static int launch_gemm_t(const GemmParams& p, hipStream_t s) {
   if (p.M <= 16) {
     if (am) {
       const int grid = gemm_argmax_partials(p.M, p.N);
-      hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kStreamU>), dim3(grid), dim3(64 * kLmNFB * kLmKS),
-                         0, s, p);
+      const size_t lds = (size_t)p.M * (p.K * sizeof(S) + 16) + 16;  // activation rows + zero chunk
+      if (lds <= (size_t)kLmXLds) {
+        allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true>>(kLmXLds);
+        hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true>), dim3(grid),
+                           dim3(64 * kLmNFB * kLmKS), lds, s, p);
+      } else {
+        hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, false>), dim3(grid),
+                           dim3(64 * kLmNFB * kLmKS), 0, s, p);
+      }
       return grid;
     }
     if (dual) launch_stream<S, true>(p, s); else launch_stream<S, false>(p, s);
