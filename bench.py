@@ -26,7 +26,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch of the LM-head stage measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE, scaled by a 1 GiB copy (profiles/decode_c1_lm_head_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
-LM_STAGE_TRAFFIC = {"fingerprint": "f78c04647b80198c", "bytes": 1160725000}
+LM_STAGE_TRAFFIC = {"fingerprint": "5d5c6e7df0c3e094", "bytes": 1160502358}
 LM_SOURCES = ("gemm.hip", "norm.hip", "common.h", "kernels.h")
 
 
@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the c=64 decode and attention measurements")
+    ap.add_argument("--attention-only", type=int, choices=(3, 4), default=0,
+                    help="time only the COD (3) or parallel-group (4) attention workload and print its line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also copy 1 GiB device-to-device 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -91,6 +93,52 @@ def decode_bytes(dims, case, T, RK):
     return weights + kv + hidden + emb + act, weights
 
 
+ATTN_NAMES = {3: "cod_attention_n4096", 4: "group_attention_n8192_chunked"}
+
+
+def measure_attention(cfg, steps, stream):
+    """COD attention N=4096 (one launch) or parallel-group attention N=8192
+    (8 query chunks of 8192): time per pass over all queries and rate."""
+    import numpy as np
+    import torch
+    from drafter_pe_build_amd import _lib as L
+    from drafter_pe_build_amd.step import to_device
+    from synth import inputs as si
+    log("attention config %d" % cfg)
+    Lay = si.cod_config(cfg)
+    T = Lay["T"]
+    Hq, Hkv, Dh = Lay["heads"]
+    q, k, v = (to_device(Lay[n], "cuda") for n in ("q", "k", "v"))
+    start = to_device(Lay["start"].astype(np.int32), "cuda")
+    depth = to_device(Lay["depth"].astype(np.int32), "cuda")
+    parent = to_device(Lay["parent"].astype(np.int32), "cuda")
+    selfr = to_device(np.arange(T, dtype=np.int32), "cuda")
+    base = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, Hq, Dh), dtype=torch.bfloat16, device="cuda")
+    chunks = [(0, T)] if cfg == 3 else [(8192 * c, 8192 * (c + 1)) for c in range(8)]
+    arglist = [L.attn_args(num_q=c1 - c0, num_seg=1, q_per_seg=c1 - c0, num_kv_rows=T, n_q_heads=Hq,
+                           n_kv_heads=Hkv, head_dim=Dh, scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16,
+                           q=q[c0:c1], q_row_stride=Hq * Dh, k=k, v=v, seg_kv_base=base,
+                           q_start=start[c0:c1], q_depth=depth[c0:c1], q_self_row=selfr[c0:c1],
+                           kv_parent=parent, max_prefix=Lay["N"], out=out[c0:c1]) for c0, c1 in chunks]
+    wsb = max(L.pe_draft_attention_workspace(a) for a in arglist)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+
+    def run_attn():
+        for a in arglist:
+            L.pe_draft_attention(a, "cuda", workspace=ws)
+
+    msa = time_loop(run_attn, steps, 2, stream)
+    pairs = int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
+    fl = pairs * Hq * 4 * Dh
+    log("  %.1f us, %.0f TFLOP/s" % (msa * 1e3, fl / (msa * 1e-3) / 1e12))
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return {"T": T, "ms": msa, "positions_per_s": T / (msa * 1e-3), "visible_pairs": pairs,
+            "tflops": fl / (msa * 1e-3) / 1e12, "mfma_frac": fl / (msa * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "launches": len(chunks)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -107,6 +155,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.attention_only:
+        r = measure_attention(args.attention_only, args.steps, stream)
+        print(json.dumps({"metric": ATTN_NAMES[args.attention_only], "value": r["tflops"], "unit": "TFLOP/s",
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
+        return
     dims = si.GPTOSS_DIMS
     log("generating the c=1 decode inputs and the drafter weights")
     t0 = time.time()
@@ -198,39 +251,7 @@ def main():
         del gs2, st2
         torch.cuda.empty_cache()
         for cfg, name in ((3, "cod_attention_n4096"), (4, "group_attention_n8192_chunked")):
-            log("attention config %d" % cfg)
-            Lay = si.cod_config(cfg)
-            T = Lay["T"]
-            Hq, Hkv, Dh = Lay["heads"]
-            q, k, v = (to_device(Lay[n], "cuda") for n in ("q", "k", "v"))
-            start = to_device(Lay["start"].astype(np.int32), "cuda")
-            depth = to_device(Lay["depth"].astype(np.int32), "cuda")
-            parent = to_device(Lay["parent"].astype(np.int32), "cuda")
-            selfr = to_device(np.arange(T, dtype=np.int32), "cuda")
-            base = torch.zeros(1, dtype=torch.int32, device="cuda")
-            out = torch.empty((T, Hq, Dh), dtype=torch.bfloat16, device="cuda")
-            chunks = [(0, T)] if cfg == 3 else [(8192 * c, 8192 * (c + 1)) for c in range(8)]
-            arglist = [L.attn_args(num_q=c1 - c0, num_seg=1, q_per_seg=c1 - c0, num_kv_rows=T, n_q_heads=Hq,
-                                   n_kv_heads=Hkv, head_dim=Dh, scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16,
-                                   q=q[c0:c1], q_row_stride=Hq * Dh, k=k, v=v, seg_kv_base=base,
-                                   q_start=start[c0:c1], q_depth=depth[c0:c1], q_self_row=selfr[c0:c1],
-                                   kv_parent=parent, max_prefix=Lay["N"], out=out[c0:c1]) for c0, c1 in chunks]
-            wsb = max(L.pe_draft_attention_workspace(a) for a in arglist)
-            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
-
-            def run_attn():
-                for a in arglist:
-                    L.pe_draft_attention(a, "cuda", workspace=ws)
-
-            msa = time_loop(run_attn, max(5, args.steps // 5), 2, stream)
-            pairs = int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
-            fl = pairs * Hq * 4 * Dh
-            extra[name] = {"T": T, "ms": msa, "positions_per_s": T / (msa * 1e-3), "visible_pairs": pairs,
-                           "tflops": fl / (msa * 1e-3) / 1e12,
-                           "mfma_frac": fl / (msa * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "launches": len(chunks)}
-            log("  %.1f us, %.0f TFLOP/s" % (msa * 1e3, fl / (msa * 1e-3) / 1e12))
-            del q, k, v, out
-            torch.cuda.empty_cache()
+            extra[name] = measure_attention(cfg, max(5, args.steps // 5), stream)
         result["secondary"] = extra
 
     if not args.no_cpu:
