@@ -345,28 +345,23 @@ pe_status pe_fuse_hidden(const pe_drafter_dims* dims, const pe_drafter_weights* 
   const FuseWs fw = fuse_ws(dims, T, workspace);
   const int d = dims->hidden;
   const int bf = dims->dtype == PE_BF16;
-  NormParams np{};
-  np.in = draft_hidden;
-  np.ld_in = 3 * (int64_t)d;
-  np.skip = rejected;
-  np.n = T;
-  np.segs = 3;
-  np.d = d;
-  np.gain = w->stream_gain;
-  np.eps = dims->eps;
-  np.out = fw.u;
-  np.ld_out = 3 * (int64_t)d;
-  np.zero = fw.zero;
-  np.nzero = fw.nzero;
-  launch_rmsnorm_rows(np, bf, bf, stream);
+  // u_s = RMSNorm(stream s) feeds w_fc (fused into the contraction's staging when it fits)
   GemmParams gp{};
-  gp.X = fw.u;
+  gp.X = draft_hidden;
   gp.ldx = 3 * (int64_t)d;
   gp.W = w->w_fc;
   gp.M = T;
   gp.N = d;
   gp.K = 3 * d;
   gp.xzero = fw.zero;
+  gp.nrm.gain = w->stream_gain;
+  gp.nrm.segs = 3;
+  gp.nrm.seg_len = d;
+  gp.nrm.eps = dims->eps;
+  gp.nrm.skip = rejected;
+  gp.nrm.tmp = fw.u;
+  gp.clear = fw.zero;
+  gp.nclear = fw.nzero;
   gp.epi.kind = EPI_FC;
   gp.epi.out_f32 = x0;
   gp.epi.ld_out = d;
@@ -428,31 +423,25 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   const int RK = R * K;
   const int qcols = Hq * Dh, kvcols = Hkv * Dh;
 
-  // a = RMSNorm(x0) for every row (rejected rows give zeros; their K/V are not written)
-  NormParams np{};
-  np.in = x0;
-  np.ld_in = d;
-  np.skip = batch->rejected;
-  np.n = T;
-  np.segs = 1;
-  np.d = d;
-  np.gain = w->attn_gain;
-  np.eps = dims->eps;
-  np.out = lw.a;
-  np.ld_out = d;
-  np.zero = lw.zero;
-  np.nzero = lw.nzero;
-  launch_rmsnorm_rows(np, 0, bf, stream);
-
-  // [q|k|v] = W_qkv a; k, v scattered to the cache by slot
+  // [q|k|v] = W_qkv RMSNorm(x0) for every row (rejected rows normalise to zeros;
+  // their K/V are not written); k, v scattered to the cache by slot
   GemmParams gp{};
-  gp.X = lw.a;
+  gp.X = x0;
   gp.ldx = d;
   gp.W = w->w_qkv;
   gp.M = T;
   gp.N = qcols + 2 * kvcols;
   gp.K = d;
   gp.xzero = lw.zero;
+  gp.nrm.gain = w->attn_gain;
+  gp.nrm.segs = 1;
+  gp.nrm.seg_len = d;
+  gp.nrm.eps = dims->eps;
+  gp.nrm.skip = batch->rejected;
+  gp.nrm.x_f32 = 1;
+  gp.nrm.tmp = lw.a;
+  gp.clear = lw.zero;
+  gp.nclear = lw.nzero;
   gp.epi.kind = EPI_QKV;
   gp.epi.out_s = lw.q;
   gp.epi.q_cols = qcols;
@@ -486,7 +475,7 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   st = run_attention(&aa, lw.attn, lw.attn_bytes, 1, stream);
   if (st != PE_OK) return st;
 
-  // x1 = x0[query rows] + W_o o;  b = RMSNorm(x1)
+  // x1 = x0[query rows] + W_o o
   gp = GemmParams{};
   gp.X = lw.o;
   gp.ldx = qcols;
@@ -502,21 +491,10 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.epi.res_rows = batch->query_rows;
   gp.epi.ld_res = d;
   launch_gemm(gp, bf, stream);
-  np = NormParams{};
-  np.in = lw.x1;
-  np.ld_in = d;
-  np.n = RK;
-  np.segs = 1;
-  np.d = d;
-  np.gain = w->mlp_gain;
-  np.eps = dims->eps;
-  np.out = lw.b;
-  np.ld_out = d;
-  launch_rmsnorm_rows(np, 0, bf, stream);
 
-  // h = silu(W_gate b) * (W_up b)
+  // h = silu(W_gate b) * (W_up b),  b = RMSNorm(x1)
   gp = GemmParams{};
-  gp.X = lw.b;
+  gp.X = lw.x1;
   gp.ldx = d;
   gp.W = w->w_gate;
   gp.W2 = w->w_up;
@@ -524,6 +502,12 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.N = F;
   gp.K = d;
   gp.xzero = lw.zero;
+  gp.nrm.gain = w->mlp_gain;
+  gp.nrm.segs = 1;
+  gp.nrm.seg_len = d;
+  gp.nrm.eps = dims->eps;
+  gp.nrm.x_f32 = 1;
+  gp.nrm.tmp = lw.b;
   gp.epi.kind = EPI_SWIGLU;
   gp.epi.out_s = lw.h;
   gp.epi.ld_out = F;
@@ -567,27 +551,23 @@ pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weight
   const LmWs lw = lm_ws(dims, n, workspace);
   const int d = dims->hidden;
   const int bf = dims->dtype == PE_BF16;
-  NormParams np{};
-  np.in = x;
-  np.ld_in = d;
-  np.n = n;
-  np.segs = 1;
-  np.d = d;
-  np.gain = w->final_gain;
-  np.eps = dims->eps;
-  np.out = lw.f;
-  np.ld_out = d;
-  np.zero = lw.zero;
-  np.nzero = lw.nzero;
-  launch_rmsnorm_rows(np, 0, bf, stream);
+  // z = w_lm RMSNorm(x): the norm is fused into the LM kernel's staging when it fits
   GemmParams gp{};
-  gp.X = lw.f;
+  gp.X = x;
   gp.ldx = d;
   gp.W = w->w_lm;
   gp.M = n;
   gp.N = dims->vocab;
   gp.K = d;
   gp.xzero = lw.zero;
+  gp.nrm.gain = w->final_gain;
+  gp.nrm.segs = 1;
+  gp.nrm.seg_len = d;
+  gp.nrm.eps = dims->eps;
+  gp.nrm.x_f32 = 1;
+  gp.nrm.tmp = lw.f;
+  gp.clear = lw.zero;
+  gp.nclear = lw.nzero;
   gp.epi.kind = EPI_ARGMAX;
   gp.epi.logits = logits;
   gp.epi.part_val = lw.pv;

@@ -26,6 +26,7 @@
 //    tiles of one N tile back to back onto one XCD (workgroup i runs on XCD
 //    i % 8) so the weight chunks are fetched from HBM once.
 #include <math.h>
+#include <type_traits>
 #include "kernels.h"
 
 namespace pe {
@@ -96,20 +97,177 @@ __device__ __forceinline__ void epi_store(const Epi& e, int m, int n, float y, f
 }
 
 // ---------------------------------------------------------------------------
-// Activation rows staged in LDS by the LM-head kernel (row pitch xp bytes,
-// a zero chunk at xs + M*xp for the padding rows of the 16-row operand).
-// Ends with a workgroup barrier.
-template <typename S>
-__device__ void stage_rows(const GemmParams& p, char* xs, int xp) {
-  constexpr int CH = Storage<S>::CH;
-  const int cpr = p.K * (int)sizeof(S) / 16;  // 16-byte chunks per row
-  const S* X = reinterpret_cast<const S*>(p.X);
-  for (int c = threadIdx.x; c < p.M * cpr; c += blockDim.x) {
-    const int row = c / cpr, col = c % cpr;
-    *reinterpret_cast<u32x4*>(xs + row * xp + col * 16) = ld16(X + (int64_t)row * p.ldx + col * CH);
+// Activation staging of the weight-streaming kernels: the M rows of X are
+// written to LDS in the operand type S, row pitch xp bytes.  Neither function
+// ends with a barrier.
+
+// Element e of a 16-byte chunk of XT values, as float.
+template <typename XT>
+__device__ __forceinline__ float chunk_elem(const u32x4& v, int e) {
+  if constexpr (sizeof(XT) == 2) return bf2f((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+  else return __uint_as_float(v[e]);
+}
+
+// Staging runs in two phases so that a kernel can request its first weight
+// batches in between: load() issues the global reads of the first round into
+// registers, finish() writes them to LDS and runs any further rounds.  The
+// memory counter retires loads in issue order, so activation reads issued
+// after a weight batch would wait for that batch.
+
+// Plain copy (X already holds S): NCP sixteen-byte chunks per thread per round.
+template <typename S, int NCP>
+struct CopyStage {
+  u32x4 v[NCP];
+  __device__ void load_round(const GemmParams& p, int base) {
+    const int cpr = p.K * (int)sizeof(S) / 16;
+    const int total = p.M * cpr;
+    const char* X = reinterpret_cast<const char*>(p.X);
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int c = min(base + (int)threadIdx.x + i * (int)blockDim.x, total - 1);
+      const int row = c / cpr, col = c - row * cpr;
+      v[i] = ld16(X + (int64_t)row * p.ldx * (int64_t)sizeof(S) + (int64_t)col * 16);
+    }
   }
-  if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(xs + p.M * xp) = zero4();
-  __syncthreads();
+  __device__ void store_round(const GemmParams& p, char* xs, int xp, int base) {
+    const int cpr = p.K * (int)sizeof(S) / 16;
+    const int total = p.M * cpr;
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int c = base + (int)threadIdx.x + i * (int)blockDim.x;
+      if (c < total) {
+        const int row = c / cpr, col = c - row * cpr;
+        *reinterpret_cast<u32x4*>(xs + row * xp + col * 16) = v[i];
+      }
+    }
+  }
+  __device__ void load(const GemmParams& p) { load_round(p, 0); }
+  __device__ void finish(const GemmParams& p, char* xs, int xp) {
+    const int total = p.M * (p.K * (int)sizeof(S) / 16);
+    const int round = NCP * (int)blockDim.x;
+    store_round(p, xs, xp, 0);
+    for (int base = round; base < total; base += round) {
+      load_round(p, base);
+      store_round(p, xs, xp, base);
+    }
+  }
+};
+
+// RMSNorm on the way in ("Attention Drift", section 4.1: RMS = ||x||_2 /
+// sqrt(d), each segment on its own): y = (x * inv) * g, the expression
+// rmsnorm_rows_kernel evaluates; skipped rows become zeros.  One wave per
+// (row, segment) pair, pairs wave, wave + nw, ...; a segment's NC chunks per
+// lane stay in registers between the sum of squares and the scaled store.
+// The gains (segs * seg_len floats) are copied to LDS at xg by all threads
+// in the same first round.  All global reads are unconditional 16-byte loads
+// (indices clamped), so none of them waits behind a branch.  finish() has a
+// barrier between the gain copy and its use.
+template <typename S, typename XT, int NC>
+struct NormStage {
+  static constexpr int CI = 16 / sizeof(XT);  // elements per chunk
+  static constexpr int GN = 3;                // gain chunks per thread per round
+  static_assert(sizeof(S) <= sizeof(XT), "the operand type is never wider than the input");
+  u32x4 raw[NC];
+  f32x4 gt[GN];
+  __device__ void load_pair(const GemmParams& p, int pr) {
+    const int lane = threadIdx.x & 63;
+    const int segs = p.nrm.segs, sl = p.nrm.seg_len, cps = sl / CI;
+    const int row = pr / segs, seg = pr - row * segs;
+    const char* x = reinterpret_cast<const char*>(p.X) + ((int64_t)row * p.ldx + (int64_t)seg * sl) * (int64_t)sizeof(XT);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) raw[c] = ld16(x + (int64_t)min(lane + 64 * c, cps - 1) * 16);
+  }
+  __device__ void load_gains(const GemmParams& p, int base) {
+    const int gch = p.nrm.segs * p.nrm.seg_len / 4;
+#pragma unroll
+    for (int i = 0; i < GN; ++i)
+      gt[i] = *reinterpret_cast<const f32x4*>(p.nrm.gain + 4 * min(base + (int)threadIdx.x + i * (int)blockDim.x, gch - 1));
+  }
+  __device__ void store_gains(const GemmParams& p, char* xg, int base) {
+    const int gch = p.nrm.segs * p.nrm.seg_len / 4;
+#pragma unroll
+    for (int i = 0; i < GN; ++i) {
+      const int c = base + (int)threadIdx.x + i * (int)blockDim.x;
+      if (c < gch) *reinterpret_cast<f32x4*>(xg + 16 * c) = gt[i];
+    }
+  }
+  __device__ void store_pair(const GemmParams& p, char* xs, int xp, const char* xg, int pr) {
+    const int lane = threadIdx.x & 63;
+    const int segs = p.nrm.segs, sl = p.nrm.seg_len, cps = sl / CI;
+    const int row = pr / segs, seg = pr - row * segs;
+    const bool skip = p.nrm.skip && p.nrm.skip[row];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bool ok = lane + 64 * c < cps && !skip;
+#pragma unroll
+      for (int e = 0; e < CI; ++e) {
+        const float f = ok ? chunk_elem<XT>(raw[c], e) : 0.f;
+        ss += f * f;
+      }
+    }
+    ss = wave_sum(ss);
+    const float inv = skip ? 0.f : 1.0f / sqrtf(ss / (float)sl + p.nrm.eps);
+    char* dst = xs + row * xp + seg * sl * (int)sizeof(S);
+    const char* gsrc = xg + seg * sl * 4;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < cps) {
+        const int e0 = ch * CI;
+        float y[CI];
+#pragma unroll
+        for (int q = 0; q < CI / 4; ++q) {
+          const f32x4 gq = *reinterpret_cast<const f32x4*>(gsrc + (e0 + 4 * q) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[4 * q + e] = (skip ? 0.f : chunk_elem<XT>(raw[c], 4 * q + e)) * inv * gq[e];
+        }
+        if constexpr (sizeof(S) == 4) {
+          f32x4 w = {y[0], y[1], y[2], y[3]};
+          *reinterpret_cast<f32x4*>(dst + e0 * 4) = w;
+        } else if constexpr (CI == 8) {
+          u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                     pack_bf16x2(y[6], y[7])};
+          *reinterpret_cast<u32x4*>(dst + e0 * 2) = w;
+        } else {
+          u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+          *reinterpret_cast<u32x2*>(dst + e0 * 2) = w;
+        }
+      }
+    }
+  }
+  __device__ void load(const GemmParams& p, int wave) {
+    if (wave < p.M * p.nrm.segs) load_pair(p, wave);
+    load_gains(p, 0);
+  }
+  __device__ void finish(const GemmParams& p, char* xs, int xp, char* xg, int wave, int nw) {
+    const int gch = p.nrm.segs * p.nrm.seg_len / 4;
+    const int round = GN * (int)blockDim.x;
+    store_gains(p, xg, 0);
+    for (int base = round; base < gch; base += round) {
+      load_gains(p, base);
+      store_gains(p, xg, base);
+    }
+    __syncthreads();
+    const int np = p.M * p.nrm.segs;
+    if (wave < np) store_pair(p, xs, xp, xg, wave);
+    for (int pr = wave + nw; pr < np; pr += nw) {
+      load_pair(p, pr);
+      store_pair(p, xs, xp, xg, pr);
+    }
+  }
+};
+
+// Chunks per lane held by NormStage: a segment of up to 3,072 elements.
+template <typename XT>
+constexpr int norm_chunks() { return 3 * (int)sizeof(XT); }
+
+// Steps per wave of gemm_stream_fnorm_kernel (its gains live in LDS).
+constexpr int kFnormMaxSteps = 16;
+
+__device__ __forceinline__ void clear_ints(const GemmParams& p) {
+  if (p.clear && blockIdx.x == 0)
+    for (int j = threadIdx.x; j < p.nclear; j += blockDim.x) p.clear[j] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -180,10 +338,238 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmParams p) {
   }
 }
 
+// Weight-streaming contraction over RMS-normalised float rows (M <= 16, one
+// segment): Y = W RMSNorm(X) with the norm folded into the stream,
+//   Y[m][n] = inv[m] * sum_k W[n][k] * S(X[m][k] * g[k]),
+//   inv[m] = 1 / sqrt(mean_k X[m][k]^2 + eps)          (zero for skipped rows)
+// ("Attention Drift", section 4.1).  Each wave reads its share of the float
+// rows with the weight steps (one round trip for both), multiplies by the
+// gains of its K share, which it keeps in its own slice of LDS, accumulates
+// the sum of squares of its elements, and the workgroup sums the partial
+// tiles and partial sums of squares through LDS in a fixed order before the
+// epilogue scales by inv.  The gain reads go out before the first weight
+// batch, so waiting for them never waits for it.
+template <typename S, int KS, int U, bool DUAL>
+__global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(4)))
+void gemm_stream_fnorm_kernel(GemmParams p) {
+  constexpr int CH = Storage<S>::CH;  // operand elements per lane per step
+  constexpr int STEP = 4 * CH;
+  constexpr int XQ = CH / 4;          // 16-byte float loads per lane per step
+  // per wave: the gains of its steps (at most kFnormMaxSteps), then KS*64
+  // partial sums of squares for the whole workgroup
+  extern __shared__ __attribute__((aligned(16))) char gs[];
+  const int lane = threadIdx.x & 63;
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nsteps = K / STEP;
+  const int fb = blockIdx.x;
+  const int s0 = (int)((int64_t)nsteps * ks / KS);
+  const int s1 = (int)((int64_t)nsteps * (ks + 1) / KS);
+  const bool xr = r < M;
+  const bool skip = xr && p.nrm.skip && p.nrm.skip[r];
+  // padding rows read row M-1 (their columns of the tile are never stored)
+  const char* xrow = reinterpret_cast<const char*>(reinterpret_cast<const float*>(p.X) +
+                                                   (int64_t)(xr ? r : M - 1) * p.ldx + g * CH);
+  const char* wb = reinterpret_cast<const char*>(p.W) + (int64_t)fb * nsteps * 1024 + lane * 16;
+  const char* wb2 = reinterpret_cast<const char*>(p.W2) + (int64_t)fb * nsteps * 1024 + lane * 16;
+  char* wg = gs + ks * (kFnormMaxSteps * STEP * 4);  // this wave's gains
+
+  // this wave's gains: (s1 - s0) * STEP floats, two 16-byte chunks per lane
+  const int gch = (s1 - s0) * STEP / 4;
+  const float* gsrc = p.nrm.gain + s0 * STEP;
+  f32x4 gt[kFnormMaxSteps * STEP / 256];
+#pragma unroll
+  for (int i = 0; i < kFnormMaxSteps * STEP / 256; ++i)
+    gt[i] = *reinterpret_cast<const f32x4*>(gsrc + 4 * min(lane + 64 * i, gch - 1));
+
+  u32x4 wv[U], w2v[U];
+  f32x4 xv[U][XQ];
+  auto load = [&](int s) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int su = min(s + u, s1 - 1);
+      wv[u] = ld16(wb + (int64_t)su * 1024);
+      if constexpr (DUAL) w2v[u] = ld16(wb2 + (int64_t)su * 1024);
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) xv[u][q] = *reinterpret_cast<const f32x4*>(xrow + (int64_t)su * STEP * 4 + 16 * q);
+    }
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  int s = s0;
+  if (s < s1) load(s);
+#pragma unroll
+  for (int i = 0; i < kFnormMaxSteps * STEP / 256; ++i)
+    if (lane + 64 * i < gch) *reinterpret_cast<f32x4*>(wg + 16 * (lane + 64 * i)) = gt[i];
+  __builtin_amdgcn_wave_barrier();  // LDS is in order within the wave
+  while (s < s1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s + u < s1) {
+        const int k0 = (s + u - s0) * STEP + g * CH;
+        float y[CH];
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+          const f32x4 gq = *reinterpret_cast<const f32x4*>(wg + (k0 + 4 * q) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = xv[u][q][e];
+            ss += x * x;
+            y[4 * q + e] = x * gq[e];
+          }
+        }
+        u32x4 b;
+        if constexpr (CH == 8) {
+          b = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+        } else {
+          b = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+        }
+        if (skip) b = u32x4{0u, 0u, 0u, 0u};  // rejected rows contribute zeros whatever they hold
+        mma16(acc, wv[u], b, S());
+        if constexpr (DUAL) mma16(acc2, w2v[u], b, S());
+      }
+    }
+    s += U;
+    if (s < s1) load(s);
+  }
+  float* ssr = reinterpret_cast<float*>(gs + KS * (kFnormMaxSteps * STEP * 4));
+  ssr[ks * 64 + lane] = ss;
+  if constexpr (KS > 1) {
+    __shared__ f32x4 red[(KS - 1) * 64 * (DUAL ? 2 : 1)];
+    if (ks > 0) {
+      red[(ks - 1) * 64 + lane] = acc;
+      if constexpr (DUAL) red[((KS - 1) + ks - 1) * 64 + lane] = acc2;
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int k = 0; k < KS - 1; ++k) {
+      acc += red[k * 64 + lane];
+      if constexpr (DUAL) acc2 += red[((KS - 1) + k) * 64 + lane];
+    }
+  } else {
+    __syncthreads();
+  }
+  if (xr) {
+    // the row's sum of squares: every wave, every lane group, in a fixed order
+    float tot = 0.f;
+    for (int w = 0; w < KS; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot += ssr[w * 64 + q * 16 + r];
+    const float inv = skip ? 0.f : 1.0f / sqrtf(tot / (float)K + p.nrm.eps);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = fb * 16 + 4 * g + j;
+      if (n < N) epi_store<S>(p.epi, r, n, acc[j] * inv, acc2[j] * inv);
+    }
+  }
+}
+
+// The same contraction with the activation rows staged once per workgroup in
+// LDS (row pitch K*elem + 16 bytes: the 16 lanes of one k-chunk hit distinct
+// banks), RMS-normalised on the way when NORM.  The activation reads are
+// issued first, then the first weight batch (and the second when EARLY2 and
+// the registers allow), so the staging hides under the weight stream's first
+// round trip; afterwards batch j+2 is in flight while batch j is multiplied.
+// At most 128 registers per lane: two 512-thread workgroups per CU, so the
+// 320-640 workgroups of the wide projections are resident at once.
+template <typename S, typename XT, int KS, int U, bool DUAL, bool NORM, bool EARLY2>
+__global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(4)))
+void gemm_stream_lds_kernel(GemmParams p) {
+  constexpr int CH = Storage<S>::CH;
+  constexpr int STEP = 4 * CH;
+  extern __shared__ __attribute__((aligned(16))) char xs[];
+  const int lane = threadIdx.x & 63;
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nsteps = K / STEP;
+  const int fb = blockIdx.x;
+  const int s0 = (int)((int64_t)nsteps * ks / KS);
+  const int s1 = (int)((int64_t)nsteps * (ks + 1) / KS);
+  const int nb = (s1 - s0 + U - 1) / U;  // batches of this wave
+  const char* wb = reinterpret_cast<const char*>(p.W) + (int64_t)fb * nsteps * 1024 + lane * 16;
+  const char* wb2 = reinterpret_cast<const char*>(p.W2) + (int64_t)fb * nsteps * 1024 + lane * 16;
+  u32x4 wv[2][U], w2v[2][U];
+  auto wload = [&](int j, int slot) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = (int64_t)min(s0 + j * U + u, s1 - 1) * 1024;
+      wv[slot][u] = ld16(wb + off);
+      if constexpr (DUAL) w2v[slot][u] = ld16(wb2 + off);
+    }
+  };
+  // activation reads first, then the weight batches (see CopyStage)
+  const int xp = K * (int)sizeof(S) + 16;
+  std::conditional_t<NORM, NormStage<S, XT, norm_chunks<XT>()>, CopyStage<S, 8>> stage;
+  if constexpr (NORM) stage.load(p, ks); else stage.load(p);
+  if (nb > 0) wload(0, 0);
+  if constexpr (EARLY2) {
+    if (nb > 1) wload(1, 1);
+  }
+  // LDS: M rows at pitch xp, the zero chunk, then the gains of a norm
+  if constexpr (NORM) stage.finish(p, xs, xp, xs + M * xp + 16, ks, KS); else stage.finish(p, xs, xp);
+  if constexpr (!EARLY2) {
+    if (nb > 1) wload(1, 1);
+  }
+  clear_ints(p);
+  if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(xs + M * xp) = zero4();
+  __syncthreads();
+
+  const bool xr = r < M;
+  const char* xrow = xr ? xs + r * xp + g * 16 : xs + M * xp;  // padding rows: the zero chunk
+  const int xstep = xr ? STEP * (int)sizeof(S) : 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+  auto batch = [&](int j, int slot) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int su = s0 + j * U + u;
+      if (su < s1) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + su * xstep);
+        mma16(acc, wv[slot][u], xv, S());
+        if constexpr (DUAL) mma16(acc2, w2v[slot][u], xv, S());
+      }
+    }
+  };
+  for (int j = 0; j < nb; j += 2) {
+    batch(j, 0);
+    if (j + 2 < nb) wload(j + 2, 0);
+    if (j + 1 < nb) {
+      batch(j + 1, 1);
+      if (j + 3 < nb) wload(j + 3, 1);
+    }
+  }
+  if constexpr (KS > 1) {
+    // the K-split partial tiles reuse the staged rows' LDS once every wave is done with them
+    __syncthreads();
+    f32x4* red = reinterpret_cast<f32x4*>(xs);
+    if (ks > 0) {
+      red[(ks - 1) * 64 + lane] = acc;
+      if constexpr (DUAL) red[((KS - 1) + ks - 1) * 64 + lane] = acc2;
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int k = 0; k < KS - 1; ++k) {
+      acc += red[k * 64 + lane];
+      if constexpr (DUAL) acc2 += red[((KS - 1) + k) * 64 + lane];
+    }
+  }
+  if (xr) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = fb * 16 + 4 * g + j;
+      if (n < N) epi_store<S>(p.epi, r, n, acc[j], acc2[j]);
+    }
+  }
+}
+
 // LM head for M <= 16: grid-stride over groups of NFB weight blocks; KS waves
 // per block split K and sum through LDS in ks order.  With XL the M
-// activation rows are staged once per workgroup in LDS by stage_rows (row
-// pitch K + 16 bytes, so the 16 lanes of one k-chunk hit distinct banks);
+// activation rows are staged once per workgroup in LDS, RMS-normalised on the
+// way when NORM (row pitch K*elem + 16 bytes, so the 16 lanes of one k-chunk
+// hit distinct banks);
 // without it (rows too wide for LDS) they are read from global memory,
 // padding rows from the zeroed buffer p.xzero.  Each wave streams its
 // weight steps in double-buffered batches of U: batch j+1 is in flight while
@@ -191,8 +577,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmParams p) {
 // first wave keeps the best (logit, lowest index) of its activation row; the
 // workgroup's best per row goes to partial slot [blockIdx][row], reduced by
 // argmax_reduce_kernel.
-template <typename S, int NFB, int KS, int U, bool XL>
-__global__ __launch_bounds__(64 * NFB * KS) void lm_argmax_stream_kernel(GemmParams p) {
+// Two workgroups per CU (four waves per SIMD, at most 128 registers per lane)
+// keep enough weight loads in flight.
+template <typename S, int NFB, int KS, int U, bool XL, bool NORM>
+__global__ __launch_bounds__(64 * NFB * KS) __attribute__((amdgpu_waves_per_eu(4)))
+void lm_argmax_stream_kernel(GemmParams p) {
   constexpr int CH = Storage<S>::CH;
   constexpr int STEP = 4 * CH;
   constexpr int NW = NFB * KS;
@@ -207,34 +596,47 @@ __global__ __launch_bounds__(64 * NFB * KS) void lm_argmax_stream_kernel(GemmPar
   const int nfb = (N + 15) >> 4;
   const int ntiles = (nfb + NFB - 1) / NFB;
   const bool xr = r < M;
+  const int nb = (s1 - s0 + U - 1) / U;  // batches per wave
+  const char* W = reinterpret_cast<const char*>(p.W) + lane * 16;
+  u32x4 wv[2][U];
+  auto wload = [&](const char* wb, int j, int slot) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) wv[slot][u] = ld16(wb + (int64_t)min(s0 + j * U + u, s1 - 1) * 1024);
+  };
+  // the first tile's first weight batch is requested right after the
+  // activation reads, so the staging hides under its round trip (not with a
+  // norm: its rows and the batch would not fit the 128 registers together)
+  const int fb0 = blockIdx.x * NFB + fbl;
+  const bool pre = !NORM && blockIdx.x < ntiles && fb0 < nfb && nb > 0;
   const char* xrow;
   int xstep;  // bytes per step (0: padding rows stay on a zero chunk)
   if constexpr (XL) {
     const int xp = K * (int)sizeof(S) + 16;  // LDS row pitch, bytes
-    stage_rows<S>(p, xs, xp);
+    std::conditional_t<NORM, NormStage<S, float, norm_chunks<float>()>, CopyStage<S, 8>> stage;
+    if constexpr (NORM) stage.load(p, wave); else stage.load(p);
+    if (pre) wload(W + (int64_t)fb0 * nsteps * 1024, 0, 0);
+    // LDS: M rows at pitch xp, the zero chunk, then the gains of a norm
+    if constexpr (NORM) stage.finish(p, xs, xp, xs + M * xp + 16, wave, NW); else stage.finish(p, xs, xp);
+    clear_ints(p);
+    if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(xs + M * xp) = zero4();
+    __syncthreads();
     xrow = xr ? xs + r * xp + g * 16 : xs + M * xp;
     xstep = xr ? STEP * (int)sizeof(S) : 0;
   } else {
+    if (pre) wload(W + (int64_t)fb0 * nsteps * 1024, 0, 0);
     xrow = xr ? reinterpret_cast<const char*>(reinterpret_cast<const S*>(p.X) + (int64_t)r * p.ldx + g * CH)
               : reinterpret_cast<const char*>(p.xzero) + g * 16;
     xstep = STEP * (int)sizeof(S);  // p.xzero holds >= K zeroed elements
   }
-  const char* W = reinterpret_cast<const char*>(p.W) + lane * 16;
   __shared__ f32x4 red[KS > 1 ? NFB * (KS - 1) * 64 : 1];
   float best = -INFINITY;
   int bidx = 0x7fffffff;
-  const int nb = (s1 - s0 + U - 1) / U;  // batches per wave
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int fb = tile * NFB + fbl;
     const bool active = fb < nfb;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (active) {
       const char* wb = W + (int64_t)fb * nsteps * 1024;
-      u32x4 wv[2][U];
-      auto wload = [&](int j, int slot) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) wv[slot][u] = ld16(wb + (int64_t)min(s0 + j * U + u, s1 - 1) * 1024);
-      };
       auto batch = [&](int j, int slot) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -242,11 +644,11 @@ __global__ __launch_bounds__(64 * NFB * KS) void lm_argmax_stream_kernel(GemmPar
           if (su < s1) mma16(acc, wv[slot][u], ld16(xrow + (int64_t)su * xstep), S());
         }
       };
-      wload(0, 0);
+      if (!pre || tile != (int)blockIdx.x) wload(wb, 0, 0);  // else the first tile's went out before the staging
       for (int j = 0; j < nb; j += 2) {
-        if (j + 1 < nb) wload(j + 1, 1);
+        if (j + 1 < nb) wload(wb, j + 1, 1);
         batch(j, 0);
-        if (j + 2 < nb) wload(j + 2, 0);
+        if (j + 2 < nb) wload(wb, j + 2, 0);
         if (j + 1 < nb) batch(j + 1, 1);
       }
     }
@@ -547,27 +949,161 @@ static void launch_stream(const GemmParams& p, hipStream_t s) {
   }
 }
 
+// Weight steps per batch of the LDS-staged streaming kernel: two batches
+// cover the 16-17 steps per wave of the widest decode contractions (fc with
+// its norm, 9; down, 8) and the 11-12 of the gate/up pair (6).
+template <bool DUAL, bool NORM>
+constexpr int stream_lds_u() { return DUAL ? 6 : NORM ? 9 : 8; }
+// Second weight batch requested before the staging finishes (registers
+// permitting: not beside the rows of a norm).
+template <typename XT, bool NORM>
+constexpr bool stream_lds_early2() { return !NORM; }
+// Largest LDS block it stages: the activation rows, the zero chunk and the
+// gains of a norm (the K-split reduction reuses the same bytes afterwards).
+static constexpr int kStreamXLds = 156 * 1024;
+
+template <typename S, typename XT, int KS, bool DUAL, bool NORM>
+static void launch_stream_lds_ks(const GemmParams& p, size_t lds, hipStream_t s) {
+  constexpr int U = stream_lds_u<DUAL, NORM>();
+  constexpr bool E2 = stream_lds_early2<XT, NORM>();
+  const size_t red = (size_t)(KS - 1) * 64 * 16 * (DUAL ? 2 : 1);
+  if (lds < red) lds = red;
+  allow_lds<&gemm_stream_lds_kernel<S, XT, KS, U, DUAL, NORM, E2>>(kStreamXLds);
+  hipLaunchKernelGGL((gemm_stream_lds_kernel<S, XT, KS, U, DUAL, NORM, E2>), dim3((p.N + 15) / 16),
+                     dim3(64 * KS), lds, s, p);
+}
+
+template <typename S, typename XT, bool DUAL, bool NORM>
+static void launch_stream_lds(const GemmParams& p, size_t lds, hipStream_t s) {
+  switch (stream_ks(p.K / (4 * Storage<S>::CH))) {
+    case 16: launch_stream_lds_ks<S, XT, 16, DUAL, NORM>(p, lds, s); break;
+    case 8: launch_stream_lds_ks<S, XT, 8, DUAL, NORM>(p, lds, s); break;
+    case 4: launch_stream_lds_ks<S, XT, 4, DUAL, NORM>(p, lds, s); break;
+    case 2: launch_stream_lds_ks<S, XT, 2, DUAL, NORM>(p, lds, s); break;
+    default: launch_stream_lds_ks<S, XT, 1, DUAL, NORM>(p, lds, s); break;
+  }
+}
+
+// Float rows normalised inside the weight stream: the gate/up pair takes 6
+// steps per batch (its two weight streams and the float rows share the 128
+// registers), single contractions 8.
+// Steps per batch of gemm_stream_fnorm_kernel, measured on the c=1 decode
+// shapes (11-12 steps per wave): 6 for single contractions (two full
+// batches, no clamped re-reads), 4 for the gate/up pair (its two weight
+// streams and the float rows fit the 128 registers without spilling).
+#ifndef PE_FNORM_U
+#define PE_FNORM_U 6
+#endif
+#ifndef PE_FNORM_DUAL_U
+#define PE_FNORM_DUAL_U 4
+#endif
+// Which float-row norms fold into the stream (1: single contractions, 2: the
+// gate/up pair; else a separate rmsnorm_rows_kernel runs first).
+#ifndef PE_FNORM_KINDS
+#define PE_FNORM_KINDS 3
+#endif
+template <typename S, bool DUAL>
+static void launch_stream_fnorm(const GemmParams& p, int ks, hipStream_t s) {
+  constexpr int U = DUAL ? PE_FNORM_DUAL_U : PE_FNORM_U;
+  const dim3 grid((p.N + 15) / 16);
+  const size_t lds = (size_t)ks * (kFnormMaxSteps * 4 * Storage<S>::CH * 4) + (size_t)ks * 64 * 4;
+  switch (ks) {
+    case 16: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 16, U, DUAL>), grid, dim3(1024), lds, s, p); break;
+    case 8: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 8, U, DUAL>), grid, dim3(512), lds, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 4, U, DUAL>), grid, dim3(256), lds, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 2, U, DUAL>), grid, dim3(128), lds, s, p); break;
+    default: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 1, U, DUAL>), grid, dim3(64), lds, s, p); break;
+  }
+}
+
+// The requested RMSNorm as its own kernel into p.nrm.tmp (also clearing
+// p.clear); returns the parameters of the contraction over the normalised rows.
 template <typename S>
-static int launch_gemm_t(const GemmParams& p, hipStream_t s) {
-  const bool dual = p.epi.kind == EPI_SWIGLU;
-  const bool am = p.epi.kind == EPI_ARGMAX;
-  if (p.M <= 16) {
+static GemmParams norm_first(const GemmParams& p, hipStream_t s) {
+  NormParams np{};
+  np.in = p.X;
+  np.ld_in = p.ldx;
+  np.skip = p.nrm.skip;
+  np.n = p.M;
+  np.segs = p.nrm.segs;
+  np.d = p.nrm.seg_len;
+  np.gain = p.nrm.gain;
+  np.eps = p.nrm.eps;
+  np.out = p.nrm.tmp;
+  np.ld_out = p.K;
+  np.zero = p.clear;
+  np.nzero = p.nclear;
+  const int sbf = sizeof(S) == 2;
+  launch_rmsnorm_rows(np, p.nrm.x_f32 ? 0 : sbf, sbf, s);
+  GemmParams q = p;
+  q.X = p.nrm.tmp;
+  q.ldx = p.K;
+  q.nrm = NormIn{};
+  q.clear = nullptr;
+  q.nclear = 0;
+  return q;
+}
+
+template <typename S>
+static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
+  const bool dual = p0.epi.kind == EPI_SWIGLU;
+  const bool am = p0.epi.kind == EPI_ARGMAX;
+  const bool norm = p0.nrm.gain != nullptr;
+  if (p0.M <= 16) {
+    // activation rows + the zero chunk of the padding rows (+ the gains of a norm)
+    const size_t lds = (size_t)p0.M * (p0.K * sizeof(S) + 16) + 16 + (norm ? (size_t)p0.K * 4 : 0);
+    const int xsz = norm && p0.nrm.x_f32 ? 4 : (int)sizeof(S);
+    const int seg_bytes = p0.nrm.seg_len * xsz;
+    const bool xf32 = xsz == 4;
+    // NormStage holds a segment in norm_chunks<XT>() chunks per lane and reads
+    // the gains as 16-byte vectors
+    const bool norm_fits = !norm || (seg_bytes % 16 == 0 && seg_bytes / 16 <= 64 * (xf32 ? 12 : 6) &&
+                                     (reinterpret_cast<uintptr_t>(p0.nrm.gain) & 15) == 0);
     if (am) {
-      const int grid = gemm_argmax_partials(p.M, p.N);
-      const size_t lds = (size_t)p.M * (p.K * sizeof(S) + 16) + 16;  // activation rows + zero chunk
+      const int grid = gemm_argmax_partials(p0.M, p0.N);
+      const dim3 block(64 * kLmNFB * kLmKS);
+      if (lds <= (size_t)kLmXLds && norm_fits && (!norm || xf32)) {
+        if (norm) {
+          allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, true>>(kLmXLds);
+          hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, true>), dim3(grid), block, lds, s,
+                             p0);
+        } else {
+          allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false>>(kLmXLds);
+          hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false>), dim3(grid), block, lds,
+                             s, p0);
+        }
+        return grid;
+      }
+      const GemmParams p = norm ? norm_first<S>(p0, s) : p0;
       if (lds <= (size_t)kLmXLds) {
-        allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true>>(kLmXLds);
-        hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true>), dim3(grid),
-                           dim3(64 * kLmNFB * kLmKS), lds, s, p);
+        allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false>>(kLmXLds);
+        hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false>), dim3(grid), block, lds, s,
+                           p);
       } else {
-        hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, false>), dim3(grid),
-                           dim3(64 * kLmNFB * kLmKS), 0, s, p);
+        hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, false, false>), dim3(grid), block, 0, s,
+                           p);
       }
       return grid;
     }
+    const int fks = stream_ks(p0.K / (4 * Storage<S>::CH));
+    const int fsteps = (p0.K / (4 * Storage<S>::CH) + fks - 1) / fks;
+    if (norm && xf32 && fsteps <= kFnormMaxSteps && (reinterpret_cast<uintptr_t>(p0.nrm.gain) & 15) == 0 &&
+        p0.nrm.segs == 1 && (PE_FNORM_KINDS & (dual ? 2 : 1))) {
+      // float rows (the residual stream): the norm folds into the weight stream
+      if (dual) launch_stream_fnorm<S, true>(p0, fks, s); else launch_stream_fnorm<S, false>(p0, fks, s);
+      return 0;
+    }
+    if (norm && norm_fits && !xf32 && !dual && lds <= (size_t)kStreamXLds) {
+      // storage-type rows (the captured streams, several segments): normalised
+      // while they are staged in LDS
+      launch_stream_lds<S, S, false, true>(p0, lds, s);
+      return 0;
+    }
+    const GemmParams p = norm ? norm_first<S>(p0, s) : p0;
     if (dual) launch_stream<S, true>(p, s); else launch_stream<S, false>(p, s);
     return 0;
   }
+  const GemmParams p = norm ? norm_first<S>(p0, s) : p0;
   const bool big = p.M >= 256;
   if (am) return big ? launch_tiled<S, 128, 128, false, true>(p, s) : launch_tiled<S, 64, 64, false, true>(p, s);
   if (dual) { if (big) launch_tiled<S, 128, 64, true, false>(p, s); else launch_tiled<S, 64, 64, true, false>(p, s); }

@@ -65,6 +65,21 @@ struct Epi {
   int32_t* part_idx;     // argmax: [P, M] their indices
 };
 
+// RMSNorm applied to the activation rows on their way into a contraction
+// (gain == nullptr: X is the operand as is).  Row m of the operand is
+//   X[m][s*seg_len + c] * inv * gain[s*seg_len + c],
+//   inv = 1 / sqrt(mean_c X[m][s*seg_len + c]^2 + eps)   (zero for skipped rows)
+// for each of the segs segments (segs * seg_len = K).
+struct NormIn {
+  const float* gain;
+  int segs, seg_len;
+  float eps;
+  const uint8_t* skip;  // flags indexed by row, or nullptr
+  int x_f32;            // X holds float32 (else the storage type)
+  void* tmp;            // [M, K] storage type: normalised rows when the norm
+                        // cannot be fused into the contraction's staging
+};
+
 struct GemmParams {
   const void* X;
   int64_t ldx;
@@ -73,6 +88,9 @@ struct GemmParams {
   int M, N, K;
   const void* xzero;  // M <= 16: >= K zeroed elements, 16-byte aligned (padding rows of X)
   Epi epi;
+  NormIn nrm;
+  int* clear;  // with a norm: ints zeroed by the launch (the padding-row buffer of later launches), or nullptr
+  int nclear;
 };
 
 
@@ -80,7 +98,9 @@ struct GemmParams {
 // streamed by the GEMM kernels (see gemm.hip).
 void launch_pack(const void* src, void* dst, int N, int row_bytes, hipStream_t s);
 // Chooses the weight-streaming kernel (M <= 16) or the LDS-tiled kernel.
-// W (and W2) are packed weights.
+// W (and W2) are packed weights.  A requested RMSNorm (p.nrm.gain) is fused
+// into the activation staging of the streaming kernels when the rows fit in
+// LDS; otherwise rmsnorm_rows_kernel writes p.nrm.tmp first.
 // EPI_ARGMAX returns the number of partial rows P to reduce with
 // launch_argmax_reduce; every other kind returns 0.
 int launch_gemm(const GemmParams& p, int bf16, hipStream_t s);

@@ -4,8 +4,10 @@ Each case runs the four stage calls through the C ABI (via DraftStep) and
 checks, stage by stage: the draft batch bit for bit; x0; the layer output of
 the query rows, the K/V rows written, and that rejected / unwritten cache
 rows keep their sentinel bits; logits and greedy tokens.  Cases cover both
-storage dtypes, both GEMM kernels (M <= 16 and M > 16), ragged windows,
-fully rejected windows, K = 1, and the full-size c=1 and c=64 decode steps.
+storage dtypes, the GEMM kernels (M <= 16 with rows staged in LDS and the
+norm fused, or rows in global memory after a separate norm; M > 16 tiled),
+ragged windows, fully rejected windows, K = 1, and full-size decode steps
+with 1, 2 and 64 requests.
 """
 import numpy as np
 import pytest
@@ -152,6 +154,15 @@ def test_decode_c1_full_size():
     dims = si.GPTOSS_DIMS
     _, _, c = si.decode_config(1, with_weights=False)
     check_case("decode c=1 d=2880 V=201088", dims, gptoss_weights(), c)
+
+
+def test_decode_two_requests_full_size():
+    # T = 15 rows with one rejected window row: the fc and down-projection rows
+    # exceed LDS (separate norm, then the weight stream over rows in global
+    # memory); the other contractions stage their rows in LDS, norm fused
+    dims = si.GPTOSS_DIMS
+    c = si.decode_case(dims, 14, R=2, K=7, W=[1, 0], kv_len=[700, 1500], n_rej=[1, 0])
+    check_case("decode R=2 K=7 d=2880 V=201088", dims, gptoss_weights(), c)
 
 
 def test_decode_c64_full_size():
