@@ -26,7 +26,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch of the LM-head stage measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE, scaled by a 1 GiB copy (profiles/decode_c1_lm_head_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
-LM_STAGE_TRAFFIC = {"fingerprint": "5d5c6e7df0c3e094", "bytes": 1160502358}
+LM_STAGE_TRAFFIC = {"fingerprint": "1bf6dd7a6ac7e33e", "bytes": 1162042534}
 LM_SOURCES = ("gemm.hip", "norm.hip", "common.h", "kernels.h")
 
 
@@ -87,7 +87,7 @@ def decode_bytes(dims, case, T, RK):
     keys = int(np.sum(case["kv_len"].astype(np.int64) + n_acc + case["K"]))   # rows read per kv head
     live = int(np.sum(n_acc)) + RK
     kv = keys * 2 * kvc * e + live * 2 * kvc * e
-    hidden = T * 3 * d * e * 3                     # target rows read, draft rows written, read by the norm
+    hidden = T * 3 * d * e * 3                     # target rows read, draft rows written, read by fc
     emb = T * d * e
     act = T * d * 4 + RK * d * 4 + RK * 4
     return weights + kv + hidden + emb + act, weights
@@ -180,13 +180,12 @@ def main():
         ms = ms_eager
         launch_mode = "the four stage calls launched eagerly on one stream"
 
-    # dominant kernel: the LM-head stage (final RMSNorm rows, the W_lm stream
-    # with the fused argmax, the reduce of the per-workgroup partials)
+    # dominant kernel: the LM-head stage (the W_lm stream with the final
+    # RMSNorm in its staging and the fused argmax, then the reduce of the
+    # per-workgroup partials)
     lm_ms = time_loop(lambda: st.lm_head(False), args.steps, args.warmup, stream)
-    # algorithmic bytes: W_lm once, x read (f32), normalised rows written and
-    # read (bf16), per-workgroup (value, index) partials written and read, tokens
-    n_part = -(-dims.vocab // 64)
-    lm_bytes = dims.vocab * dims.hidden * 2 + RK * dims.hidden * (4 + 2 + 2) + 2 * n_part * RK * 8 + RK * 4
+    # algorithmic bytes: W_lm once, the x rows (f32), the tokens
+    lm_bytes = dims.vocab * dims.hidden * 2 + RK * dims.hidden * 4 + RK * 4
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
     log("LM head stage: %.1f us, %.0f GB/s" % (lm_ms * 1e3, lm_gbs))
 
@@ -213,7 +212,7 @@ def main():
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm",
-                     "kernel": "LM-head stage: final RMSNorm + W_lm stream with fused argmax + partial reduce",
+                     "kernel": "LM-head stage: W_lm stream with the final RMSNorm and the argmax fused, partial reduce",
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
                      "traffic": (LM_STAGE_TRAFFIC["bytes"]
                                  if source_fingerprint() == LM_STAGE_TRAFFIC["fingerprint"] else None),
