@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the c=64 decode and attention measurements")
     ap.add_argument("--attention-only", type=int, choices=(3, 4), default=0,
                     help="time only the COD (3) or parallel-group (4) attention workload and print its line")
+    ap.add_argument("--decode64-only", action="store_true",
+                    help="time only the c=64 decode step and print its line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also copy 1 GiB device-to-device 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -139,6 +141,33 @@ def measure_attention(cfg, steps, stream):
             "launches": len(chunks)}
 
 
+def measure_decode64(dims, W, steps, stream):
+    """The c=64 decode step (64 requests x 7 slots, ragged caches), one graph
+    replay per step: time, rate, HBM and matrix-core fractions."""
+    import numpy as np
+    import torch
+    from drafter_pe_build_amd.step import DraftStep, GraphStep
+    from synth import inputs as si
+    log("c=64 decode step")
+    _, _, case2 = si.decode_config(2, with_weights=False)
+    st2 = DraftStep(dims, W, case2)
+    RK2 = st2.R * st2.K
+    gs2 = GraphStep(st2)
+    ms2 = time_loop(gs2.replay, steps, 3, stream)
+    b2, _ = decode_bytes(dims, case2, st2.T, RK2)
+    live2 = int(np.sum(np.diff(case2["cu_window"]) - case2["n_rej"])) + RK2
+    fl2 = 2.0 * (live2 * (3 * dims.hidden * dims.hidden + dims.qkv_rows * dims.hidden)
+                 + RK2 * (dims.hidden * dims.n_q_heads * dims.head_dim + 3 * dims.ffn * dims.hidden
+                          + dims.vocab * dims.hidden))
+    log("  %.1f us" % (ms2 * 1e3))
+    del gs2, st2
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms2, "draft_positions_per_s": RK2 / (ms2 * 1e-3),
+            "hbm_gbs": b2 / (ms2 * 1e-3) / 1e9, "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gemm_tflops": fl2 / (ms2 * 1e-3) / 1e12,
+            "mfma_frac": fl2 / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -161,6 +190,13 @@ def main():
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
         return
     dims = si.GPTOSS_DIMS
+    if args.decode64_only:
+        log("generating the drafter weights")
+        r = measure_decode64(dims, si.drafter_weights(dims, 1), args.steps, stream)
+        print(json.dumps({"metric": "decode_c64_draft_positions_per_s", "value": r["draft_positions_per_s"],
+                          "unit": "draft positions/s", "higher_is_better": True, "dtype": "bf16",
+                          "data": "synthetic", **r}), flush=True)
+        return
     log("generating the c=1 decode inputs and the drafter weights")
     t0 = time.time()
     W = si.drafter_weights(dims, 1)
@@ -231,24 +267,7 @@ def main():
 
     if not args.no_extra:
         extra = {}
-        log("c=64 decode step")
-        _, _, case2 = si.decode_config(2, with_weights=False)
-        st2 = DraftStep(dims, W, case2)
-        RK2 = st2.R * st2.K
-        gs2 = GraphStep(st2)
-        ms2 = time_loop(gs2.replay, max(5, args.steps // 5), 3, stream)
-        b2, _ = decode_bytes(dims, case2, st2.T, RK2)
-        live2 = int(np.sum(np.diff(case2["cu_window"]) - case2["n_rej"])) + RK2
-        fl2 = 2.0 * (live2 * (3 * dims.hidden * dims.hidden + dims.qkv_rows * dims.hidden)
-                     + RK2 * (dims.hidden * dims.n_q_heads * dims.head_dim + 3 * dims.ffn * dims.hidden
-                              + dims.vocab * dims.hidden))
-        extra["decode_c64"] = {"ms_per_step": ms2, "draft_positions_per_s": RK2 / (ms2 * 1e-3),
-                               "hbm_gbs": b2 / (ms2 * 1e-3) / 1e9, "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                               "gemm_tflops": fl2 / (ms2 * 1e-3) / 1e12,
-                               "mfma_frac": fl2 / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-        log("  %.1f us" % (ms2 * 1e3))
-        del gs2, st2
-        torch.cuda.empty_cache()
+        extra["decode_c64"] = measure_decode64(dims, W, max(5, args.steps // 5), stream)
         for cfg, name in ((3, "cod_attention_n4096"), (4, "group_attention_n8192_chunked")):
             extra[name] = measure_attention(cfg, max(5, args.steps // 5), stream)
         result["secondary"] = extra

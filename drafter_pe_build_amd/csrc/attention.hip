@@ -70,12 +70,6 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return r;
 }
 
-// One 16-byte copy per lane from global memory straight into LDS: lane l
-// writes bytes [16 l, 16 l + 16) after the wave-uniform LDS address dst.
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-}
-
 // Max and sum over the four lanes r, r+16, r+32, r+48 (one matrix-core
 // column), with the gfx950 lane-swap instructions: after a swap of the two
 // 32-lane halves (then of the 16-lane rows within them) every lane holds its

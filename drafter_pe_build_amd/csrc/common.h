@@ -52,6 +52,13 @@ __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// One 16-byte copy per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l writes bytes [16 l, 16 l + 16) after the
+// wave-uniform LDS address dst.  Counted by vmcnt like any global load.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
 // One 16-byte-per-lane contraction step into a 16x16 f32 tile.
 __device__ __forceinline__ void mma16(f32x4& acc, u32x4 a, u32x4 b, uint16_t) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),

@@ -1,0 +1,48 @@
+// The epilogues that finish a contraction element Y[m][n] (see EpiKind in
+// kernels.h), shared by the streaming and the tiled kernels.
+#pragma once
+#include "kernels.h"
+
+namespace pe {
+
+template <typename S>
+__device__ __forceinline__ void epi_store(const Epi& e, int m, int n, float y, float y2) {
+  switch (e.kind) {
+    case EPI_FC: {
+      if (e.rejected && e.rejected[m]) return;
+      const int id = e.ids[m];
+      float emb = 0.f;
+      if (id >= 0 && id < e.embed_rows)
+        emb = Storage<S>::to_f32(reinterpret_cast<const S*>(e.embed)[(int64_t)id * e.ld_out + n]);
+      e.out_f32[(int64_t)m * e.ld_out + n] = y + emb;
+      break;
+    }
+    case EPI_QKV: {
+      if (n < e.q_cols) {
+        reinterpret_cast<S*>(e.out_s)[(int64_t)m * e.q_cols + n] = Storage<S>::from_f32(y);
+      } else {
+        const int slot = e.slots[m];
+        if (slot < 0 || slot >= e.kv_rows) return;
+        int c = n - e.q_cols;
+        S* dst = reinterpret_cast<S*>(c < e.kv_cols ? e.k_cache : e.v_cache);
+        if (c >= e.kv_cols) c -= e.kv_cols;
+        dst[(int64_t)slot * e.kv_cols + c] = Storage<S>::from_f32(y);
+      }
+      break;
+    }
+    case EPI_RESID: {
+      const int rr = e.res_rows ? e.res_rows[m] : m;
+      e.out_f32[(int64_t)m * e.ld_out + n] = y + e.res[(int64_t)rr * e.ld_res + n];
+      break;
+    }
+    case EPI_SWIGLU: {
+      const float si = y / (1.0f + __expf(-y));
+      reinterpret_cast<S*>(e.out_s)[(int64_t)m * e.ld_out + n] = Storage<S>::from_f32(si * y2);
+      break;
+    }
+    default:
+      break;
+  }
+}
+
+}  // namespace pe

@@ -27,7 +27,7 @@
 //    i % 8) so the weight chunks are fetched from HBM once.
 #include <math.h>
 #include <type_traits>
-#include "kernels.h"
+#include "epilogue.h"
 
 namespace pe {
 
@@ -54,46 +54,6 @@ void launch_pack(const void* src, void* dst, int N, int row_bytes, hipStream_t s
   const int64_t total16 = (int64_t)((N + 15) / 16) * (row_bytes / 64) * 64;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((total16 + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const char*>(src), reinterpret_cast<char*>(dst), N, row_bytes, total16);
-}
-
-template <typename S>
-__device__ __forceinline__ void epi_store(const Epi& e, int m, int n, float y, float y2) {
-  switch (e.kind) {
-    case EPI_FC: {
-      if (e.rejected && e.rejected[m]) return;
-      const int id = e.ids[m];
-      float emb = 0.f;
-      if (id >= 0 && id < e.embed_rows)
-        emb = Storage<S>::to_f32(reinterpret_cast<const S*>(e.embed)[(int64_t)id * e.ld_out + n]);
-      e.out_f32[(int64_t)m * e.ld_out + n] = y + emb;
-      break;
-    }
-    case EPI_QKV: {
-      if (n < e.q_cols) {
-        reinterpret_cast<S*>(e.out_s)[(int64_t)m * e.q_cols + n] = Storage<S>::from_f32(y);
-      } else {
-        const int slot = e.slots[m];
-        if (slot < 0 || slot >= e.kv_rows) return;
-        int c = n - e.q_cols;
-        S* dst = reinterpret_cast<S*>(c < e.kv_cols ? e.k_cache : e.v_cache);
-        if (c >= e.kv_cols) c -= e.kv_cols;
-        dst[(int64_t)slot * e.kv_cols + c] = Storage<S>::from_f32(y);
-      }
-      break;
-    }
-    case EPI_RESID: {
-      const int rr = e.res_rows ? e.res_rows[m] : m;
-      e.out_f32[(int64_t)m * e.ld_out + n] = y + e.res[(int64_t)rr * e.ld_res + n];
-      break;
-    }
-    case EPI_SWIGLU: {
-      const float si = y / (1.0f + __expf(-y));
-      reinterpret_cast<S*>(e.out_s)[(int64_t)m * e.ld_out + n] = Storage<S>::from_f32(si * y2);
-      break;
-    }
-    default:
-      break;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1104,9 +1064,14 @@ static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
     return 0;
   }
   const GemmParams p = norm ? norm_first<S>(p0, s) : p0;
-  const bool big = p.M >= 256;
+  // 128-wide tiles only when they still give every CU two workgroups (the
+  // N = 2,880 projections get 64 x 64 tiles)
+  const bool big = p.M >= 256 && (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) >= 512;
+  // the LM head of a large batch: 256 x 256 tiles through LDS
+  if (am && sizeof(S) == 2 && p.M >= 128 && p.K >= 64) return launch_gemm_big(p, s);
   if (am) return big ? launch_tiled<S, 128, 128, false, true>(p, s) : launch_tiled<S, 64, 64, false, true>(p, s);
-  if (dual) { if (big) launch_tiled<S, 128, 64, true, false>(p, s); else launch_tiled<S, 64, 64, true, false>(p, s); }
+  // the gate/up pair keeps 128 x 64 tiles from 256 rows on (two weight streams per tile)
+  if (dual) { if (p.M >= 256) launch_tiled<S, 128, 64, true, false>(p, s); else launch_tiled<S, 64, 64, true, false>(p, s); }
   else { if (big) launch_tiled<S, 128, 128, false, false>(p, s); else launch_tiled<S, 64, 64, false, false>(p, s); }
   return 0;
 }

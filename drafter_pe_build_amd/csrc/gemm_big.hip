@@ -1,0 +1,240 @@
+// Large-M contractions on the gfx950 matrix cores, bf16 operands:
+//   Y[m][n] = sum_k X[m][k] * W[n][k]   (X: [M, K] activation rows, W: packed weights)
+// for the batched decode shapes (M in the hundreds), finished by the same
+// epilogues as the other contractions (gemm.hip).
+//
+// A workgroup of 8 waves (2 x 4) owns an output tile of BM activation rows x
+// BN features; each wave a (BM/2) x (BN/4) sub-tile accumulated in registers
+// (128 x 64 of a 256 x 256 tile: 128 accumulator registers per lane, two
+// waves per SIMD).  Both operands go through LDS in a ring of four stages,
+// one 32-wide k-step each, copied by global_load_lds_dwordx4 without passing
+// through registers; three k-steps are in flight while one is multiplied
+// (the copies come from HBM for the weights and take one loaded round trip,
+// about the time of three steps of matrix work):
+//  * weights: the packed 1 KB chunks as they are (one chunk = the operand of
+//    one 16-feature x 32-k step, lane l's 16 bytes at 16 l), so a wave reads
+//    its operand with one conflict-free ds_read_b128;
+//  * activations: 64 bytes (32 k) per row, the four 16-byte chunks of row R
+//    stored at position chunk ^ ((R >> 1) & 3), so the rows of one operand
+//    read land in distinct banks.  Rows past M copy row M-1 (their results
+//    are dropped).
+// One barrier per k-step.  Workgroup ids map the M tiles of one N tile back
+// to back onto one XCD (workgroup i runs on XCD i % 8), so each weight chunk
+// is fetched from HBM once.  L2->LDS traffic per flop is (BM + BN) / (BM BN)
+// bytes: 1/128 for 256 x 256, half of the 128 x 128 tiles' figure.
+#include <math.h>
+#include "epilogue.h"
+
+namespace pe {
+
+// Waits until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 12 + 12) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else static_assert(N == 0, "add this count");
+}
+
+// Two waves per SIMD: two 4-wave workgroups (or one 8-wave one) per CU.
+template <int BM, int BN, int WN, int D, bool DUAL, bool ARGMAX>
+__global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
+  constexpr int NW = 2 * WN;           // waves: 2 along the rows x WN along the features
+  constexpr int WB = BN / 16;          // 16-feature weight blocks per tile
+  constexpr int FW = BN / 16 / WN;     // weight blocks per wave
+  constexpr int RW = BM / 32;          // 16-row activation groups per wave
+  constexpr int WBYTES = WB * 1024;    // one weight matrix, one k-step
+  constexpr int XOFF = WBYTES * (DUAL ? 2 : 1);
+  constexpr int STAGE = XOFF + BM * 64;
+  constexpr int WI = WB / NW;          // weight copies per wave per k-step (per matrix)
+  constexpr int XI = BM / 16 / NW;     // activation copies per wave per k-step
+  constexpr int PT = WI * (DUAL ? 2 : 1) + XI;  // vector-memory operations per wave per k-step
+  static_assert(BM % 32 == 0 && BN % 64 == 0 && WB % NW == 0 && (BM / 16) % NW == 0, "tile shape");
+  extern __shared__ __attribute__((aligned(16))) char lds[];  // D stages
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, jj = bid >> 3;
+  const int mt = jj % n_mt;
+  const int ft = (jj / n_mt) * 8 + xcd;
+  if (ft >= n_ft) return;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nsteps = K / 32;
+  const int nfb = (N + 15) >> 4;
+  const int n0 = ft * BN, m0 = mt * BM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int wm = wave / WN, wn = wave % WN;
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(p.X);
+
+  // weight chunks this wave copies: blocks wave + NW * i (clamped past N)
+  const char* wsrc[WI];
+  const char* w2src[DUAL ? WI : 1];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int64_t off = (int64_t)min(n0 / 16 + wave + NW * i, nfb - 1) * nsteps * 1024 + lane * 16;
+    wsrc[i] = reinterpret_cast<const char*>(p.W) + off;
+    if constexpr (DUAL) w2src[i] = reinterpret_cast<const char*>(p.W2) + off;
+  }
+  // activation chunks: instruction i covers rows 16 (wave + NW i) .. +15, four
+  // 16-byte chunks each; row R keeps chunk c at position c ^ ((R >> 1) & 3)
+  const uint16_t* xsrc[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int row = (wave + NW * i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * p.ldx + c * 8;
+  }
+  auto issue = [&](int t) {
+    char* st = lds + (t % D) * STAGE;
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      copy16_to_lds(wsrc[i] + (int64_t)t * 1024, st + (wave + NW * i) * 1024);
+      if constexpr (DUAL) copy16_to_lds(w2src[i] + (int64_t)t * 1024, st + WBYTES + (wave + NW * i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < XI; ++i) copy16_to_lds(xsrc[i] + t * 32, st + XOFF + (wave + NW * i) * 1024);
+  };
+
+  f32x4 acc[FW][RW], acc2[DUAL ? FW : 1][DUAL ? RW : 1];
+#pragma unroll
+  for (int f = 0; f < FW; ++f)
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+      acc[f][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (DUAL) acc2[f][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // Pipeline: every stage of the ring holds a k-step in flight or resident.
+  // Iteration t: issue step t's matrix products (their operands are already
+  // in registers), then wait until step t+1 has landed (the barrier also
+  // means every wave is done reading step t's stage), refill that stage with
+  // step t+D and read step t+1's operands into the other register set while
+  // the products run.
+  u32x4 fa[2][FW], fa2[2][DUAL ? FW : 1], fb[2][RW];
+#define PE_BIG_FRAGS(T, SET)                                                                             \
+  {                                                                                                      \
+    const char* st_ = lds + ((T) % D) * STAGE;                                                           \
+    _Pragma("unroll") for (int f = 0; f < FW; ++f) {                                                     \
+      fa[SET][f] = *reinterpret_cast<const u32x4*>(st_ + (wn * FW + f) * 1024 + lane * 16);              \
+      if constexpr (DUAL) fa2[SET][f] = *reinterpret_cast<const u32x4*>(st_ + WBYTES + (wn * FW + f) * 1024 + lane * 16); \
+    }                                                                                                    \
+    _Pragma("unroll") for (int q = 0; q < RW; ++q) {                                                     \
+      const int R_ = wm * (BM / 2) + q * 16 + r;                                                         \
+      fb[SET][q] = *reinterpret_cast<const u32x4*>(st_ + XOFF + R_ * 64 + 16 * (g ^ ((R_ >> 1) & 3)));   \
+    }                                                                                                    \
+  }
+#define PE_BIG_ITER(T, CUR, NXT)                                                                         \
+  {                                                                                                      \
+    _Pragma("unroll") for (int f = 0; f < FW; ++f)                                                       \
+      _Pragma("unroll") for (int q = 0; q < RW; ++q) {                                                   \
+        mma16(acc[f][q], fa[CUR][f], fb[CUR][q], uint16_t());                                            \
+        if constexpr (DUAL) mma16(acc2[f][q], fa2[CUR][f], fb[CUR][q], uint16_t());                      \
+      }                                                                                                  \
+    if ((T) + 1 < nsteps) {                                                                              \
+      if ((T) + D - 1 < nsteps) wait_vm<PT * (D - 2)>(); else wait_vm<0>();                              \
+      __syncthreads();                                                                                   \
+      if ((T) + D < nsteps) issue((T) + D);                                                              \
+      PE_BIG_FRAGS((T) + 1, NXT)                                                                         \
+    }                                                                                                    \
+  }
+#pragma unroll
+  for (int t = 0; t < D; ++t)
+    if (t < nsteps) issue(t);
+  if (nsteps >= D) wait_vm<PT * (D - 1)>(); else wait_vm<0>();
+  __syncthreads();
+  PE_BIG_FRAGS(0, 0)
+  for (int t = 0; t < nsteps; t += 2) {
+    PE_BIG_ITER(t, 0, 1)
+    if (t + 1 < nsteps) PE_BIG_ITER(t + 1, 1, 0)
+  }
+#undef PE_BIG_ITER
+#undef PE_BIG_FRAGS
+
+  if constexpr (ARGMAX) {
+    __shared__ float sbv[WN][BM];
+    __shared__ int sbi[WN][BM];
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+      const int mloc = wm * (BM / 2) + q * 16 + r;
+      const int m = m0 + mloc;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int f = 0; f < FW; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * (BN / WN) + f * 16 + 4 * g + j;
+          if (n < N && m < M) {
+            const float v = acc[f][q][j];
+            if (p.epi.logits) p.epi.logits[(int64_t)m * N + n] = v;
+            if (better(v, n, bv, bi)) { bv = v; bi = n; }
+          }
+        }
+      for (int o = 16; o < 64; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (g == 0) { sbv[wn][mloc] = bv; sbi[wn][mloc] = bi; }
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < M) {
+      float bv = sbv[0][tid];
+      int bi = sbi[0][tid];
+      for (int w = 1; w < WN; ++w)
+        if (better(sbv[w][tid], sbi[w][tid], bv, bi)) { bv = sbv[w][tid]; bi = sbi[w][tid]; }
+      p.epi.part_val[(int64_t)ft * M + m0 + tid] = bv;
+      p.epi.part_idx[(int64_t)ft * M + m0 + tid] = bi;
+    }
+  } else {
+#pragma unroll
+    for (int f = 0; f < FW; ++f)
+#pragma unroll
+      for (int q = 0; q < RW; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * (BN / WN) + f * 16 + 4 * g + j;
+          const int m = m0 + wm * (BM / 2) + q * 16 + r;
+          if (n < N && m < M)
+            epi_store<uint16_t>(p.epi, m, n, acc[f][q][j], DUAL ? acc2[DUAL ? f : 0][DUAL ? q : 0][j] : 0.f);
+        }
+  }
+}
+
+template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX>
+static int launch_big(const GemmParams& p, hipStream_t s) {
+  constexpr int STAGE = (BN / 16) * 1024 * (DUAL ? 2 : 1) + BM * 64;
+  static bool attr = false;
+  if (!attr) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, STAGES * STAGE);
+    attr = true;
+  }
+  const int n_ft = (p.N + BN - 1) / BN, n_mt = (p.M + BM - 1) / BM;
+  const int grid = ((n_ft + 7) / 8) * 8 * n_mt;
+  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX>), dim3(grid), dim3(128 * WN), STAGES * STAGE, s, p, n_ft,
+                     n_mt);
+  return n_ft;
+}
+
+int launch_gemm_big(const GemmParams& p, hipStream_t s) {
+  const bool dual = p.epi.kind == EPI_SWIGLU;
+  const bool am = p.epi.kind == EPI_ARGMAX;
+#ifndef PE_BIG_LM
+#define PE_BIG_LM 256, 128, 2, 3
+#endif
+  if (am) return launch_big<PE_BIG_LM, false, true>(p, s);
+  if (dual) return launch_big<256, 128, 4, 4, true, false>(p, s), 0;
+  return launch_big<256, 256, 4, 4, false, false>(p, s), 0;
+}
+
+int gemm_big_partials(int N) { return (N + 63) / 64; }  // the smallest feature tile used (64)
+
+}  // namespace pe

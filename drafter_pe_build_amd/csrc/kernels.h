@@ -106,6 +106,10 @@ void launch_pack(const void* src, void* dst, int N, int row_bytes, hipStream_t s
 int launch_gemm(const GemmParams& p, int bf16, hipStream_t s);
 // Upper bound of P for an argmax GEMM of this shape.
 int gemm_argmax_partials(int M, int N);
+// Large-M bf16 contraction through LDS-staged 256-row tiles (gemm_big.hip);
+// EPI_ARGMAX returns the partial count P = gemm_big_partials(N).
+int launch_gemm_big(const GemmParams& p, hipStream_t s);
+int gemm_big_partials(int N);
 
 void launch_argmax_reduce(const float* pv, const int32_t* pi, int P, int M, int32_t* tokens, hipStream_t s);
 

@@ -143,6 +143,20 @@ def test_small_many_queries(dtype, head_dim):
     check_case("small %s Dh=%d R=9 K=7" % (dtype, head_dim), dims, W, c)
 
 
+def test_many_requests_large_tile_lm_head():
+    # R*K = 140 query rows: the LM head runs on 256-row LDS tiles (a partial
+    # row tile and a partial feature tile), hidden 96 gives an odd number of
+    # 32-wide k steps (a half k-tile at the end)
+    dims = si.DrafterDims(hidden=96, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=160, vocab=1000, dtype="bf16")
+    W = si.drafter_weights(dims, 15, random_gains=True)
+    g = np.random.default_rng(15)
+    R = 20
+    Wn = g.integers(0, 4, R)
+    n_rej = np.array([g.integers(0, w + 1) for w in Wn])
+    c = si.decode_case(dims, 15, R=R, K=7, W=Wn, kv_len=g.integers(0, 100, R), n_rej=n_rej)
+    check_case("LM 256-row tiles R=20 K=7 d=96", dims, W, c)
+
+
 def test_single_draft_slot():
     dims = small_dims("bf16", hq=16, hkv=2)
     W = si.drafter_weights(dims, 13)
