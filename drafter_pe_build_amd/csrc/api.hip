@@ -163,6 +163,8 @@ int zero_ints(size_t max_k_bytes) { return (int)((max_k_bytes + 255) / 256 * 64)
 struct LayerWs {
   void *a, *q, *o, *b, *h, *attn;
   float* x1;
+  float* split;  // K-split partial products of the large-M contractions
+  int64_t split_bytes;
   int* zero;
   int nzero;
   size_t attn_bytes, total;
@@ -190,6 +192,11 @@ LayerWs layer_ws(const pe_drafter_dims* d, int T, int R, int K, int max_pos, voi
   choose_split(R * ((K + QPW - 1) / QPW) * d->n_kv_heads, max_pos, 0, &n_splits, &split_len);
   w.attn_bytes = attn_ws_bytes(RK, d->n_q_heads, d->n_kv_heads, d->head_dim, n_splits);
   w.attn = c.take(w.attn_bytes);
+  int nmax = d->hidden > (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim ? d->hidden
+                                                                         : (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  if (d->ffn > nmax) nmax = d->ffn;
+  w.split_bytes = d->dtype == PE_BF16 ? gemm_split_bytes(T, nmax) : 0;
+  w.split = static_cast<float*>(c.take((size_t)w.split_bytes));
   w.total = c.off;
   return w;
 }
@@ -197,6 +204,8 @@ LayerWs layer_ws(const pe_drafter_dims* d, int T, int R, int K, int max_pos, voi
 // Workspace of the fc fusion.
 struct FuseWs {
   void* u;
+  float* split;  // K-split partial products of a large-M fc
+  int64_t split_bytes;
   int* zero;
   int nzero;
   size_t total;
@@ -208,7 +217,8 @@ FuseWs fuse_ws(const pe_drafter_dims* d, int T, void* base) {
   w.nzero = zero_ints((size_t)3 * d->hidden * esize(d->dtype));
   w.u = c.take((size_t)T * 3 * d->hidden * esize(d->dtype));
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
-
+  w.split_bytes = d->dtype == PE_BF16 ? gemm_split_bytes(T, d->hidden) : 0;
+  w.split = static_cast<float*>(c.take((size_t)w.split_bytes));
   w.total = c.off;
   return w;
 }
@@ -362,6 +372,8 @@ pe_status pe_fuse_hidden(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.nrm.tmp = fw.u;
   gp.clear = fw.zero;
   gp.nclear = fw.nzero;
+  gp.split_ws = fw.split;
+  gp.split_cap = fw.split_bytes;
   gp.epi.kind = EPI_FC;
   gp.epi.out_f32 = x0;
   gp.epi.ld_out = d;
@@ -433,6 +445,8 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.N = qcols + 2 * kvcols;
   gp.K = d;
   gp.xzero = lw.zero;
+  gp.split_ws = lw.split;
+  gp.split_cap = lw.split_bytes;
   gp.nrm.gain = w->attn_gain;
   gp.nrm.segs = 1;
   gp.nrm.seg_len = d;
@@ -484,6 +498,8 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.N = d;
   gp.K = qcols;
   gp.xzero = lw.zero;
+  gp.split_ws = lw.split;
+  gp.split_cap = lw.split_bytes;
   gp.epi.kind = EPI_RESID;
   gp.epi.out_f32 = lw.x1;
   gp.epi.ld_out = d;
@@ -502,6 +518,8 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.N = F;
   gp.K = d;
   gp.xzero = lw.zero;
+  gp.split_ws = lw.split;
+  gp.split_cap = lw.split_bytes;
   gp.nrm.gain = w->mlp_gain;
   gp.nrm.segs = 1;
   gp.nrm.seg_len = d;
@@ -522,6 +540,8 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.N = d;
   gp.K = F;
   gp.xzero = lw.zero;
+  gp.split_ws = lw.split;
+  gp.split_cap = lw.split_bytes;
   gp.epi.kind = EPI_RESID;
   gp.epi.out_f32 = x_out;
   gp.epi.ld_out = d;

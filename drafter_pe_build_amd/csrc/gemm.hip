@@ -1067,8 +1067,12 @@ static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
   // 128-wide tiles only when they still give every CU two workgroups (the
   // N = 2,880 projections get 64 x 64 tiles)
   const bool big = p.M >= 256 && (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) >= 512;
-  // the LM head of a large batch: 256 x 256 tiles through LDS
-  if (am && sizeof(S) == 2 && p.M >= 128 && p.K >= 64) return launch_gemm_big(p, s);
+  // bf16 batches of 128+ rows: the LDS-tiled kernel of gemm_big.hip (the LM
+  // head always, the other contractions when they split K)
+  if (sizeof(S) == 2 && p.M >= 128 && p.K >= 64) {
+    const int r = launch_gemm_big(p, s);
+    if (r >= 0) return r;
+  }
   if (am) return big ? launch_tiled<S, 128, 128, false, true>(p, s) : launch_tiled<S, 64, 64, false, true>(p, s);
   // the gate/up pair keeps 128 x 64 tiles from 256 rows on (two weight streams per tile)
   if (dual) { if (p.M >= 256) launch_tiled<S, 128, 64, true, false>(p, s); else launch_tiled<S, 64, 64, true, false>(p, s); }

@@ -42,7 +42,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Two waves per SIMD: two 4-wave workgroups (or one 8-wave one) per CU.
-template <int BM, int BN, int WN, int D, bool DUAL, bool ARGMAX>
+template <int BM, int BN, int WN, int D, bool DUAL, bool ARGMAX, bool SPLIT>
 __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   constexpr int NW = 2 * WN;           // waves: 2 along the rows x WN along the features
@@ -64,7 +64,10 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   const int ft = (jj / n_mt) * 8 + xcd;
   if (ft >= n_ft) return;
   const int M = p.M, N = p.N, K = p.K;
-  const int nsteps = K / 32;
+  // K split: workgroup (x, y) takes the y-th share of the 32-wide k-steps
+  const int ksteps = K / 32;
+  const int kbeg = SPLIT ? (int)((int64_t)ksteps * blockIdx.y / gridDim.y) : 0;
+  const int nsteps = SPLIT ? (int)((int64_t)ksteps * (blockIdx.y + 1) / gridDim.y) - kbeg : ksteps;
   const int nfb = (N + 15) >> 4;
   const int n0 = ft * BN, m0 = mt * BM;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -78,7 +81,7 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   const char* w2src[DUAL ? WI : 1];
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
-    const int64_t off = (int64_t)min(n0 / 16 + wave + NW * i, nfb - 1) * nsteps * 1024 + lane * 16;
+    const int64_t off = ((int64_t)min(n0 / 16 + wave + NW * i, nfb - 1) * ksteps + kbeg) * 1024 + lane * 16;
     wsrc[i] = reinterpret_cast<const char*>(p.W) + off;
     if constexpr (DUAL) w2src[i] = reinterpret_cast<const char*>(p.W2) + off;
   }
@@ -89,7 +92,7 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   for (int i = 0; i < XI; ++i) {
     const int row = (wave + NW * i) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 1) & 3);
-    xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * p.ldx + c * 8;
+    xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * p.ldx + kbeg * 32 + c * 8;
   }
   auto issue = [&](int t) {
     char* st = lds + (t % D) * STAGE;
@@ -193,6 +196,21 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
       p.epi.part_val[(int64_t)ft * M + m0 + tid] = bv;
       p.epi.part_idx[(int64_t)ft * M + m0 + tid] = bi;
     }
+  } else if constexpr (SPLIT) {
+    // partial tile of split y: [y][m][n] (the second matrix's after all splits)
+    float* part = p.split_ws + (int64_t)blockIdx.y * M * N;
+    float* part2 = p.split_ws + ((int64_t)gridDim.y + blockIdx.y) * M * N;
+#pragma unroll
+    for (int f = 0; f < FW; ++f)
+#pragma unroll
+      for (int q = 0; q < RW; ++q) {
+        const int n = n0 + wn * (BN / WN) + f * 16 + 4 * g;  // N is a multiple of 4 here
+        const int m = m0 + wm * (BM / 2) + q * 16 + r;
+        if (n < N && m < M) {
+          *reinterpret_cast<f32x4*>(part + (int64_t)m * N + n) = acc[f][q];
+          if constexpr (DUAL) *reinterpret_cast<f32x4*>(part2 + (int64_t)m * N + n) = acc2[DUAL ? f : 0][DUAL ? q : 0];
+        }
+      }
   } else {
 #pragma unroll
     for (int f = 0; f < FW; ++f)
@@ -208,33 +226,83 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   }
 }
 
-template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX>
-static int launch_big(const GemmParams& p, hipStream_t s) {
+// Sum of the K-split partial products in split order (deterministic), then
+// the contraction's epilogue; one thread per four features of one row.
+template <bool DUAL>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int splits) {
+  const int M = p.M, N = p.N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * (N / 4)) return;
+  const int m = (int)(i / (N / 4)), n = (int)(i % (N / 4)) * 4;
+  f32x4 y = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) {
+    y += *reinterpret_cast<const f32x4*>(p.split_ws + ((int64_t)s * M + m) * N + n);
+    if constexpr (DUAL) y2 += *reinterpret_cast<const f32x4*>(p.split_ws + ((int64_t)(splits + s) * M + m) * N + n);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) epi_store<uint16_t>(p.epi, m, n + j, y[j], y2[j]);
+}
+
+template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX, bool SPLIT>
+static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
   constexpr int STAGE = (BN / 16) * 1024 * (DUAL ? 2 : 1) + BM * 64;
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX>),
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, STAGES * STAGE);
     attr = true;
   }
   const int n_ft = (p.N + BN - 1) / BN, n_mt = (p.M + BM - 1) / BM;
   const int grid = ((n_ft + 7) / 8) * 8 * n_mt;
-  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX>), dim3(grid), dim3(128 * WN), STAGES * STAGE, s, p, n_ft,
-                     n_mt);
+  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT>), dim3(grid, splits), dim3(128 * WN),
+                     STAGES * STAGE, s, p, n_ft, n_mt);
   return n_ft;
 }
 
-int launch_gemm_big(const GemmParams& p, hipStream_t s) {
-  const bool dual = p.epi.kind == EPI_SWIGLU;
-  const bool am = p.epi.kind == EPI_ARGMAX;
+// Tile shapes: 256 rows x 128 features (four waves, three-stage ring) for
+// single contractions and the LM head (the eight-wave gate/up variant is
+// kept but not dispatched).  Contractions with too few tiles to
+// give every CU two workgroups split K over up to 8 workgroups (at least
+// 16 k-steps each) when the caller's workspace holds the partial products;
+// without a split the function returns -1 and launches nothing.
 #ifndef PE_BIG_LM
 #define PE_BIG_LM 256, 128, 2, 3
 #endif
-  if (am) return launch_big<PE_BIG_LM, false, true>(p, s);
-  if (dual) return launch_big<256, 128, 4, 4, true, false>(p, s), 0;
-  return launch_big<256, 256, 4, 4, false, false>(p, s), 0;
+int launch_gemm_big(const GemmParams& p, hipStream_t s) {
+  const bool dual = p.epi.kind == EPI_SWIGLU;
+  const bool am = p.epi.kind == EPI_ARGMAX;
+  if (am) return launch_big<PE_BIG_LM, false, true, false>(p, 1, s);
+  // the gate/up pair measured faster on the 128 x 64 register-fed tiles
+  // (67.6 us against 76 us split at 448 rows)
+  if (dual) return -1;
+  const int tiles = ((p.N + 127) / 128) * ((p.M + 255) / 256);
+  int splits = 1;
+  if (p.split_ws && p.N % 4 == 0) {
+    const int64_t per = (int64_t)p.M * p.N * 4 * (dual ? 2 : 1);
+    splits = (512 + tiles - 1) / tiles;
+    splits = min(splits, 8);
+    splits = min(splits, (p.K / 32) / 16);
+    while (splits > 1 && (int64_t)splits * per > p.split_cap) --splits;
+    if (splits < 2) splits = 1;
+  }
+  if (splits > 1) {
+    if (dual) launch_big<256, 128, 4, 4, true, false, true>(p, splits, s);
+    else launch_big<256, 128, 2, 3, false, false, true>(p, splits, s);
+    const int64_t n4 = (int64_t)p.M * (p.N / 4);
+    const dim3 grid((unsigned)((n4 + 255) / 256));
+    if (dual) hipLaunchKernelGGL(splitk_reduce_kernel<true>, grid, dim3(256), 0, s, p, splits);
+    else hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, s, p, splits);
+    return 0;
+  }
+  return -1;  // no split: the caller's 128-tile kernel keeps the contraction
 }
 
-int gemm_big_partials(int N) { return (N + 63) / 64; }  // the smallest feature tile used (64)
+int gemm_big_partials(int N) { return (N + 127) / 128; }
+
+int64_t gemm_split_bytes(int T, int nmax) {
+  if (T < 128) return 0;
+  const int64_t full = (int64_t)8 * T * nmax * 4 * 2;  // 8 splits of a gate/up pair
+  return full < ((int64_t)64 << 20) ? full : ((int64_t)64 << 20);
+}
 
 }  // namespace pe

@@ -91,6 +91,8 @@ struct GemmParams {
   NormIn nrm;
   int* clear;  // with a norm: ints zeroed by the launch (the padding-row buffer of later launches), or nullptr
   int nclear;
+  float* split_ws;     // large M: room for K-split partial products, or nullptr (no split)
+  int64_t split_cap;   // its size in bytes
 };
 
 
@@ -106,9 +108,14 @@ void launch_pack(const void* src, void* dst, int N, int row_bytes, hipStream_t s
 int launch_gemm(const GemmParams& p, int bf16, hipStream_t s);
 // Upper bound of P for an argmax GEMM of this shape.
 int gemm_argmax_partials(int M, int N);
-// Large-M bf16 contraction through LDS-staged 256-row tiles (gemm_big.hip);
-// EPI_ARGMAX returns the partial count P = gemm_big_partials(N).
+// Large-M bf16 contraction through LDS-staged 256-row tiles (gemm_big.hip):
+// EPI_ARGMAX returns the partial count P = gemm_big_partials(N); other
+// epilogues return 0 when launched with a K split (p.split_ws), -1 when the
+// shape does not call for one (nothing launched).
 int launch_gemm_big(const GemmParams& p, hipStream_t s);
+// Bytes of K-split workspace worth giving a large-M stage (T rows, widest
+// contraction output nmax).
+int64_t gemm_split_bytes(int T, int nmax);
 int gemm_big_partials(int N);
 
 void launch_argmax_reduce(const float* pv, const int32_t* pi, int P, int M, int32_t* tokens, hipStream_t s);

@@ -157,6 +157,19 @@ def test_many_requests_large_tile_lm_head():
     check_case("LM 256-row tiles R=20 K=7 d=96", dims, W, c)
 
 
+def test_many_requests_split_k():
+    # hidden 1024 with ~170 draft rows: fc, QKV, gate/up and down split K over
+    # several workgroups (partial products reduced in a second kernel)
+    dims = si.DrafterDims(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1024, vocab=1000, dtype="bf16")
+    W = si.drafter_weights(dims, 16, random_gains=True)
+    g = np.random.default_rng(16)
+    R = 20
+    Wn = g.integers(0, 4, R)
+    n_rej = np.array([g.integers(0, w + 1) for w in Wn])
+    c = si.decode_case(dims, 16, R=R, K=7, W=Wn, kv_len=g.integers(0, 200, R), n_rej=n_rej)
+    check_case("split K R=20 K=7 d=1024", dims, W, c)
+
+
 def test_single_draft_slot():
     dims = small_dims("bf16", hq=16, hkv=2)
     W = si.drafter_weights(dims, 13)
