@@ -26,7 +26,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch of the LM-head stage measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE, scaled by a 1 GiB copy (profiles/decode_c1_lm_head_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
-LM_STAGE_TRAFFIC = {"fingerprint": "1bf6dd7a6ac7e33e", "bytes": 1162042534}
+LM_STAGE_TRAFFIC = {"fingerprint": "fe43f26c408ed6ae", "bytes": 1162076182}
 LM_SOURCES = ("gemm.hip", "norm.hip", "common.h", "kernels.h")
 
 
