@@ -170,6 +170,26 @@ def test_many_requests_split_k():
     check_case("split K R=20 K=7 d=1024", dims, W, c)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sixteen_rows_streaming(dtype):
+    # T = R*K = 16: every contraction on the weight-streaming kernels with a
+    # full 16-row operand (no padding rows), norms folded into them
+    dims = small_dims(dtype)
+    W = si.drafter_weights(dims, 17, random_gains=True)
+    c = si.decode_case(dims, 17, R=2, K=8, W=[0, 0], kv_len=[50, 130], n_rej=[0, 0])
+    check_case("16 rows %s" % dtype, dims, W, c)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_few_rows_with_rejections(dtype):
+    # T = 13 rows, two rejected: the fused stream norms + fc (rows staged in
+    # LDS) in both storage types, rejected rows skipped
+    dims = small_dims(dtype)
+    W = si.drafter_weights(dims, 18, random_gains=True)
+    c = si.decode_case(dims, 18, R=2, K=5, W=[2, 1], kv_len=[20, 75], n_rej=[1, 1])
+    check_case("13 rows %s" % dtype, dims, W, c)
+
+
 def test_single_draft_slot():
     dims = small_dims("bf16", hq=16, hkv=2)
     W = si.drafter_weights(dims, 13)
