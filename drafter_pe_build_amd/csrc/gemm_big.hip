@@ -3,14 +3,13 @@
 // for the batched decode shapes (M in the hundreds), finished by the same
 // epilogues as the other contractions (gemm.hip).
 //
-// A workgroup of 8 waves (2 x 4) owns an output tile of BM activation rows x
-// BN features; each wave a (BM/2) x (BN/4) sub-tile accumulated in registers
-// (128 x 64 of a 256 x 256 tile: 128 accumulator registers per lane, two
-// waves per SIMD).  Both operands go through LDS in a ring of four stages,
-// one 32-wide k-step each, copied by global_load_lds_dwordx4 without passing
-// through registers; three k-steps are in flight while one is multiplied
-// (the copies come from HBM for the weights and take one loaded round trip,
-// about the time of three steps of matrix work):
+// A workgroup of 2 x WN waves owns an output tile of BM activation rows x BN
+// features; each wave a (BM/2) x (BN/WN) sub-tile accumulated in registers
+// (112 or 128 rows x 64 features for the 224/256 x 128 tiles with four
+// waves: up to 128 accumulator registers per lane, two waves per SIMD).  Both
+// operands go through LDS in a ring of D stages, one 32-wide k-step each,
+// copied by global_load_lds_dwordx4 without passing through registers; D - 1
+// k-steps are in flight while one is multiplied:
 //  * weights: the packed 1 KB chunks as they are (one chunk = the operand of
 //    one 16-feature x 32-k step, lane l's 16 bytes at 16 l), so a wave reads
 //    its operand with one conflict-free ds_read_b128;
@@ -21,7 +20,7 @@
 // One barrier per k-step.  Workgroup ids map the M tiles of one N tile back
 // to back onto one XCD (workgroup i runs on XCD i % 8), so each weight chunk
 // is fetched from HBM once.  L2->LDS traffic per flop is (BM + BN) / (BM BN)
-// bytes: 1/128 for 256 x 256, half of the 128 x 128 tiles' figure.
+// bytes: 3/256 for 256 x 128, against 1/64 for the 128 x 128 tiles.
 #include <math.h>
 #include "epilogue.h"
 
@@ -53,9 +52,10 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   constexpr int XOFF = WBYTES * (DUAL ? 2 : 1);
   constexpr int STAGE = XOFF + BM * 64;
   constexpr int WI = WB / NW;          // weight copies per wave per k-step (per matrix)
-  constexpr int XI = BM / 16 / NW;     // activation copies per wave per k-step
+  constexpr int XI = (BM / 16 + NW - 1) / NW;  // activation copies per wave per k-step (the
+                                               // last group repeats when NW does not divide BM / 16)
   constexpr int PT = WI * (DUAL ? 2 : 1) + XI;  // vector-memory operations per wave per k-step
-  static_assert(BM % 32 == 0 && BN % 64 == 0 && WB % NW == 0 && (BM / 16) % NW == 0, "tile shape");
+  static_assert(BM % 32 == 0 && BN % 64 == 0 && WB % NW == 0, "tile shape");
   extern __shared__ __attribute__((aligned(16))) char lds[];  // D stages
 
   const int bid = blockIdx.x;
@@ -90,7 +90,7 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   const uint16_t* xsrc[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
-    const int row = (wave + NW * i) * 16 + (lane >> 2);
+    const int row = min(wave + NW * i, BM / 16 - 1) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 1) & 3);
     xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * p.ldx + kbeg * 32 + c * 8;
   }
@@ -102,7 +102,7 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
       if constexpr (DUAL) copy16_to_lds(w2src[i] + (int64_t)t * 1024, st + WBYTES + (wave + NW * i) * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < XI; ++i) copy16_to_lds(xsrc[i] + t * 32, st + XOFF + (wave + NW * i) * 1024);
+    for (int i = 0; i < XI; ++i) copy16_to_lds(xsrc[i] + t * 32, st + XOFF + min(wave + NW * i, BM / 16 - 1) * 1024);
   };
 
   f32x4 acc[FW][RW], acc2[DUAL ? FW : 1][DUAL ? RW : 1];
@@ -259,42 +259,41 @@ static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
   return n_ft;
 }
 
-// Tile shapes: 256 rows x 128 features (four waves, three-stage ring) for
-// single contractions and the LM head (the eight-wave gate/up variant is
-// kept but not dispatched).  Contractions with too few tiles to
-// give every CU two workgroups split K over up to 8 workgroups (at least
-// 16 k-steps each) when the caller's workspace holds the partial products;
-// without a split the function returns -1 and launches nothing.
-#ifndef PE_BIG_LM
-#define PE_BIG_LM 256, 128, 2, 3
-#endif
+// Tile shapes: 256 or 224 rows (whichever pads M less: 448 = 2 x 224,
+// 896 = 4 x 224) x 128 features, four waves and a three-stage ring, for
+// single contractions and the LM head (the eight-wave gate/up variant is kept
+// but not dispatched).  Contractions with too few tiles to give every CU two
+// workgroups split K over up to 8 workgroups (at least 16 k-steps each) when
+// the caller's workspace holds the partial products; without a split the
+// function returns -1 and launches nothing.
 int launch_gemm_big(const GemmParams& p, hipStream_t s) {
   const bool dual = p.epi.kind == EPI_SWIGLU;
   const bool am = p.epi.kind == EPI_ARGMAX;
-  if (am) return launch_big<PE_BIG_LM, false, true, false>(p, 1, s);
+  const bool r224 = ((p.M + 223) / 224) * 224 < ((p.M + 255) / 256) * 256;
+  if (am) {
+    return r224 ? launch_big<224, 128, 2, 3, false, true, false>(p, 1, s)
+                : launch_big<256, 128, 2, 3, false, true, false>(p, 1, s);
+  }
   // the gate/up pair measured faster on the 128 x 64 register-fed tiles
   // (67.6 us against 76 us split at 448 rows)
   if (dual) return -1;
-  const int tiles = ((p.N + 127) / 128) * ((p.M + 255) / 256);
+  const int bm = r224 ? 224 : 256;
+  const int tiles = ((p.N + 127) / 128) * ((p.M + bm - 1) / bm);
   int splits = 1;
   if (p.split_ws && p.N % 4 == 0) {
-    const int64_t per = (int64_t)p.M * p.N * 4 * (dual ? 2 : 1);
+    const int64_t per = (int64_t)p.M * p.N * 4;
     splits = (512 + tiles - 1) / tiles;
     splits = min(splits, 8);
     splits = min(splits, (p.K / 32) / 16);
     while (splits > 1 && (int64_t)splits * per > p.split_cap) --splits;
     if (splits < 2) splits = 1;
   }
-  if (splits > 1) {
-    if (dual) launch_big<256, 128, 4, 4, true, false, true>(p, splits, s);
-    else launch_big<256, 128, 2, 3, false, false, true>(p, splits, s);
-    const int64_t n4 = (int64_t)p.M * (p.N / 4);
-    const dim3 grid((unsigned)((n4 + 255) / 256));
-    if (dual) hipLaunchKernelGGL(splitk_reduce_kernel<true>, grid, dim3(256), 0, s, p, splits);
-    else hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, s, p, splits);
-    return 0;
-  }
-  return -1;  // no split: the caller's 128-tile kernel keeps the contraction
+  if (splits < 2) return -1;  // no split: the caller's 128-tile kernel keeps the contraction
+  if (r224) launch_big<224, 128, 2, 3, false, false, true>(p, splits, s);
+  else launch_big<256, 128, 2, 3, false, false, true>(p, splits, s);
+  const int64_t n4 = (int64_t)p.M * (p.N / 4);
+  hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p, splits);
+  return 0;
 }
 
 int gemm_big_partials(int N) { return (N + 127) / 128; }
