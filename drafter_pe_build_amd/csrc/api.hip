@@ -237,7 +237,7 @@ LmWs lm_ws(const pe_drafter_dims* d, int n, void* base) {
   LmWs w{};
   Carver c(base);
   const size_t P = (size_t)gemm_argmax_partials(n, d->vocab);
-  w.f = c.take((size_t)n * d->hidden * esize(d->dtype));
+  w.f = c.take((size_t)((n + 15) / 16 * 16) * d->hidden * esize(d->dtype));  // rows padded to 16 (operand layout)
   w.pv = static_cast<float*>(c.take(P * n * 4));
   w.pi = static_cast<int32_t*>(c.take(P * n * 4));
   w.nzero = zero_ints((size_t)d->hidden * esize(d->dtype));

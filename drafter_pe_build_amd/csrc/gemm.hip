@@ -978,8 +978,9 @@ static void launch_stream_fnorm(const GemmParams& p, int ks, hipStream_t s) {
 
 // The requested RMSNorm as its own kernel into p.nrm.tmp (also clearing
 // p.clear); returns the parameters of the contraction over the normalised rows.
+// packed: p.nrm.tmp receives the operand layout (rows rounded up to 16).
 template <typename S>
-static GemmParams norm_first(const GemmParams& p, hipStream_t s) {
+static GemmParams norm_first(const GemmParams& p, hipStream_t s, bool packed = false) {
   NormParams np{};
   np.in = p.X;
   np.ld_in = p.ldx;
@@ -993,6 +994,7 @@ static GemmParams norm_first(const GemmParams& p, hipStream_t s) {
   np.ld_out = p.K;
   np.zero = p.clear;
   np.nzero = p.nclear;
+  np.packed = packed;
   const int sbf = sizeof(S) == 2;
   launch_rmsnorm_rows(np, p.nrm.x_f32 ? 0 : sbf, sbf, s);
   GemmParams q = p;
@@ -1001,6 +1003,7 @@ static GemmParams norm_first(const GemmParams& p, hipStream_t s) {
   q.nrm = NormIn{};
   q.clear = nullptr;
   q.nclear = 0;
+  q.x_packed = packed;
   return q;
 }
 
@@ -1063,7 +1066,10 @@ static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
     if (dual) launch_stream<S, true>(p, s); else launch_stream<S, false>(p, s);
     return 0;
   }
-  const GemmParams p = norm ? norm_first<S>(p0, s) : p0;
+  // the LM head of a large batch reads its normalised rows as 1 KB operand
+  // chunks (gemm_big.hip), half the cache lines of 64-byte row pieces
+  const bool big_lm = am && sizeof(S) == 2 && p0.M >= 128 && p0.K >= 64;
+  const GemmParams p = norm ? norm_first<S>(p0, s, big_lm) : p0;
   // 128-wide tiles only when they still give every CU two workgroups (the
   // N = 2,880 projections get 64 x 64 tiles)
   const bool big = p.M >= 256 && (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) >= 512;

@@ -16,7 +16,10 @@
 //  * activations: 64 bytes (32 k) per row, the four 16-byte chunks of row R
 //    stored at position chunk ^ ((R >> 1) & 3), so the rows of one operand
 //    read land in distinct banks.  Rows past M copy row M-1 (their results
-//    are dropped).
+//    are dropped).  Activations already in the operand layout (PX: 1 KB
+//    chunks of 16 rows x 32 k, lane slot 16 c + r = row r, k 8c..8c+7) are
+//    copied chunk by chunk: one copy touches 8 cache lines instead of 16,
+//    which is what bounds the activation traffic of these tiles.
 // One barrier per k-step.  Workgroup ids map the M tiles of one N tile back
 // to back onto one XCD (workgroup i runs on XCD i % 8), so each weight chunk
 // is fetched from HBM once.  L2->LDS traffic per flop is (BM + BN) / (BM BN)
@@ -30,18 +33,11 @@ namespace pe {
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if constexpr (N == 12 + 12) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else static_assert(N == 0, "add this count");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 // Two waves per SIMD: two 4-wave workgroups (or one 8-wave one) per CU.
-template <int BM, int BN, int WN, int D, bool DUAL, bool ARGMAX, bool SPLIT>
+template <int BM, int BN, int WN, int D, bool DUAL, bool ARGMAX, bool SPLIT, bool PX>
 __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   constexpr int NW = 2 * WN;           // waves: 2 along the rows x WN along the features
@@ -90,9 +86,15 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   const uint16_t* xsrc[XI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
-    const int row = min(wave + NW * i, BM / 16 - 1) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
-    xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * p.ldx + kbeg * 32 + c * 8;
+    if constexpr (PX) {
+      // chunk of 16-row group G, k-step t at element (G * ksteps + t) * 512
+      const int grp = min(mt * (BM / 16) + min(wave + NW * i, BM / 16 - 1), (M + 15) / 16 - 1);
+      xsrc[i] = X + ((int64_t)grp * ksteps + kbeg) * 512 + lane * 8;
+    } else {
+      const int row = min(wave + NW * i, BM / 16 - 1) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 1) & 3);
+      xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * p.ldx + kbeg * 32 + c * 8;
+    }
   }
   auto issue = [&](int t) {
     char* st = lds + (t % D) * STAGE;
@@ -102,7 +104,8 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
       if constexpr (DUAL) copy16_to_lds(w2src[i] + (int64_t)t * 1024, st + WBYTES + (wave + NW * i) * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < XI; ++i) copy16_to_lds(xsrc[i] + t * 32, st + XOFF + min(wave + NW * i, BM / 16 - 1) * 1024);
+    for (int i = 0; i < XI; ++i)
+      copy16_to_lds(xsrc[i] + (int64_t)t * (PX ? 512 : 32), st + XOFF + min(wave + NW * i, BM / 16 - 1) * 1024);
   };
 
   f32x4 acc[FW][RW], acc2[DUAL ? FW : 1][DUAL ? RW : 1];
@@ -130,7 +133,8 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
     }                                                                                                    \
     _Pragma("unroll") for (int q = 0; q < RW; ++q) {                                                     \
       const int R_ = wm * (BM / 2) + q * 16 + r;                                                         \
-      fb[SET][q] = *reinterpret_cast<const u32x4*>(st_ + XOFF + R_ * 64 + 16 * (g ^ ((R_ >> 1) & 3)));   \
+      fb[SET][q] = *reinterpret_cast<const u32x4*>(st_ + XOFF + (PX ? (R_ >> 4) * 1024 + lane * 16        \
+                                                                    : R_ * 64 + 16 * (g ^ ((R_ >> 1) & 3)))); \
     }                                                                                                    \
   }
 #define PE_BIG_ITER(T, CUR, NXT)                                                                         \
@@ -243,18 +247,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int sp
   for (int j = 0; j < 4; ++j) epi_store<uint16_t>(p.epi, m, n + j, y[j], y2[j]);
 }
 
-template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX, bool SPLIT>
+template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX, bool SPLIT, bool PX = false>
 static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
   constexpr int STAGE = (BN / 16) * 1024 * (DUAL ? 2 : 1) + BM * 64;
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT>),
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, STAGES * STAGE);
     attr = true;
   }
   const int n_ft = (p.N + BN - 1) / BN, n_mt = (p.M + BM - 1) / BM;
   const int grid = ((n_ft + 7) / 8) * 8 * n_mt;
-  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT>), dim3(grid, splits), dim3(128 * WN),
+  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX>), dim3(grid, splits), dim3(128 * WN),
                      STAGES * STAGE, s, p, n_ft, n_mt);
   return n_ft;
 }
@@ -271,9 +275,13 @@ int launch_gemm_big(const GemmParams& p, hipStream_t s) {
   const bool am = p.epi.kind == EPI_ARGMAX;
   const bool r224 = ((p.M + 223) / 224) * 224 < ((p.M + 255) / 256) * 256;
   if (am) {
+    if (p.x_packed)
+      return r224 ? launch_big<224, 128, 2, 3, false, true, false, true>(p, 1, s)
+                  : launch_big<256, 128, 2, 3, false, true, false, true>(p, 1, s);
     return r224 ? launch_big<224, 128, 2, 3, false, true, false>(p, 1, s)
                 : launch_big<256, 128, 2, 3, false, true, false>(p, 1, s);
   }
+  if (p.x_packed) return -1;  // packed rows only feed the argmax tiles
   // the gate/up pair measured faster on the 128 x 64 register-fed tiles
   // (67.6 us against 76 us split at 448 rows)
   if (dual) return -1;

@@ -28,6 +28,12 @@ struct NormParams {
   int64_t ld_out;
   int* zero;             // counters cleared by the launch (block 0), or nullptr
   int nzero;
+  // bf16 output only: 0 = rows of ld_out elements; 1 = the matrix-core operand
+  // layout of the large-M contractions (ld_out = K, a multiple of 32): the
+  // 16-row x 32-column piece (G, S) is the 1 KB chunk G * (K / 32) + S, whose
+  // 16-byte lane slot 16 c + r holds row 16 G + r, columns 32 S + 8 c .. + 7.
+  // Rows n .. n_pad - 1 (n_pad = n rounded up to 16) are written as zeros.
+  int packed;
 };
 // Row count limit of one segment: 8 x 256 sixteen-byte chunks per row.
 constexpr int kNormMaxChunks = 8;
@@ -93,6 +99,7 @@ struct GemmParams {
   int nclear;
   float* split_ws;     // large M: room for K-split partial products, or nullptr (no split)
   int64_t split_cap;   // its size in bytes
+  int x_packed;        // X in the operand layout of NormParams::packed (large-M argmax only)
 };
 
 

@@ -6,7 +6,8 @@
 // One workgroup per (row, segment).  Every 16-byte chunk of the row segment is
 // loaded into registers up front (at most kNormMaxChunks per thread), so the
 // kernel costs one memory round trip, one workgroup reduction and one store.
-// Rows flagged in `skip` are written as zeros.  Block (0, 0) also clears the
+// Rows flagged in `skip` are written as zeros; bf16 output can also go to
+// the matrix-core operand layout of the large-M contractions (`packed`).  Block (0, 0) also clears the
 // split-K tile counters of the contraction that consumes this output.
 #include "kernels.h"
 
@@ -18,11 +19,19 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(NormParams p) {
   const int i = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x;
   if (p.zero && i == 0 && seg == 0)
     for (int j = tid; j < p.nzero; j += 256) p.zero[j] = 0;
-  const int row = p.rows ? p.rows[i] : i;
-  const bool skip = p.skip && p.skip[row];
+  const bool pad = i >= p.n;  // padding rows of the packed layout
+  const int row = pad ? 0 : (p.rows ? p.rows[i] : i);
+  const bool skip = pad || (p.skip && p.skip[row]);
   const char* x = reinterpret_cast<const char*>(p.in) + ((int64_t)row * p.ld_in + (int64_t)seg * p.d) * sizeof(Sin);
   const float* gain = p.gain + (int64_t)seg * p.d;
   Sout* out = reinterpret_cast<Sout*>(p.out) + (int64_t)i * p.ld_out + (int64_t)seg * p.d;
+  // element k of this row segment (k a multiple of 4 here)
+  auto dst = [&](int k) -> Sout* {
+    if (!p.packed) return out + k;
+    const int col = seg * p.d + k;
+    const int64_t chunk = (int64_t)(i >> 4) * (p.ld_out >> 5) + (col >> 5);
+    return reinterpret_cast<Sout*>(p.out) + chunk * 512 + (((col >> 3) & 3) * 16 + (i & 15)) * 8 + (col & 7);
+  };
   const int nch = p.d / CI;
   float v[kNormMaxChunks][CI];
   float ss = 0.f;
@@ -57,10 +66,10 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(NormParams p) {
     if constexpr (sizeof(Sout) == 2) {
       if constexpr (CI == 8) {
         u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
-        *reinterpret_cast<u32x4*>(out + e0) = w;
+        *reinterpret_cast<u32x4*>(dst(e0)) = w;
       } else {
         u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-        *reinterpret_cast<u32x2*>(out + e0) = w;
+        *reinterpret_cast<u32x2*>(dst(e0)) = w;
       }
     } else {
 #pragma unroll
@@ -73,7 +82,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(NormParams p) {
 }
 
 void launch_rmsnorm_rows(const NormParams& p, int in_bf16, int out_bf16, hipStream_t s) {
-  dim3 grid(p.n, p.segs);
+  dim3 grid(p.packed ? (p.n + 15) / 16 * 16 : p.n, p.segs);
   if (in_bf16 && out_bf16) hipLaunchKernelGGL((rmsnorm_rows_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s, p);
   else if (!in_bf16 && out_bf16) hipLaunchKernelGGL((rmsnorm_rows_kernel<float, uint16_t>), grid, dim3(256), 0, s, p);
   else if (in_bf16 && !out_bf16) hipLaunchKernelGGL((rmsnorm_rows_kernel<uint16_t, float>), grid, dim3(256), 0, s, p);

@@ -144,9 +144,9 @@ def test_small_many_queries(dtype, head_dim):
 
 
 def test_many_requests_large_tile_lm_head():
-    # R*K = 140 query rows: the LM head runs on 256-row LDS tiles (a partial
-    # row tile and a partial feature tile), hidden 96 gives an odd number of
-    # 32-wide k steps (a half k-tile at the end)
+    # R*K = 140 query rows: the LM head runs on one 224-row LDS tile (a partial
+    # row tile and a partial feature tile), hidden 96 gives three 32-wide
+    # k-steps, as many as the copy ring has stages
     dims = si.DrafterDims(hidden=96, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=160, vocab=1000, dtype="bf16")
     W = si.drafter_weights(dims, 15, random_gains=True)
     g = np.random.default_rng(15)
@@ -155,6 +155,20 @@ def test_many_requests_large_tile_lm_head():
     n_rej = np.array([g.integers(0, w + 1) for w in Wn])
     c = si.decode_case(dims, 15, R=R, K=7, W=Wn, kv_len=g.integers(0, 100, R), n_rej=n_rej)
     check_case("LM 256-row tiles R=20 K=7 d=96", dims, W, c)
+
+
+def test_many_requests_two_row_tiles():
+    # R*K = 301 query rows: the LM head reads its normalised rows in the 1 KB
+    # operand layout over two 224-row tiles; the second tile ends inside a
+    # 16-row group (zero padding rows) and clamps the groups past it
+    dims = small_dims("bf16")
+    W = si.drafter_weights(dims, 19, random_gains=True)
+    g = np.random.default_rng(19)
+    R = 43
+    Wn = g.integers(0, 4, R)
+    n_rej = np.array([g.integers(0, w + 1) for w in Wn])
+    c = si.decode_case(dims, 19, R=R, K=7, W=Wn, kv_len=g.integers(0, 150, R), n_rej=n_rej)
+    check_case("LM two row tiles R=43 K=7", dims, W, c)
 
 
 def test_many_requests_split_k():
