@@ -179,7 +179,7 @@ LayerWs layer_ws(const pe_drafter_dims* d, int T, int R, int K, int max_pos, voi
   int kmax = d->hidden > qc ? d->hidden : qc;
   if (d->ffn > kmax) kmax = d->ffn;
   w.nzero = zero_ints((size_t)kmax * e);
-  w.a = c.take((size_t)T * d->hidden * e);
+  w.a = c.take((size_t)((T + 15) / 16 * 16) * d->hidden * e);  // rows padded to 16 (operand layout)
   w.q = c.take((size_t)T * qc * e);
   w.o = c.take((size_t)RK * qc * e);
   w.x1 = static_cast<float*>(c.take((size_t)RK * d->hidden * 4));
@@ -215,7 +215,7 @@ FuseWs fuse_ws(const pe_drafter_dims* d, int T, void* base) {
   FuseWs w{};
   Carver c(base);
   w.nzero = zero_ints((size_t)3 * d->hidden * esize(d->dtype));
-  w.u = c.take((size_t)T * 3 * d->hidden * esize(d->dtype));
+  w.u = c.take((size_t)((T + 15) / 16 * 16) * 3 * d->hidden * esize(d->dtype));  // rows padded to 16
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
   w.split_bytes = d->dtype == PE_BF16 ? gemm_split_bytes(T, d->hidden) : 0;
   w.split = static_cast<float*>(c.take((size_t)w.split_bytes));

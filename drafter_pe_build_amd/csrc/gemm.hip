@@ -1066,10 +1066,11 @@ static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
     if (dual) launch_stream<S, true>(p, s); else launch_stream<S, false>(p, s);
     return 0;
   }
-  // the LM head of a large batch reads its normalised rows as 1 KB operand
-  // chunks (gemm_big.hip), half the cache lines of 64-byte row pieces
-  const bool big_lm = am && sizeof(S) == 2 && p0.M >= 128 && p0.K >= 64;
-  const GemmParams p = norm ? norm_first<S>(p0, s, big_lm) : p0;
+  // rows normalised for the LDS-tiled kernel of gemm_big.hip go to its 1 KB
+  // operand chunks (half the cache lines of 64-byte row pieces)
+  const bool to_big = sizeof(S) == 2 && p0.M >= 128 && p0.K >= 64 && norm &&
+                      norm_packable(p0.nrm.seg_len, !p0.nrm.x_f32) && (am || gemm_big_splits(p0) > 0);
+  const GemmParams p = norm ? norm_first<S>(p0, s, to_big) : p0;
   // 128-wide tiles only when they still give every CU two workgroups (the
   // N = 2,880 projections get 64 x 64 tiles)
   const bool big = p.M >= 256 && (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) >= 512;

@@ -137,19 +137,31 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
                                                                     : R_ * 64 + 16 * (g ^ ((R_ >> 1) & 3)))); \
     }                                                                                                    \
   }
+#ifndef PE_BIG_SCHED
+#define PE_BIG_SCHED
+#endif
+#ifndef PE_BIG_SPLIT
+#define PE_BIG_SPLIT 0
+#endif
+  // FH: weight blocks whose products run before the barrier (the rest hide the
+  // operand reads of the next step)
+  constexpr int FH = PE_BIG_SPLIT ? FW / 2 : FW;
+#define PE_BIG_MMA(CUR, F0, F1)                                                                          \
+  _Pragma("unroll") for (int f = F0; f < F1; ++f)                                                        \
+    _Pragma("unroll") for (int q = 0; q < RW; ++q) {                                                     \
+      mma16(acc[f][q], fa[CUR][f], fb[CUR][q], uint16_t());                                              \
+      if constexpr (DUAL) mma16(acc2[f][q], fa2[CUR][f], fb[CUR][q], uint16_t());                        \
+    }
 #define PE_BIG_ITER(T, CUR, NXT)                                                                         \
   {                                                                                                      \
-    _Pragma("unroll") for (int f = 0; f < FW; ++f)                                                       \
-      _Pragma("unroll") for (int q = 0; q < RW; ++q) {                                                   \
-        mma16(acc[f][q], fa[CUR][f], fb[CUR][q], uint16_t());                                            \
-        if constexpr (DUAL) mma16(acc2[f][q], fa2[CUR][f], fb[CUR][q], uint16_t());                      \
-      }                                                                                                  \
+    PE_BIG_MMA(CUR, 0, FH)                                                                               \
     if ((T) + 1 < nsteps) {                                                                              \
       if ((T) + D - 1 < nsteps) wait_vm<PT * (D - 2)>(); else wait_vm<0>();                              \
       __syncthreads();                                                                                   \
       if ((T) + D < nsteps) issue((T) + D);                                                              \
       PE_BIG_FRAGS((T) + 1, NXT)                                                                         \
     }                                                                                                    \
+    if constexpr (FH < FW) { PE_BIG_SCHED PE_BIG_MMA(CUR, FH, FW) }                                      \
   }
 #pragma unroll
   for (int t = 0; t < D; ++t)
@@ -162,6 +174,7 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
     if (t + 1 < nsteps) PE_BIG_ITER(t + 1, 1, 0)
   }
 #undef PE_BIG_ITER
+#undef PE_BIG_MMA
 #undef PE_BIG_FRAGS
 
   if constexpr (ARGMAX) {
@@ -268,37 +281,59 @@ static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
 // single contractions and the LM head (the eight-wave gate/up variant is kept
 // but not dispatched).  Contractions with too few tiles to give every CU two
 // workgroups split K over up to 8 workgroups (at least 16 k-steps each) when
-// the caller's workspace holds the partial products; without a split the
-// function returns -1 and launches nothing.
+// the caller's workspace holds the partial products (gemm_big_splits); without
+// a split launch_gemm_big returns -1 and launches nothing.
+static bool rows224(int M) { return ((M + 223) / 224) * 224 < ((M + 255) / 256) * 256; }
+
+// K-split policy: enough workgroups for PE_SPLIT_SLOTS resident tiles, at
+// most PE_SPLIT_MAX shares of at least PE_SPLIT_MINSTEPS k-steps each, and a
+// PE_SPLIT_STAGES-deep copy ring.
+#ifndef PE_SPLIT_SLOTS
+#define PE_SPLIT_SLOTS 512
+#endif
+#ifndef PE_SPLIT_MAX
+#define PE_SPLIT_MAX 8
+#endif
+#ifndef PE_SPLIT_MINSTEPS
+#define PE_SPLIT_MINSTEPS 16
+#endif
+#ifndef PE_SPLIT_STAGES
+#define PE_SPLIT_STAGES 3
+#endif
+
+int gemm_big_splits(const GemmParams& p) {
+  // the gate/up pair measured faster on the 128 x 64 register-fed tiles
+  // (67.6 us against 76 us split at 448 rows)
+  if (p.epi.kind == EPI_SWIGLU || p.epi.kind == EPI_ARGMAX) return 0;
+  if (!p.split_ws || p.N % 4) return 0;
+  const int bm = rows224(p.M) ? 224 : 256;
+  const int tiles = ((p.N + 127) / 128) * ((p.M + bm - 1) / bm);
+  const int64_t per = (int64_t)p.M * p.N * 4;
+  int splits = (PE_SPLIT_SLOTS + tiles - 1) / tiles;
+  splits = min(splits, PE_SPLIT_MAX);
+  splits = min(splits, (p.K / 32) / PE_SPLIT_MINSTEPS);
+  while (splits > 1 && (int64_t)splits * per > p.split_cap) --splits;
+  return splits >= 2 ? splits : 0;
+}
+
 int launch_gemm_big(const GemmParams& p, hipStream_t s) {
-  const bool dual = p.epi.kind == EPI_SWIGLU;
-  const bool am = p.epi.kind == EPI_ARGMAX;
-  const bool r224 = ((p.M + 223) / 224) * 224 < ((p.M + 255) / 256) * 256;
-  if (am) {
+  const bool r224 = rows224(p.M);
+  if (p.epi.kind == EPI_ARGMAX) {
     if (p.x_packed)
       return r224 ? launch_big<224, 128, 2, 3, false, true, false, true>(p, 1, s)
                   : launch_big<256, 128, 2, 3, false, true, false, true>(p, 1, s);
     return r224 ? launch_big<224, 128, 2, 3, false, true, false>(p, 1, s)
                 : launch_big<256, 128, 2, 3, false, true, false>(p, 1, s);
   }
-  if (p.x_packed) return -1;  // packed rows only feed the argmax tiles
-  // the gate/up pair measured faster on the 128 x 64 register-fed tiles
-  // (67.6 us against 76 us split at 448 rows)
-  if (dual) return -1;
-  const int bm = r224 ? 224 : 256;
-  const int tiles = ((p.N + 127) / 128) * ((p.M + bm - 1) / bm);
-  int splits = 1;
-  if (p.split_ws && p.N % 4 == 0) {
-    const int64_t per = (int64_t)p.M * p.N * 4;
-    splits = (512 + tiles - 1) / tiles;
-    splits = min(splits, 8);
-    splits = min(splits, (p.K / 32) / 16);
-    while (splits > 1 && (int64_t)splits * per > p.split_cap) --splits;
-    if (splits < 2) splits = 1;
+  const int splits = gemm_big_splits(p);
+  if (!splits) return -1;  // the caller's 128-tile kernel keeps the contraction
+  if (p.x_packed) {
+    if (r224) launch_big<224, 128, 2, PE_SPLIT_STAGES, false, false, true, true>(p, splits, s);
+    else launch_big<256, 128, 2, PE_SPLIT_STAGES, false, false, true, true>(p, splits, s);
+  } else {
+    if (r224) launch_big<224, 128, 2, PE_SPLIT_STAGES, false, false, true>(p, splits, s);
+    else launch_big<256, 128, 2, PE_SPLIT_STAGES, false, false, true>(p, splits, s);
   }
-  if (splits < 2) return -1;  // no split: the caller's 128-tile kernel keeps the contraction
-  if (r224) launch_big<224, 128, 2, 3, false, false, true>(p, splits, s);
-  else launch_big<256, 128, 2, 3, false, false, true>(p, splits, s);
   const int64_t n4 = (int64_t)p.M * (p.N / 4);
   hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p, splits);
   return 0;

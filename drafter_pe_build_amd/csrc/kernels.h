@@ -37,7 +37,11 @@ struct NormParams {
 };
 // Row count limit of one segment: 8 x 256 sixteen-byte chunks per row.
 constexpr int kNormMaxChunks = 8;
+// Packed output: a wave per row, at most this many 16-byte chunks per lane.
+constexpr int kPackedMaxChunks = 12;
 void launch_rmsnorm_rows(const NormParams& p, int in_bf16, int out_bf16, hipStream_t s);
+// Whether launch_rmsnorm_rows can write a row segment of d elements packed.
+bool norm_packable(int d, int in_bf16);
 
 // GEMM epilogues.  The product Y[m][n] = sum_k X[m][k] W[n][k] of output row m
 // (an X row) and feature n (a W row) is finished by one of these.
@@ -120,6 +124,9 @@ int gemm_argmax_partials(int M, int N);
 // epilogues return 0 when launched with a K split (p.split_ws), -1 when the
 // shape does not call for one (nothing launched).
 int launch_gemm_big(const GemmParams& p, hipStream_t s);
+// K-split count launch_gemm_big uses for a non-argmax contraction; 0 = it
+// launches nothing for this shape.
+int gemm_big_splits(const GemmParams& p);
 // Bytes of K-split workspace worth giving a large-M stage (T rows, widest
 // contraction output nmax).
 int64_t gemm_split_bytes(int T, int nmax);
