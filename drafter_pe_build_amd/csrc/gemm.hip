@@ -539,8 +539,11 @@ void gemm_stream_lds_kernel(GemmParams p) {
 // argmax_reduce_kernel.
 // Two workgroups per CU (four waves per SIMD, at most 128 registers per lane)
 // keep enough weight loads in flight.
+#ifndef PE_LM_WPE
+#define PE_LM_WPE 4
+#endif
 template <typename S, int NFB, int KS, int U, bool XL, bool NORM>
-__global__ __launch_bounds__(64 * NFB * KS) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(64 * NFB * KS) __attribute__((amdgpu_waves_per_eu(PE_LM_WPE)))
 void lm_argmax_stream_kernel(GemmParams p) {
   constexpr int CH = Storage<S>::CH;
   constexpr int STEP = 4 * CH;
@@ -849,13 +852,13 @@ static constexpr int kStreamU = 8;     // 1 KB steps in flight per wave
 #define PE_LM_NFB 4
 #endif
 #ifndef PE_LM_KS
-#define PE_LM_KS 2
+#define PE_LM_KS 3
 #endif
 #ifndef PE_LM_GRID
 #define PE_LM_GRID 1024
 #endif
 #ifndef PE_LM_U
-#define PE_LM_U 8
+#define PE_LM_U 5
 #endif
 static constexpr int kLmNFB = PE_LM_NFB, kLmKS = PE_LM_KS, kLmGrid = PE_LM_GRID, kLmU = PE_LM_U;
 // Largest activation block the LM-head kernel stages in LDS (its own arrays
