@@ -46,8 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the c=64 decode and attention measurements")
-    ap.add_argument("--attention-only", type=int, choices=(3, 4), default=0,
-                    help="time only the COD (3) or parallel-group (4) attention workload and print its line")
+    ap.add_argument("--attention-only", type=int, choices=(3, 4, 5), default=0,
+                    help="time only the COD (3), parallel-group (4) or random-anchor (5) attention workload "
+                         "and print its line")
     ap.add_argument("--decode64-only", action="store_true",
                     help="time only the c=64 decode step and print its line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -114,7 +115,7 @@ def decode_bytes(dims, case, T, RK):
     return weights + kv + hidden + emb + act, weights
 
 
-ATTN_NAMES = {3: "cod_attention_n4096", 4: "group_attention_n8192_chunked"}
+ATTN_NAMES = {3: "cod_attention_n4096", 4: "group_attention_n8192_chunked", 5: "anchor_attention_n8192"}
 
 
 def measure_attention(cfg, steps, stream):
@@ -158,6 +159,42 @@ def measure_attention(cfg, steps, stream):
     return {"T": T, "ms": msa, "positions_per_s": T / (msa * 1e-3), "visible_pairs": pairs,
             "tflops": fl / (msa * 1e-3) / 1e12, "mfma_frac": fl / (msa * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "launches": len(chunks)}
+
+
+def measure_anchor(steps, stream):
+    """Random-anchor (max_anchors) attention at 8K: 1024 anchors' rows query
+    every original position plus the anchors' chain rows; one launch."""
+    import numpy as np
+    import torch
+    from drafter_pe_build_amd import _lib as L
+    from drafter_pe_build_amd.step import to_device
+    from synth import inputs as si
+    log("random-anchor attention N=8192")
+    A = si.anchor_config()
+    qr = A["q_rows"]
+    nq, T = A["num_q"], A["T"]
+    Hq, Hkv, Dh = A["heads"]
+    q, k, v = (to_device(A[n], "cuda") for n in ("q", "k", "v"))
+    q_start = to_device(A["start"][qr].astype(np.int32), "cuda")
+    q_depth = to_device(A["depth"][qr].astype(np.int32), "cuda")
+    q_self = to_device(qr.astype(np.int32), "cuda")
+    parent = to_device(A["parent"].astype(np.int32), "cuda")
+    base = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((nq, Hq, Dh), dtype=torch.bfloat16, device="cuda")
+    a = L.attn_args(num_q=nq, num_seg=1, q_per_seg=nq, num_kv_rows=T, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=Dh,
+                    scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16, q=q, q_row_stride=Hq * Dh, k=k, v=v,
+                    seg_kv_base=base, q_start=q_start, q_depth=q_depth, q_self_row=q_self, kv_parent=parent,
+                    max_prefix=A["N"], out=out)
+    ws = torch.empty(max(L.pe_draft_attention_workspace(a), 256), dtype=torch.uint8, device="cuda")
+    msa = time_sustained(lambda: L.pe_draft_attention(a, "cuda", workspace=ws), steps, stream)
+    pairs = int(np.sum(A["start"][qr].astype(np.int64) + 1 + A["depth"][qr]))
+    fl = pairs * Hq * 4 * Dh
+    log("  %.1f us, %.0f TFLOP/s" % (msa * 1e3, fl / (msa * 1e-3) / 1e12))
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return {"queries": nq, "key_rows": T, "anchors": int(len(A["anchors"])), "ms": msa,
+            "queries_per_s": nq / (msa * 1e-3), "visible_pairs": pairs, "tflops": fl / (msa * 1e-3) / 1e12,
+            "mfma_frac": fl / (msa * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "launches": 1}
 
 
 def measure_decode64(dims, W, steps, stream):
@@ -204,7 +241,10 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     if args.attention_only:
-        r = measure_attention(args.attention_only, args.steps, stream)
+        if args.attention_only == 5:
+            r = measure_anchor(args.steps, stream)
+        else:
+            r = measure_attention(args.attention_only, args.steps, stream)
         print(json.dumps({"metric": ATTN_NAMES[args.attention_only], "value": r["tflops"], "unit": "TFLOP/s",
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
         return
@@ -289,6 +329,7 @@ def main():
         extra["decode_c64"] = measure_decode64(dims, W, max(5, args.steps // 5), stream)
         for cfg, name in ((3, "cod_attention_n4096"), (4, "group_attention_n8192_chunked")):
             extra[name] = measure_attention(cfg, max(5, args.steps // 5), stream)
+        extra["anchor_attention_n8192"] = measure_anchor(max(5, args.steps // 5), stream)
         result["secondary"] = extra
 
     if not args.no_cpu:

@@ -54,16 +54,20 @@ pe_status check_dims(const pe_drafter_dims* d) {
 pe_status launched() { return hipGetLastError() == hipSuccess ? PE_OK : PE_ERR_DEVICE; }
 
 // Split of the prefix range so that a decode-shaped launch still fills the chip
-// (two attention workgroups share a CU: 512 run at once).  A launch of 1024
-// or more workgroups is not split: there the unnormalised partials would only
-// add HBM traffic and a combine pass.
+// (two attention workgroups share a CU: 512 run at once).  A launch of 512
+// or more workgroups is not split: it already occupies every slot, and the
+// unnormalised partials would only add HBM traffic and a combine pass (the
+// 64-request decode step's attention: 139 -> 107 us unsplit).
+#ifndef PE_ATTN_NOSPLIT_GROUPS
+#define PE_ATTN_NOSPLIT_GROUPS 512
+#endif
 void choose_split(int base_groups, int max_prefix, int split_req, int* n_splits, int* split_len) {
   const int mp = max_prefix > 1 ? max_prefix : 1;
   int sl;
   if (split_req > 0) {
     sl = up64(split_req);
   } else {
-    int want = base_groups >= 1024 ? 1 : (2048 + base_groups - 1) / base_groups;
+    int want = base_groups >= PE_ATTN_NOSPLIT_GROUPS ? 1 : (2048 + base_groups - 1) / base_groups;
     const int maxs = (mp + 63) / 64;
     if (want > maxs) want = maxs;
     if (want > 64) want = 64;

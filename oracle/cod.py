@@ -6,6 +6,9 @@ position, then the token after that for a kept fraction of those chains
 the layout therefore holds N * sum_{n<D} p^n positions.  [RFC] "Random
 Anchor Subsampling": depth 0 is always the full sequence.  [RFC] "Proposed
 Change": only loss-mask=1 positions start chains at depth >= 1.
+[RFC] "Proposed Change" (max_anchors): chains start only from a random
+subset of the loss-mask=1 positions and only those anchors' rows are
+queries, against every original position plus the anchors' deeper rows.
 [PD] "Training on long sequences": with N positions and K parallel groups
 there are N*K positions (N=8192, K=8 gives 65,536 and an attention matrix of
 more than 4e9 elements), which the sequence partition splits into contiguous
@@ -43,6 +46,41 @@ def cod_rows(loss_mask, U, keep, n_depths):
     return rows
 
 
+def anchor_rows(loss_mask, anchors, U, keep, n_depths):
+    """Row labels and query rows of a random-anchor COD sample.
+
+    [RFC] "Proposed Change": at most max_anchors chain starts, drawn from the
+    loss-mask=1 positions, instead of every position; the keys/values are the
+    whole original sequence plus the anchors' deeper rows, the queries only
+    the anchors' rows (anchors x sum_{n<D} p^n queries against
+    N + anchors x sum_{1<=n<D} p^n keys).  Anchor a reaches depth e >= 1 when
+    its first e keep draws U[a, 0..e-1] are all below ``keep``.
+
+    Returns (rows, queries): rows = (start, depth) labels in depth-major
+    order, every original position at depth 0 first (row index = position);
+    queries = the row indices of the anchors' depth-0 rows and of every chain
+    row, in row order.  Written as plain loops.
+    """
+    N = len(loss_mask)
+    chosen = sorted(int(a) for a in anchors)
+    for a in chosen:
+        if not loss_mask[a]:
+            raise ValueError("anchor %d is not a loss-mask position" % a)
+    rows = [(i, 0) for i in range(N)]
+    queries = list(chosen)
+    for e in range(1, n_depths):
+        for a in chosen:
+            ok = True
+            for t in range(e):
+                if not (U[a][t] < keep):
+                    ok = False
+                    break
+            if ok:
+                queries.append(len(rows))
+                rows.append((a, e))
+    return rows, queries
+
+
 def visible(start_q, depth_q, start_k, depth_k):
     """The parallel-draft / COD mask predicate (vectorised over keys)."""
     start_k = np.asarray(start_k)
@@ -52,28 +90,30 @@ def visible(start_q, depth_q, start_k, depth_k):
     return prefix | chain
 
 
-def attention(q, k, v, start, depth, queries=None, scale=None):
+def attention(q, k, v, start, depth, queries=None, scale=None, q_by_query=False):
     """o = softmax(q k^T * scale) v over the visible keys of each query, per head.
 
     q [T,Hq,Dh], k/v [T,Hkv,Dh] float64 (any row order); start/depth [T].
     Query head h reads kv head h // (Hq/Hkv).  Returns (out [nq,Hq,Dh],
     lse [nq,Hq]) for the rows listed in ``queries`` (all rows by default),
-    lse being the natural-log log-sum-exp of the scaled scores.
+    lse being the natural-log log-sum-exp of the scaled scores.  With
+    ``q_by_query`` q holds one row per listed query ([nq,Hq,Dh], the
+    random-anchor case where only the sampled rows are queries).
     """
-    T, Hq, Dh = q.shape
+    _, Hq, Dh = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(Dh)
     if queries is None:
-        queries = np.arange(T)
+        queries = np.arange(len(start))
     out = np.zeros((len(queries), Hq, Dh))
     lse = np.zeros((len(queries), Hq))
     for n, t in enumerate(queries):
         keys = np.nonzero(visible(start[t], depth[t], start, depth))[0]
         Ks = k[keys]
         Vs = v[keys]
-        qh = q[t].reshape(Hkv, G, Dh)
+        qh = (q[n] if q_by_query else q[t]).reshape(Hkv, G, Dh)
         s = np.einsum("hgd,khd->hgk", qh, Ks) * scale
         m = s.max(axis=-1, keepdims=True)
         p = np.exp(s - m)

@@ -256,6 +256,27 @@ def decode_config(cfg: int, with_weights: bool = True) -> tuple:
     return dims, weights, case
 
 
+def _depth_major(N: int, starters: np.ndarray, U: np.ndarray, keep: float, n_depths: int) -> dict:
+    """Depth-major layout: group 0 = positions 0..N-1, group e = the starters
+    whose first e draws U[i, 0..e-1] are below ``keep``, sorted by start;
+    ``parent`` links each row of depth >= 2 to its (start, depth-1) row."""
+    starts = [np.arange(N, dtype=np.int64)]
+    alive = starters.copy()
+    for e in range(1, n_depths):
+        alive = alive & (U[:, e - 1] < keep)
+        starts.append(np.nonzero(alive)[0].astype(np.int64))
+    group_off = np.zeros(n_depths + 1, dtype=np.int64)
+    group_off[1:] = np.cumsum([len(s) for s in starts])
+    T = int(group_off[-1])
+    start = np.concatenate(starts).astype(np.int32)
+    depth = np.concatenate([np.full(len(s), e, dtype=np.int32) for e, s in enumerate(starts)])
+    parent = np.full(T, -1, dtype=np.int32)
+    for e in range(2, n_depths):
+        pos = np.searchsorted(starts[e - 1], starts[e])
+        parent[group_off[e]:group_off[e + 1]] = (group_off[e - 1] + pos).astype(np.int32)
+    return dict(start=start, depth=depth, parent=parent, group_off=group_off.astype(np.int32), T=T)
+
+
 def cod_case(N: int, n_depths: int, keep: float, loss_rate: float, seed: int,
              heads=COD_HEADS, dtype: str = "bf16", draw_qkv: bool = True) -> dict:
     """Training-shaped COD attention input in depth-major layout.
@@ -271,30 +292,59 @@ def cod_case(N: int, n_depths: int, keep: float, loss_rate: float, seed: int,
     Hq, Hkv, Dh = heads
     loss_mask = rng(seed, 30).random(N) < loss_rate
     U = rng(seed, 31).random((N, max(n_depths - 1, 0)))
-    starts = [np.arange(N, dtype=np.int64)]
-    alive = loss_mask.copy()
-    for e in range(1, n_depths):
-        alive = alive & (U[:, e - 1] < keep)
-        starts.append(np.nonzero(alive)[0].astype(np.int64))
-    group_off = np.zeros(n_depths + 1, dtype=np.int64)
-    group_off[1:] = np.cumsum([len(s) for s in starts])
-    T = int(group_off[-1])
-    start = np.concatenate(starts).astype(np.int32)
-    depth = np.concatenate([np.full(len(s), e, dtype=np.int32) for e, s in enumerate(starts)])
-    parent = np.full(T, -1, dtype=np.int32)
-    for e in range(2, n_depths):
-        prev = starts[e - 1]
-        cur = starts[e]
-        pos = np.searchsorted(prev, cur)
-        parent[group_off[e]:group_off[e + 1]] = (group_off[e - 1] + pos).astype(np.int32)
-    out = dict(N=N, n_depths=n_depths, keep=keep, loss_mask=loss_mask, U=U,
-               start=start, depth=depth, parent=parent,
-               group_off=group_off.astype(np.int32), T=T, heads=heads, dtype=dtype)
+    out = dict(N=N, n_depths=n_depths, keep=keep, loss_mask=loss_mask, U=U, heads=heads, dtype=dtype)
+    out.update(_depth_major(N, loss_mask, U, keep, n_depths))
+    T = out["T"]
     if draw_qkv:
         out["q"] = to_storage(_normal(seed, 32, (T, Hq, Dh), 1.0), dtype)
         out["k"] = to_storage(_normal(seed, 33, (T, Hkv, Dh), 1.0), dtype)
         out["v"] = to_storage(_normal(seed, 34, (T, Hkv, Dh), 1.0), dtype)
     return out
+
+
+def anchor_case(N: int, n_depths: int, keep: float, loss_rate: float, max_anchors: int, seed: int,
+                heads=COD_HEADS, dtype: str = "bf16", draw_qkv: bool = True) -> dict:
+    """Random-anchor COD attention input (the max_anchors variant).
+
+    Draws: ``loss_mask = U[0,1) < loss_rate`` (tag 40); min(max_anchors,
+    #loss-mask positions) anchors chosen uniformly without replacement among
+    the loss-mask positions (tag 41); keep draws ``U`` [N, n_depths-1] (tag
+    42).  Only anchors start chains.  Keys/values: the depth-major layout of
+    all N positions plus the anchors' chain rows ([T, Hkv, Dh], tags 44-45);
+    queries: the anchors' depth-0 rows, then every chain row, in row order
+    (``q_rows``), with Q [num_q, Hq, Dh] in that order (tag 43).  All values
+    N(0,1).
+    """
+    Hq, Hkv, Dh = heads
+    loss_mask = rng(seed, 40).random(N) < loss_rate
+    elig = np.nonzero(loss_mask)[0]
+    na = min(max_anchors, len(elig))
+    anchors = np.sort(rng(seed, 41).choice(elig, size=na, replace=False)).astype(np.int64)
+    U = rng(seed, 42).random((N, max(n_depths - 1, 0)))
+    starters = np.zeros(N, dtype=bool)
+    starters[anchors] = True
+    out = dict(N=N, n_depths=n_depths, keep=keep, loss_mask=loss_mask, U=U, anchors=anchors,
+               heads=heads, dtype=dtype)
+    out.update(_depth_major(N, starters, U, keep, n_depths))
+    T = out["T"]
+    q_rows = np.concatenate([anchors, np.arange(N, T)]).astype(np.int32)
+    out["q_rows"] = q_rows
+    out["num_q"] = len(q_rows)
+    if draw_qkv:
+        out["q"] = to_storage(_normal(seed, 43, (len(q_rows), Hq, Dh), 1.0), dtype)
+        out["k"] = to_storage(_normal(seed, 44, (T, Hkv, Dh), 1.0), dtype)
+        out["v"] = to_storage(_normal(seed, 45, (T, Hkv, Dh), 1.0), dtype)
+    return out
+
+
+# The pages' long-context setting for random anchors: 8K positions, 1024
+# anchors, keep (down-sample ratio) 0.5, 8 depths; loss-mask rate 0.5 as in
+# the N=4096 COD case.
+ANCHOR_8K = dict(N=8192, n_depths=8, keep=0.5, loss_rate=0.5, max_anchors=1024, seed=5)
+
+
+def anchor_config(draw_qkv: bool = True) -> dict:
+    return anchor_case(draw_qkv=draw_qkv, **ANCHOR_8K)
 
 
 def cod_config(cfg: int, draw_qkv: bool = True) -> dict:

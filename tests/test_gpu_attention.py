@@ -9,6 +9,9 @@
   values on a sample of queries (every depth's first and last rows).
 * Decode-shaped segments with ragged lengths through the split-KV path,
   plus empty queries and num_q = 0.
+* Random anchors (max_anchors): the sampled query subset against every key
+  row, small layouts in full (unsplit and split) and the 8K setting on a
+  sample of queries, index stats of every query.
 """
 import numpy as np
 import pytest
@@ -140,6 +143,93 @@ def test_cod_training_shape_n4096():
         np.testing.assert_array_equal(gc[:, j], rc)
         np.testing.assert_array_equal(gh[:, j], rh)
     assert int(rc.sum()) == int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
+
+
+def upload_anchor(A):
+    qr = A["q_rows"]
+    return dict(q=to_device(A["q"], "cuda"), k=to_device(A["k"], "cuda"), v=to_device(A["v"], "cuda"),
+                q_start=to_device(A["start"][qr].astype(np.int32), "cuda"),
+                q_depth=to_device(A["depth"][qr].astype(np.int32), "cuda"),
+                q_self=to_device(qr.astype(np.int32), "cuda"),
+                parent=to_device(A["parent"].astype(np.int32), "cuda"),
+                base=torch.zeros(1, dtype=torch.int32, device="cuda"), dtype=A["dtype"])
+
+
+def run_anchor(D, A, dbg=True, split_len=0):
+    """Random-anchor attention: the num_q sampled rows query all T key rows."""
+    nq, T = A["num_q"], A["T"]
+    Hq, Hkv, Dh = A["heads"]
+    sdt = torch.bfloat16 if D["dtype"] == "bf16" else torch.float32
+    out = torch.empty((nq, Hq, Dh), dtype=sdt, device="cuda")
+    lse = torch.empty((nq, Hq), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros((nq, Hkv), dtype=torch.int64, device="cuda") if dbg else None
+    hsh = torch.zeros((nq, Hkv), dtype=torch.int64, device="cuda") if dbg else None
+    a = L.attn_args(num_q=nq, num_seg=1, q_per_seg=nq, num_kv_rows=T, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=Dh,
+                    scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16 if D["dtype"] == "bf16" else L.PE_F32,
+                    q=D["q"], q_row_stride=Hq * Dh, k=D["k"], v=D["v"], seg_kv_base=D["base"],
+                    q_start=D["q_start"], q_depth=D["q_depth"], q_self_row=D["q_self"], kv_parent=D["parent"],
+                    max_prefix=A["N"], split_len=split_len, out=out, lse=lse, dbg_count=cnt, dbg_hash=hsh)
+    L.pe_draft_attention(a, "cuda")
+    return out, lse, cnt, hsh
+
+
+def check_anchor(A, out, lse, cnt, hsh, sel, name):
+    """sel: indices into the query list compared by value; index stats of every query."""
+    dt = A["dtype"]
+    tol = TOL[dt]
+    qr = A["q_rows"]
+    q64 = od.to_f64(A["q"][sel], dt)
+    ref_o, ref_l = oc.attention(q64, od.to_f64(A["k"], dt), od.to_f64(A["v"], dt), A["start"], A["depth"],
+                                qr[sel], q_by_query=True)
+    e = om.relerr(dev_to_f64(out)[sel], ref_o)
+    el = om.relerr(lse.cpu().numpy()[sel], ref_l)
+    say("  [%s] out relerr %.3g  lse relerr %.3g  (%d of %d queries)" % (name, e, el, len(sel), len(qr)))
+    assert e <= tol and el <= tol
+    if cnt is not None:
+        rc, rh = oc.index_stats(A["start"], A["depth"], qr)
+        gc = cnt.cpu().numpy()
+        gh = hsh.cpu().numpy().view(np.uint64)
+        for j in range(gc.shape[1]):
+            np.testing.assert_array_equal(gc[:, j], rc)
+            np.testing.assert_array_equal(gh[:, j], rh)
+
+
+@pytest.mark.parametrize("dtype,heads,N,D,keep,anchors", [
+    ("bf16", (8, 2, 128), 300, 5, 0.7, 40),
+    ("bf16", (32, 8, 128), 520, 8, 0.5, 130),
+    ("f32", (8, 2, 64), 260, 4, 0.9, 60),
+    ("bf16", (16, 4, 64), 200, 3, 1.0, 500),   # more anchors than loss-mask positions: all of them
+])
+def test_anchor_small_layouts(dtype, heads, N, D, keep, anchors):
+    A = si.anchor_case(N, D, keep, 0.5, anchors, 23, heads=heads, dtype=dtype)
+    name = "anchors %s N=%d D=%d heads=%s queries=%d keys=%d" % (dtype, N, D, heads, A["num_q"], A["T"])
+    say(name)
+    Dv = upload_anchor(A)
+    out, lse, cnt, hsh = run_anchor(Dv, A)
+    torch.cuda.synchronize()
+    check_anchor(A, out, lse, cnt, hsh, np.arange(A["num_q"]), name)
+    # a fixed split of the prefix range (several splits and the combine) agrees too
+    out1, lse1, _, _ = run_anchor(Dv, A, dbg=False, split_len=64)
+    torch.cuda.synchronize()
+    check_anchor(A, out1, lse1, None, None, np.arange(A["num_q"]), name + " split 64")
+
+
+def test_anchor_long_sequence_n8192():
+    A = si.anchor_config()
+    say("random anchors N=8192: %d anchors, %d queries, %d key rows" % (len(A["anchors"]), A["num_q"], A["T"]))
+    Dv = upload_anchor(A)
+    out, lse, cnt, hsh = run_anchor(Dv, A)
+    torch.cuda.synchronize()
+    # the query set's visible pairs through the kernel's own counters
+    qr = A["q_rows"]
+    pairs = int(np.sum(A["start"][qr].astype(np.int64) + 1 + A["depth"][qr]))
+    assert int(cnt[:, 0].sum().item()) == pairs
+    first = np.searchsorted(qr, A["group_off"][:-1])   # first query of each depth group
+    sel = set()
+    for i in first.tolist() + [A["num_q"] - 1]:
+        sel.update(range(max(0, i - 2), min(A["num_q"], i + 3)))
+    sel.update(np.random.default_rng(2).choice(A["num_q"], 24, replace=False).tolist())
+    check_anchor(A, out, lse, cnt, hsh, np.array(sorted(sel)), "anchors N=8192 sampled")
 
 
 def test_long_sequence_chunked_n8192():

@@ -12,6 +12,10 @@
   1.0; the mean of T over seeds against N * sum_{n<D} p^n; the page's
   rounded 2.73 against the exact 2.7731; (N*K)^2 > 4e9 at N=8192, K=8.
 * Q = 0 gives the mean of the visible V rows.
+* Random anchors: a hand-worked layout with its key sets; the generator
+  against the oracle's loop-built rows and parent chains; anchors on every
+  loss-mask position reduce to the symmetric COD rows; the query and key
+  counts against the page's (anchors x 2.73) x (anchors x 1.73 + N).
 """
 import itertools
 
@@ -208,3 +212,89 @@ def test_mix64_reference_values():
     # SplitMix64 seeded with 0 yields these first outputs (states gamma, 2*gamma, ...)
     outs = oc.mix64(np.arange(3, dtype=np.uint64) * oc.GOLDEN_GAMMA)
     assert [hex(int(x)) for x in outs] == ["0xe220a8397b1dcdaf", "0x6e789e6aa1b965f4", "0x6c45d188009454f"]
+
+
+# ---- random anchors (max_anchors): a query subset against the full sequence
+
+def test_anchor_rows_hand_example():
+    # N = 8, loss mask at 1, 2, 4, 6; anchors 2 and 6; keep 0.5, 3 depths.
+    # Anchor 2 draws (0.3, 0.4): depths 1 and 2; anchor 6 draws (0.2, 0.9):
+    # depth 1 only.  Non-anchor rows draw 0 (they would survive if they
+    # started chains, which they must not).
+    loss = np.zeros(8, bool)
+    loss[[1, 2, 4, 6]] = True
+    U = np.zeros((8, 2))
+    U[2] = (0.3, 0.4)
+    U[6] = (0.2, 0.9)
+    rows, queries = oc.anchor_rows(loss, [6, 2], U, 0.5, 3)
+    assert rows == [(i, 0) for i in range(8)] + [(2, 1), (6, 1), (2, 2)]
+    assert queries == [2, 6, 8, 9, 10]
+    start = np.array([r[0] for r in rows])
+    depth = np.array([r[1] for r in rows])
+    keys = [set(np.nonzero(oc.visible(start[t], depth[t], start, depth))[0].tolist()) for t in queries]
+    assert keys == [{0, 1, 2}, set(range(7)), {0, 1, 2, 8}, set(range(7)) | {9}, {0, 1, 2, 8, 10}]
+    with pytest.raises(ValueError):
+        oc.anchor_rows(loss, [3], U, 0.5, 3)   # 3 is not a loss-mask position
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_anchor_generator_matches_oracle_rows(seed):
+    A = si.anchor_case(60, 5, 0.7, 0.5, 9, seed, heads=(4, 2, 8), dtype="f32")
+    assert len(A["anchors"]) == 9 and all(A["loss_mask"][A["anchors"]])
+    rows, queries = oc.anchor_rows(A["loss_mask"], A["anchors"], A["U"], 0.7, 5)
+    assert list(zip(A["start"].tolist(), A["depth"].tolist())) == rows
+    assert A["q_rows"].tolist() == queries
+    # parent links walk each chain row back to depth 1 through its own start
+    for t in range(A["N"], A["T"]):
+        r, d = t, int(A["depth"][t])
+        while d > 1:
+            r = int(A["parent"][r])
+            d -= 1
+            assert (int(A["start"][r]), int(A["depth"][r])) == (int(A["start"][t]), d)
+        assert int(A["parent"][r]) == -1
+
+
+def test_anchors_on_every_loss_position_reduce_to_cod_rows():
+    # with every loss-mask position an anchor, the key rows are the COD layout
+    # of the symmetric case, and the queries are its chain rows plus the anchors
+    A = _layout(50, 4, 0.7, 0.5, 3)
+    anchors = np.nonzero(A["loss_mask"])[0]
+    rows, queries = oc.anchor_rows(A["loss_mask"], anchors, A["U"], 0.7, 4)
+    assert rows == oc.cod_rows(A["loss_mask"], A["U"], 0.7, 4)
+    assert queries == sorted(anchors.tolist()) + list(range(50, len(rows)))
+
+
+def test_anchor_shape_formula():
+    # [RFC] "Proposed Change": (anchors x 2.73) queries against
+    # (anchors x 1.73 + sequence length) keys at keep 0.7 and 4 speculative tokens
+    p, D = 0.7, 5
+    q_mult = sum(p ** n for n in range(D))
+    k_mult = sum(p ** n for n in range(1, D))
+    assert abs(q_mult - 2.7731) < 1e-12 and abs(k_mult - 1.7731) < 1e-12
+    assert abs(q_mult - 2.73) / q_mult < 0.016 and abs(k_mult - 1.73) / k_mult < 0.025
+    N, A = 2048, 256
+    EL = k_mult
+    var = sum((2 * e - 1) * p ** e for e in range(1, D)) - EL ** 2   # chain length variance
+    nq = [si.anchor_case(N, D, p, 0.5, A, 2000 + s, draw_qkv=False)["num_q"] for s in range(100)]
+    nk = [si.anchor_case(N, D, p, 0.5, A, 2000 + s, draw_qkv=False)["T"] for s in range(100)]
+    tol = 4 * np.sqrt(A * var) / np.sqrt(100)
+    assert abs(np.mean(nq) - A * q_mult) < tol
+    assert abs(np.mean(nk) - (A * k_mult + N)) < tol
+    # the 8K setting: 1024 anchors at keep 0.5 over 8 depths
+    c = si.anchor_config(draw_qkv=False)
+    assert c["N"] == 8192 and len(c["anchors"]) == 1024
+    EL8 = sum(0.5 ** n for n in range(1, 8))
+    var8 = sum((2 * e - 1) * 0.5 ** e for e in range(1, 8)) - EL8 ** 2
+    assert abs(c["num_q"] - 1024 * (1 + EL8)) < 4 * np.sqrt(1024 * var8)
+
+
+def test_query_ordered_q_matches_row_ordered_q():
+    A = si.anchor_case(40, 4, 0.8, 0.6, 7, 11, heads=(4, 2, 8), dtype="f32", draw_qkv=False)
+    T, qr = A["T"], A["q_rows"]
+    g = np.random.default_rng(5)
+    qfull = g.standard_normal((T, 4, 8))
+    k = g.standard_normal((T, 2, 8))
+    v = g.standard_normal((T, 2, 8))
+    a, la = oc.attention(qfull, k, v, A["start"], A["depth"], qr)
+    b, lb = oc.attention(qfull[qr], k, v, A["start"], A["depth"], qr, q_by_query=True)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
