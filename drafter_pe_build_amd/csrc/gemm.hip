@@ -555,16 +555,27 @@ void lm_argmax_stream_kernel(GemmParams p) {
   const int r = lane & 15, g = lane >> 4;
   const int M = p.M, N = p.N, K = p.K;
   const int nsteps = K / STEP;
-  const int s0 = nsteps * ks / KS, s1 = nsteps * (ks + 1) / KS;
+#ifndef PE_LM_INTERLEAVE
+#define PE_LM_INTERLEAVE 0
+#endif
+  // k-steps of this wave: a contiguous share, or (interleaved) every KS-th
+  // step from ks, so that a block's waves read one contiguous run together
+  const int s0 = PE_LM_INTERLEAVE ? ks : nsteps * ks / KS;
+  const int sst = PE_LM_INTERLEAVE ? KS : 1;
+  const int cnt = PE_LM_INTERLEAVE ? (nsteps - ks + KS - 1) / KS : nsteps * (ks + 1) / KS - s0;
   const int nfb = (N + 15) >> 4;
   const int ntiles = (nfb + NFB - 1) / NFB;
   const bool xr = r < M;
-  const int nb = (s1 - s0 + U - 1) / U;  // batches per wave
+  const int nb = (cnt + U - 1) / U;  // batches per wave
+  // padding slots of a batch re-read the wave's last step (step 0 for a wave
+  // without steps, which K smaller than KS k-steps leaves), never a chunk
+  // outside the block
+  const int slast = cnt > 0 ? s0 + (cnt - 1) * sst : 0;
   const char* W = reinterpret_cast<const char*>(p.W) + lane * 16;
   u32x4 wv[2][U];
   auto wload = [&](const char* wb, int j, int slot) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) wv[slot][u] = ld16(wb + (int64_t)min(s0 + j * U + u, s1 - 1) * 1024);
+    for (int u = 0; u < U; ++u) wv[slot][u] = ld16(wb + (int64_t)(j * U + u < cnt ? s0 + (j * U + u) * sst : slast) * 1024);
   };
   // the first tile's first weight batch is requested right after the
   // activation reads, so the staging hides under its round trip (not with a
@@ -603,8 +614,8 @@ void lm_argmax_stream_kernel(GemmParams p) {
       auto batch = [&](int j, int slot) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int su = s0 + j * U + u;
-          if (su < s1) mma16(acc, wv[slot][u], ld16(xrow + (int64_t)su * xstep), S());
+          const int su = s0 + (j * U + u) * sst;
+          if (j * U + u < cnt) mma16(acc, wv[slot][u], ld16(xrow + (int64_t)su * xstep), S());
         }
       };
       if (!pre || tile != (int)blockIdx.x) wload(wb, 0, 0);  // else the first tile's went out before the staging

@@ -204,6 +204,17 @@ def test_few_rows_with_rejections(dtype):
     check_case("13 rows %s" % dtype, dims, W, c)
 
 
+@pytest.mark.parametrize("dtype,hidden", [("bf16", 32), ("f32", 16)])
+def test_hidden_of_one_k_step(dtype, hidden):
+    # hidden = one 32-wide (bf16) or 16-wide (f32) k-step: the LM head's K
+    # split gives some waves no step at all (their padding loads must stay
+    # inside the weight block)
+    dims = si.DrafterDims(hidden=hidden, n_q_heads=2, n_kv_heads=1, head_dim=64, ffn=64, vocab=500, dtype=dtype)
+    W = si.drafter_weights(dims, 24, random_gains=True)
+    c = si.decode_case(dims, 24, R=2, K=4, W=[3, 1], kv_len=[30, 8], n_rej=[1, 0])
+    check_case("hidden %d %s" % (hidden, dtype), dims, W, c)
+
+
 def test_single_draft_slot():
     dims = small_dims("bf16", hq=16, hkv=2)
     W = si.drafter_weights(dims, 13)
