@@ -81,16 +81,24 @@ def anchor_rows(loss_mask, anchors, U, keep, n_depths):
     return rows, queries
 
 
-def visible(start_q, depth_q, start_k, depth_k):
-    """The parallel-draft / COD mask predicate (vectorised over keys)."""
+def visible(start_q, depth_q, start_k, depth_k, sink=0, window=0):
+    """The parallel-draft / COD mask predicate (vectorised over keys).
+
+    With ``window`` > 0 (the StreamingLLM variant, [RFC] "Separate Ablation:
+    StreamingLLM"), a depth-0 key j <= start_q stays visible only when it is
+    one of the first ``sink`` positions or one of the ``window`` most recent
+    (start_q - j < window); chain keys are unchanged.
+    """
     start_k = np.asarray(start_k)
     depth_k = np.asarray(depth_k)
     prefix = (depth_k == 0) & (start_k <= start_q)
+    if window > 0:
+        prefix = prefix & ((start_k < sink) | (start_q - start_k < window))
     chain = (start_k == start_q) & (depth_k >= 1) & (depth_k <= depth_q)
     return prefix | chain
 
 
-def attention(q, k, v, start, depth, queries=None, scale=None, q_by_query=False):
+def attention(q, k, v, start, depth, queries=None, scale=None, q_by_query=False, sink=0, window=0):
     """o = softmax(q k^T * scale) v over the visible keys of each query, per head.
 
     q [T,Hq,Dh], k/v [T,Hkv,Dh] float64 (any row order); start/depth [T].
@@ -98,7 +106,8 @@ def attention(q, k, v, start, depth, queries=None, scale=None, q_by_query=False)
     lse [nq,Hq]) for the rows listed in ``queries`` (all rows by default),
     lse being the natural-log log-sum-exp of the scaled scores.  With
     ``q_by_query`` q holds one row per listed query ([nq,Hq,Dh], the
-    random-anchor case where only the sampled rows are queries).
+    random-anchor case where only the sampled rows are queries).  ``sink``
+    and ``window`` select the StreamingLLM predicate of visible().
     """
     _, Hq, Dh = q.shape
     Hkv = k.shape[1]
@@ -110,7 +119,7 @@ def attention(q, k, v, start, depth, queries=None, scale=None, q_by_query=False)
     out = np.zeros((len(queries), Hq, Dh))
     lse = np.zeros((len(queries), Hq))
     for n, t in enumerate(queries):
-        keys = np.nonzero(visible(start[t], depth[t], start, depth))[0]
+        keys = np.nonzero(visible(start[t], depth[t], start, depth, sink, window))[0]
         Ks = k[keys]
         Vs = v[keys]
         qh = (q[n] if q_by_query else q[t]).reshape(Hkv, G, Dh)
@@ -148,7 +157,7 @@ def mix64(x):
     return z ^ (z >> np.uint64(31))
 
 
-def index_stats(start, depth, queries=None, row_offset=0):
+def index_stats(start, depth, queries=None, row_offset=0, sink=0, window=0):
     """Per query: number of visible keys, and the sum mod 2^64 of mix64(key row).
 
     ``row_offset`` is added to every key row before hashing (the kv row
@@ -161,7 +170,7 @@ def index_stats(start, depth, queries=None, row_offset=0):
     hsh = np.zeros(len(queries), np.uint64)
     with np.errstate(over="ignore"):
         for n, t in enumerate(queries):
-            keys = np.nonzero(visible(start[t], depth[t], start, depth))[0]
+            keys = np.nonzero(visible(start[t], depth[t], start, depth, sink, window))[0]
             cnt[n] = len(keys)
             hsh[n] = np.sum(mix64(keys.astype(np.uint64) + np.uint64(row_offset)), dtype=np.uint64)
     return cnt, hsh

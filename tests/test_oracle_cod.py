@@ -16,6 +16,9 @@
   against the oracle's loop-built rows and parent chains; anchors on every
   loss-mask position reduce to the symmetric COD rows; the query and key
   counts against the page's (anchors x 2.73) x (anchors x 1.73 + N).
+* StreamingLLM window: a hand-worked example, the per-query count in closed
+  form, reduction to the plain predicate when the window spans the
+  sequence, one depth against SDPA with a banded-plus-sink mask.
 """
 import itertools
 
@@ -298,3 +301,46 @@ def test_query_ordered_q_matches_row_ordered_q():
     a, la = oc.attention(qfull, k, v, A["start"], A["depth"], qr)
     b, lb = oc.attention(qfull[qr], k, v, A["start"], A["depth"], qr, q_by_query=True)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+# ---- StreamingLLM window (sink + recent window over the depth-0 keys)
+
+def test_window_hand_example():
+    # N = 10, chains of start 7 to depth 2: rows 0..9 at depth 0, (7,1) = row 10, (7,2) = row 11
+    start = np.array(list(range(10)) + [7, 7])
+    depth = np.array([0] * 10 + [1, 2])
+    keys = lambda t: set(np.nonzero(oc.visible(start[t], depth[t], start, depth, sink=2, window=3))[0].tolist())
+    assert keys(7) == {0, 1, 5, 6, 7}
+    assert keys(11) == {0, 1, 5, 6, 7, 10, 11}
+    assert keys(3) == {0, 1, 2, 3}            # the window reaches back into the sink
+    assert keys(0) == {0}
+
+
+def test_window_count_closed_form_and_reduction():
+    L = _layout(300, 5, 0.7, 0.5, 12)
+    for sink, window in ((4, 16), (0, 1), (32, 64), (1, 300)):
+        cnt, _ = oc.index_stats(L["start"], L["depth"], sink=sink, window=window)
+        i = L["start"].astype(np.int64)
+        lo = np.maximum(sink, i - window + 1)
+        closed = np.minimum(sink, i + 1) + np.maximum(0, i - lo + 1) + L["depth"]
+        np.testing.assert_array_equal(cnt, closed)
+    # a window covering the whole sequence is the unwindowed predicate
+    full, fh = oc.index_stats(L["start"], L["depth"])
+    wide, wh = oc.index_stats(L["start"], L["depth"], sink=0, window=300)
+    assert np.array_equal(full, wide) and np.array_equal(fh, wh)
+
+
+def test_window_single_depth_is_banded_sdpa():
+    g = np.random.default_rng(6)
+    N, Hq, Hkv, Dh, sink, window = 45, 4, 2, 16, 3, 7
+    q = g.standard_normal((N, Hq, Dh))
+    k = g.standard_normal((N, Hkv, Dh))
+    v = g.standard_normal((N, Hkv, Dh))
+    out, _ = oc.attention(q, k, v, np.arange(N), np.zeros(N, int), sink=sink, window=window)
+    ones = torch.ones(N, N, dtype=torch.bool)
+    col = torch.arange(N)[None, :].expand(N, N)
+    mask = torch.tril(ones) & (torch.triu(ones, diagonal=-(window - 1)) | (col < sink))
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2)[None], torch.from_numpy(k).permute(1, 0, 2)[None],
+        torch.from_numpy(v).permute(1, 0, 2)[None], attn_mask=mask[None, None], enable_gqa=True)
+    np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
