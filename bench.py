@@ -46,9 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the c=64 decode and attention measurements")
-    ap.add_argument("--attention-only", type=int, choices=(3, 4, 5), default=0,
-                    help="time only the COD (3), parallel-group (4) or random-anchor (5) attention workload "
-                         "and print its line")
+    ap.add_argument("--attention-only", type=int, choices=(3, 4, 5, 6), default=0,
+                    help="time only the COD (3), parallel-group (4), random-anchor (5) or windowed "
+                         "parallel-group (6) attention workload and print its line")
     ap.add_argument("--decode64-only", action="store_true",
                     help="time only the c=64 decode step and print its line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -115,19 +115,24 @@ def decode_bytes(dims, case, T, RK):
     return weights + kv + hidden + emb + act, weights
 
 
-ATTN_NAMES = {3: "cod_attention_n4096", 4: "group_attention_n8192_chunked", 5: "anchor_attention_n8192"}
+ATTN_NAMES = {3: "cod_attention_n4096", 4: "group_attention_n8192_chunked", 5: "anchor_attention_n8192",
+              6: "window_attention_n8192_chunked"}
+# StreamingLLM setting of the pages' 8K ablation: sink 256, window 2048
+WINDOW_SINK, WINDOW_LEN = 256, 2048
 
 
 def measure_attention(cfg, steps, stream):
     """COD attention N=4096 (one launch) or parallel-group attention N=8192
-    (8 query chunks of 8192): time per pass over all queries and rate."""
+    (8 query chunks of 8192; cfg 6: with the StreamingLLM window): time per
+    pass over all queries and rate."""
     import numpy as np
     import torch
     from drafter_pe_build_amd import _lib as L
     from drafter_pe_build_amd.step import to_device
     from synth import inputs as si
     log("attention config %d" % cfg)
-    Lay = si.cod_config(cfg)
+    Lay = si.cod_config(4 if cfg == 6 else cfg)
+    sink, window = (WINDOW_SINK, WINDOW_LEN) if cfg == 6 else (0, 0)
     T = Lay["T"]
     Hq, Hkv, Dh = Lay["heads"]
     q, k, v = (to_device(Lay[n], "cuda") for n in ("q", "k", "v"))
@@ -142,7 +147,8 @@ def measure_attention(cfg, steps, stream):
                            n_kv_heads=Hkv, head_dim=Dh, scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16,
                            q=q[c0:c1], q_row_stride=Hq * Dh, k=k, v=v, seg_kv_base=base,
                            q_start=start[c0:c1], q_depth=depth[c0:c1], q_self_row=selfr[c0:c1],
-                           kv_parent=parent, max_prefix=Lay["N"], out=out[c0:c1]) for c0, c1 in chunks]
+                           kv_parent=parent, max_prefix=Lay["N"], out=out[c0:c1], window_sink=sink,
+                           window_len=window) for c0, c1 in chunks]
     wsb = max(L.pe_draft_attention_workspace(a) for a in arglist)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
 
@@ -151,7 +157,12 @@ def measure_attention(cfg, steps, stream):
             L.pe_draft_attention(a, "cuda", workspace=ws)
 
     msa = time_sustained(run_attn, steps, stream)
-    pairs = int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
+    i = Lay["start"].astype(np.int64)
+    if window:   # visible depth-0 keys: the sink plus the window, per query
+        pairs = int(np.sum(np.minimum(sink, i + 1) + np.maximum(0, i - np.maximum(sink, i - window + 1) + 1)
+                           + Lay["depth"]))
+    else:
+        pairs = int(np.sum(i + 1 + Lay["depth"]))
     fl = pairs * Hq * 4 * Dh
     log("  %.1f us, %.0f TFLOP/s" % (msa * 1e3, fl / (msa * 1e-3) / 1e12))
     del q, k, v, out
@@ -330,6 +341,7 @@ def main():
         for cfg, name in ((3, "cod_attention_n4096"), (4, "group_attention_n8192_chunked")):
             extra[name] = measure_attention(cfg, max(5, args.steps // 5), stream)
         extra["anchor_attention_n8192"] = measure_anchor(max(5, args.steps // 5), stream)
+        extra["window_attention_n8192_chunked"] = measure_attention(6, max(5, args.steps // 5), stream)
         result["secondary"] = extra
 
     if not args.no_cpu:

@@ -89,6 +89,8 @@ pe_status check_attn(const pe_attn_args* a) {
   if (a->head_dim != 64 && a->head_dim != 128) return PE_ERR_UNSUPPORTED;
   if (!(a->scale > 0.f) || !isfinite(a->scale)) return PE_ERR_INVALID_ARG;
   if (a->split_len < 0 || a->max_prefix < 0) return PE_ERR_INVALID_ARG;
+  if (a->window_sink < 0 || a->window_len < 0) return PE_ERR_INVALID_ARG;
+  if (a->window_len > 0 && a->split_len > 0) return PE_ERR_UNSUPPORTED;  // a window is never split
   if (a->num_q == 0) return PE_OK;
   if (!a->q || !a->k || !a->v || !a->seg_kv_base || !a->q_start || !a->out) return PE_ERR_INVALID_ARG;
   if (a->q_depth && (!a->q_self_row || !a->kv_parent)) return PE_ERR_INVALID_ARG;
@@ -113,6 +115,10 @@ void attn_split_for(const pe_attn_args* a, int* n_splits, int* split_len) {
   int base = a->num_seg * tps * a->n_kv_heads;
   if (base < 1) base = 1;
   choose_split(base, a->max_prefix, a->split_len, n_splits, split_len);
+  if (a->window_len > 0) {  // the window kernel walks two tile ranges of one unsplit prefix
+    *n_splits = 1;
+    *split_len = up64(a->max_prefix > 1 ? a->max_prefix : 1);
+  }
 }
 
 pe_status run_attention(const pe_attn_args* a, void* ws, size_t ws_bytes, int meta_by_row, hipStream_t s) {
@@ -142,6 +148,8 @@ pe_status run_attention(const pe_attn_args* a, void* ws, size_t ws_bytes, int me
   p.kv_parent = a->kv_parent;
   p.n_splits = n_splits;
   p.split_len = split_len;
+  p.win_sink = a->window_sink;
+  p.win_len = a->window_len;
   p.out = a->out;
   p.lse = a->lse;
   p.dbg_count = a->dbg_count;

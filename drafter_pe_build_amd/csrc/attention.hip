@@ -87,7 +87,7 @@ __device__ __forceinline__ float colgroup_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <typename S, int DH, bool DBG>
+template <typename S, int DH, bool DBG, bool WIN>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int tps) {
   constexpr bool BF = sizeof(S) == 2;
   constexpr int CH = Storage<S>::CH;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   __shared__ int s_start[QMAX], s_off[QMAX + 1];
   __shared__ int s_anc_row[ANC_MAX];                               // chain rows, then
   __shared__ __attribute__((aligned(16))) int s_anc_own[ANC_MAX];  // -1 to the end of the tile
-  __shared__ int s_red[8];
+  __shared__ int s_red[12];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,11 +154,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
   if (lane == 63) s_red[wave] = incl;
   if (lane == 0) s_red[4 + wave] = mx;
+  if constexpr (WIN) {  // the earliest prefix end among the queries that have one
+    int mn = (tid < nq && st >= 0) ? st : 0x7fffffff;
+    for (int o = 32; o > 0; o >>= 1) mn = min(mn, __shfl_xor(mn, o, 64));
+    if (lane == 0) s_red[8 + wave] = mn;
+  }
   __syncthreads();
   int wofs = 0;
   for (int w = 0; w < wave; ++w) wofs += s_red[w];
   const int n_anc_all = s_red[0] + s_red[1] + s_red[2] + s_red[3];
   const int max_start = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
+  const int min_start = WIN ? min(min(s_red[8], s_red[9]), min(s_red[10], s_red[11])) : 0;
   if (tid < QMAX) s_off[tid] = wofs + incl - cnt;
   if (tid == 0) s_off[QMAX] = n_anc_all;
   if (cnt > 0) {
@@ -184,7 +190,23 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   // ---- this split's prefix range [kbeg, kend]
   const int kbeg = sp * p.split_len;
   const int kend = (sp == p.n_splits - 1) ? max_start : min(max_start, kbeg + p.split_len - 1);
-  const int n_pref = (kend >= kbeg) ? (kend - kbeg + KT) / KT : 0;
+  int n_pref = (kend >= kbeg) ? (kend - kbeg + KT) / KT : 0;
+  // StreamingLLM window (never split): the sink tiles, then the tiles from the
+  // earliest window start of this workgroup's queries to its last prefix key
+  int w_na = 0, w_bt = 0;
+  if constexpr (WIN) {
+    if (n_pref > 0) {
+      w_na = min((p.win_sink + KT - 1) / KT, n_pref);
+      const int wlo = min_start == 0x7fffffff ? 0x7fffffff - KT : max(min_start - p.win_len + 1, 0);
+      w_bt = max(wlo / KT, w_na);
+      n_pref = w_na + max(n_pref - w_bt, 0);
+    }
+  }
+  // first key of prefix tile it
+  auto pkey = [&](int it) -> int {
+    if constexpr (WIN) return (it < w_na ? it : w_bt + it - w_na) * KT;
+    else return kbeg + it * KT;
+  };
   const int n_tiles = n_pref + (n_anc + KT - 1) / KT;
 
   // ---- this lane's columns, one per column block
@@ -265,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   auto load_tile = [&](int it) {
     if constexpr (BF) return;
     if (it < n_pref) {
-      const int p0 = kbeg + it * KT;
+      const int p0 = pkey(it);
       const int row0 = max(min(seg_base + p0, last_row), 0);
       const int room = max(min(kend - p0, last_row - row0), 0);  // keys past it repeat the last held row
       const S* kb = Kg + (int64_t)row0 * rstride + kvh * DH;
@@ -340,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
   auto dma_tile = [&](int it, int buf) {
     if constexpr (BF) {
       if (it < n_pref) {
-        const int p0 = kbeg + it * KT;
+        const int p0 = pkey(it);
         const int row0 = max(min(seg_base + p0, last_row), 0);
         const int room = max(min(kend - p0, last_row - row0), 0);  // keys past it repeat the last held row
         const bool whole = room >= KT - 1;
@@ -424,21 +446,27 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb) {
         const int d = climit[cb] - k0 - 4 * g;
+        const int dl = d - p.win_len, ds = p.win_sink - k0 - 4 * g;  // window bounds, same offsets
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            sacc[cb][bb][j] = (16 * (2 * h + bb) + j <= d) ? sacc[cb][bb][j] : -INFINITY;
+          for (int j = 0; j < 4; ++j) {
+            const int x = 16 * (2 * h + bb) + j;
+            const bool vis = x <= d && (!WIN || x < ds || x > dl);
+            sacc[cb][bb][j] = vis ? sacc[cb][bb][j] : -INFINITY;
+          }
       }
     }
     if constexpr (DBG) {
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb) {
         const int d = climit[cb] - k0 - 4 * g;
+        const int dl = d - p.win_len, ds = p.win_sink - k0 - 4 * g;
         for (int i = 0; i < 8; ++i) {
           const int bq = 2 * h + (i >> 2), j = i & 3;
           const int kk = 16 * bq + 4 * g + j;
-          const bool vis = anc ? (s_anc_own[k0 + kk] == cq[cb]) : (16 * bq + j <= d);
+          const int x = 16 * bq + j;
+          const bool vis = anc ? (s_anc_own[k0 + kk] == cq[cb]) : (x <= d && (!WIN || x < ds || x > dl));
           if (vis) {
             const int row = anc ? s_anc_row[k0 + kk] : seg_base + k0 + kk;
             ++dcnt[cb];
@@ -564,10 +592,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int t
     }
 
     const bool anc = it >= n_pref;
-    const int k0 = anc ? (it - n_pref) * KT : kbeg + it * KT;
-    const bool skip = anc ? (k0 + KT <= wa0 || k0 >= wa1) : (k0 > wmax);
+    const int k0 = anc ? (it - n_pref) * KT : pkey(it);
+    // window: a tile no column sees is past the sink and before every window
+    const bool skip = anc ? (k0 + KT <= wa0 || k0 >= wa1)
+                          : (k0 > wmax || (WIN && k0 >= p.win_sink && k0 + KT - 1 <= wmin - p.win_len));
     if (!skip) {
-      const bool full = !DBG && !anc && (k0 + KT - 1 <= wmin);
+      const bool full = !DBG && !anc && (k0 + KT - 1 <= wmin) &&
+                        (!WIN || k0 + KT - 1 < p.win_sink || k0 > wmax - p.win_len);
       const char* Kb = Ks[buf];
       const char* Vb = Vs[buf];
       HalfS s0, s1;
@@ -698,8 +729,13 @@ static void launch_attn_t(const AttnParams& p, hipStream_t s) {
   const int QPW = attn_queries_per_workgroup(G, DH);
   const int tps = (p.q_per_seg + QPW - 1) / QPW;
   const int grid = p.num_seg * tps * p.n_splits * p.Hkv;
-  if (p.dbg_count) hipLaunchKernelGGL((attn_kernel<S, DH, true>), dim3(grid), dim3(256), 0, s, p, G, tps);
-  else hipLaunchKernelGGL((attn_kernel<S, DH, false>), dim3(grid), dim3(256), 0, s, p, G, tps);
+  if (p.win_len > 0) {
+    if (p.dbg_count) hipLaunchKernelGGL((attn_kernel<S, DH, true, true>), dim3(grid), dim3(256), 0, s, p, G, tps);
+    else hipLaunchKernelGGL((attn_kernel<S, DH, false, true>), dim3(grid), dim3(256), 0, s, p, G, tps);
+  } else {
+    if (p.dbg_count) hipLaunchKernelGGL((attn_kernel<S, DH, true, false>), dim3(grid), dim3(256), 0, s, p, G, tps);
+    else hipLaunchKernelGGL((attn_kernel<S, DH, false, false>), dim3(grid), dim3(256), 0, s, p, G, tps);
+  }
   if (p.n_splits > 1) {
     const int64_t nqh = (int64_t)p.num_q * p.Hq;
     const int64_t nqk = (int64_t)p.num_q * p.Hkv;

@@ -151,6 +151,7 @@ struct AttnParams {
   float* part_o;       // [n_splits, num_q*Hq, Dh]
   float* part_ml;      // [n_splits, num_q*Hq, 2]
   uint64_t* part_dbg;  // [n_splits, num_q*Hkv, 2]
+  int win_sink, win_len;  // StreamingLLM window over the prefix keys (win_len 0: none; never split)
 };
 void launch_attention(const AttnParams& p, int bf16, int head_dim, hipStream_t s);
 // Queries one attention workgroup takes: 128 (query, head) columns of one kv

@@ -264,6 +264,16 @@ typedef struct {
     int64_t* dbg_count;     /* [num_q, Hkv] keys seen, or NULL                 */
     uint64_t* dbg_hash;     /* [num_q, Hkv] sum mod 2^64 of SplitMix64(row)
                                over the rows seen, or NULL                     */
+    int32_t window_sink;    /* StreamingLLM variant ([RFC] "Separate Ablation:
+                               StreamingLLM", sink=256, window=2048): with
+                               window_len > 0, prefix row j (0 <= j <= q_start)
+                               is seen only when j < window_sink or
+                               q_start - j < window_len; chain rows are
+                               unchanged.  0 and 0 (the default of a zeroed
+                               struct): the full prefix.  Both >= 0; a window
+                               is never split (split_len must be 0, else
+                               PE_ERR_UNSUPPORTED).                          */
+    int32_t window_len;
 } pe_attn_args;
 
 /*

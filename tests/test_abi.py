@@ -108,3 +108,15 @@ def test_attention_validation_and_workspace():
         assert lib.pe_draft_attention(ctypes.byref(a2), None, 0, None) in (1, 2), kw
     # split path without workspace is refused
     assert lib.pe_draft_attention(ctypes.byref(a), None, 0, None) == 1
+    # StreamingLLM window: negative sizes are invalid, a requested split is unsupported,
+    # and a window is never split (no workspace needed)
+    base = dict(num_q=7, num_seg=1, q_per_seg=7, num_kv_rows=2055, n_q_heads=64, n_kv_heads=8, head_dim=64,
+                scale=0.125, dtype=L.PE_BF16, q=FAKE, q_row_stride=4096, k=FAKE, v=FAKE, seg_kv_base=FAKE,
+                q_start=FAKE, out=FAKE, max_prefix=2055)
+    for kw, code in ((dict(window_len=-1), 1), (dict(window_sink=-3, window_len=8), 1),
+                     (dict(window_sink=4, window_len=64, split_len=128), 2)):
+        a3 = L.attn_args(**{**base, **kw})
+        assert lib.pe_draft_attention(ctypes.byref(a3), None, 0, None) == code, kw
+    a4 = L.attn_args(**{**base, "window_sink": 256, "window_len": 2048})
+    assert lib.pe_draft_attention_workspace(ctypes.byref(a4), ctypes.byref(n)) == 0
+    assert n.value == 16

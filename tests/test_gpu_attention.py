@@ -12,6 +12,10 @@
 * Random anchors (max_anchors): the sampled query subset against every key
   row, small layouts in full (unsplit and split) and the 8K setting on a
   sample of queries, index stats of every query.
+* StreamingLLM window (sink + recent window over the depth-0 keys): small
+  layouts in full with chunked == unchunked, and the pages' sink 256 /
+  window 2048 on the N=8192, K=8 layout (per-query counts in closed form,
+  values on a sample).
 """
 import numpy as np
 import pytest
@@ -48,7 +52,7 @@ def upload_layout(Lay):
                 base=torch.zeros(1, dtype=torch.int32, device="cuda"), dtype=dt)
 
 
-def run_cod(D, Lay, c0=0, c1=None, out=None, lse=None, dbg=True, split_len=0):
+def run_cod(D, Lay, c0=0, c1=None, out=None, lse=None, dbg=True, split_len=0, sink=0, window=0):
     T = Lay["T"]
     c1 = T if c1 is None else c1
     nq = c1 - c0
@@ -65,25 +69,25 @@ def run_cod(D, Lay, c0=0, c1=None, out=None, lse=None, dbg=True, split_len=0):
                     q=D["q"][c0:c1], q_row_stride=Hq * Dh, k=D["k"], v=D["v"], seg_kv_base=D["base"],
                     q_start=D["start"][c0:c1], q_depth=D["depth"][c0:c1], q_self_row=D["self_row"][c0:c1],
                     kv_parent=D["parent"], max_prefix=Lay["N"], split_len=split_len, out=out, lse=lse,
-                    dbg_count=cnt, dbg_hash=hsh)
+                    dbg_count=cnt, dbg_hash=hsh, window_sink=sink, window_len=window)
     L.pe_draft_attention(a, "cuda")
     return out, lse, cnt, hsh
 
 
-def check_against_oracle(Lay, out, lse, cnt, hsh, queries, name):
+def check_against_oracle(Lay, out, lse, cnt, hsh, queries, name, sink=0, window=0):
     dt = Lay["dtype"]
     tol = TOL[dt]
     q64 = LazyRows(Lay["q"], dt)
     k64 = od.to_f64(Lay["k"], dt)
     v64 = od.to_f64(Lay["v"], dt)
-    ref_o, ref_l = oc.attention(q64, k64, v64, Lay["start"], Lay["depth"], queries)
+    ref_o, ref_l = oc.attention(q64, k64, v64, Lay["start"], Lay["depth"], queries, sink=sink, window=window)
     o = dev_to_f64(out)[queries]
     e = om.relerr(o, ref_o)
     el = om.relerr(lse.cpu().numpy()[queries], ref_l)
     say("  [%s] out relerr %.3g  lse relerr %.3g  (%d queries)" % (name, e, el, len(queries)))
     assert e <= tol and el <= tol
     if cnt is not None:
-        rc, rh = oc.index_stats(Lay["start"], Lay["depth"], queries)
+        rc, rh = oc.index_stats(Lay["start"], Lay["depth"], queries, sink=sink, window=window)
         gc = cnt.cpu().numpy()[queries]
         gh = hsh.cpu().numpy().view(np.uint64)[queries]
         for j in range(gc.shape[1]):
@@ -143,6 +147,52 @@ def test_cod_training_shape_n4096():
         np.testing.assert_array_equal(gc[:, j], rc)
         np.testing.assert_array_equal(gh[:, j], rh)
     assert int(rc.sum()) == int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
+
+
+@pytest.mark.parametrize("dtype,heads,N,D,keep,sink,window", [
+    ("bf16", (8, 2, 128), 400, 5, 0.7, 16, 100),     # windows inside and across tiles, sink < one tile
+    ("bf16", (32, 8, 128), 300, 8, 1.0, 64, 64),     # sink = one tile, window = one tile
+    ("f32", (8, 2, 64), 350, 4, 0.8, 0, 37),         # no sink
+    ("bf16", (16, 4, 64), 260, 3, 0.9, 100, 1),      # the window is the query itself
+    ("bf16", (8, 8, 128), 200, 5, 0.7, 8, 500),      # window wider than the sequence
+])
+def test_window_small_layouts(dtype, heads, N, D, keep, sink, window):
+    Lay = si.cod_case(N, D, keep, 0.5, 25, heads=heads, dtype=dtype)
+    name = "window %s N=%d D=%d heads=%s sink=%d window=%d T=%d" % (dtype, N, D, heads, sink, window, Lay["T"])
+    say(name)
+    Dv = upload_layout(Lay)
+    out, lse, cnt, hsh = run_cod(Dv, Lay, sink=sink, window=window)
+    torch.cuda.synchronize()
+    check_against_oracle(Lay, out, lse, cnt, hsh, np.arange(Lay["T"]), name, sink=sink, window=window)
+    # chunks of 256 queries (and a ragged tail) give the same bits
+    out1, lse1, _, _ = run_cod(Dv, Lay, dbg=False, sink=sink, window=window)
+    out2 = torch.empty_like(out1)
+    lse2 = torch.empty_like(lse1)
+    for c0 in range(0, Lay["T"], 256):
+        c1 = min(Lay["T"], c0 + 256)
+        run_cod(Dv, Lay, c0, c1, out=out2[c0:c1], lse=lse2[c0:c1], dbg=False, sink=sink, window=window)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out2), bits(out1)) and np.array_equal(bits(lse2), bits(lse1))
+
+
+def test_window_long_sequence_n8192():
+    # the pages' StreamingLLM setting (sink 256, window 2048) on the N=8192, K=8 layout
+    Lay = si.cod_config(4)
+    T = Lay["T"]
+    say("window N=8192 K=8 sink=256 window=2048")
+    Dv = upload_layout(Lay)
+    out, lse, cnt, hsh = run_cod(Dv, Lay, sink=256, window=2048)
+    torch.cuda.synchronize()
+    i = Lay["start"].astype(np.int64)
+    closed = np.minimum(256, i + 1) + np.maximum(0, i - np.maximum(256, i - 2047) + 1) + Lay["depth"]
+    np.testing.assert_array_equal(cnt[:, 0].cpu().numpy(), closed)
+    g = np.random.default_rng(3)
+    sample = set()
+    for c in range(8):
+        sample.update([8192 * c, 8192 * c + 300, 8192 * c + 2300, 8192 * c + 8191])
+    sample.update(g.choice(T, 24, replace=False).tolist())
+    check_against_oracle(Lay, out, lse, cnt, hsh, np.array(sorted(sample)), "window N=8192 sampled",
+                         sink=256, window=2048)
 
 
 def upload_anchor(A):
