@@ -142,6 +142,40 @@ def lm_head_argmax(x, final_gain, w_lm, eps, dtype="f64", chunk=16384, keep_logi
     return tok, best - second, logits, np.sqrt(ss / V)
 
 
+def lm_head_loss(x, final_gain, w_lm, eps, targets, dtype="f64", chunk=16384):
+    """Log-sum-exp and cross-entropy of the LM-head logits, row by row.
+
+    f = RMSNorm(x); z = W_lm f; lse = log sum_v exp(z_v);
+    loss = lse - z[target] (the negative log-probability of the target
+    token), 0 where target < 0 (an ignored row).  [RFC] "Separate Ablation:
+    StreamingLLM & The 32K Wall": at long sequences the [T, V] logits tensor,
+    not attention, exhausts memory, which a loss computed slice by slice
+    avoids.  ``w_lm`` is upcast to float64 one vocabulary slice at a time;
+    the log-sum-exp is accumulated over the slices with a running maximum.
+    Returns (lse, loss) [n] float64.
+    """
+    f = rmsnorm(np.asarray(x, dtype=np.float64), final_gain, eps)
+    V = w_lm.shape[0]
+    n = f.shape[0]
+    targets = np.asarray(targets, dtype=np.int64)
+    m = np.full(n, -np.inf)
+    ssum = np.zeros(n)
+    zt = np.zeros(n)
+    for s in range(0, V, chunk):
+        w = w_lm[s:s + chunk]
+        w = bf16_to_f64(w) if dtype == "bf16" else np.asarray(w, dtype=np.float64)
+        z = f @ w.T
+        mz = np.maximum(m, z.max(axis=1))
+        ssum = ssum * np.exp(m - mz) + np.exp(z - mz[:, None]).sum(axis=1)
+        m = mz
+        inside = (targets >= s) & (targets < s + z.shape[1])
+        rows = np.nonzero(inside)[0]
+        zt[rows] = z[rows, targets[rows] - s]
+    lse = m + np.log(ssum)
+    loss = np.where(targets >= 0, lse - zt, 0.0)
+    return lse, loss
+
+
 def drafter_forward(dims, weights, batch, kv_base, k_cache, v_cache, keep_logits=True):
     """Stages 2-4 of the drafter on a built batch (stage 1 is oracle.batch).
 

@@ -4,7 +4,9 @@ RMSNorm: its closed form (unit-gain output has RMS sqrt(ms/(ms+eps))), scale
 invariance, and torch.nn.functional.rms_norm in fp64.  Layer: a composition
 of torch fp64 CPU ops (rms_norm, linear, scaled_dot_product_attention with a
 boolean mask and GQA, silu).  Argmax: numpy's first maximum, including ties
-across the oracle's vocabulary slices.
+across the oracle's vocabulary slices.  LM-head loss: torch's logsumexp and
+cross_entropy (ignore_index) in fp64 over slices that do not divide V, log V
+for equal logits, and direct summation on a two-token vocabulary.
 """
 import numpy as np
 import pytest
@@ -140,3 +142,38 @@ def test_argmax_ties_and_slices():
     assert np.any(gap == 0.0)
     for i in range(len(x)):
         assert tok[i] == np.nonzero(z[i] == z[i].max())[0][0]
+
+
+def test_lm_head_loss_against_torch_cross_entropy():
+    g = np.random.default_rng(31)
+    n, d, V = 9, 24, 1000
+    x = g.standard_normal((n, d))
+    gain = g.uniform(0.5, 1.5, d)
+    w = g.standard_normal((V, d)) * 0.5
+    targets = g.integers(0, V, n)
+    targets[3] = -1                                      # an ignored row
+    lse, loss = od.lm_head_loss(x, gain, w, 1e-6, targets, chunk=300)   # slices that do not divide V
+    f = od.rmsnorm(x, gain, 1e-6)
+    z = torch.from_numpy(f @ w.T)
+    ref_lse = torch.logsumexp(z, dim=1).numpy()
+    ref = torch.nn.functional.cross_entropy(z, torch.from_numpy(targets), ignore_index=-1, reduction="none").numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
+    np.testing.assert_allclose(loss, ref, rtol=1e-12, atol=1e-13)
+    assert loss[3] == 0.0
+
+
+def test_lm_head_loss_closed_forms():
+    # equal logits: lse = log V and every target costs log V
+    n, d, V = 4, 8, 777
+    x = np.random.default_rng(1).standard_normal((n, d))
+    lse, loss = od.lm_head_loss(x, np.ones(d), np.zeros((V, d)), 1e-6, [0, 5, 776, 300], chunk=128)
+    np.testing.assert_allclose(lse, np.log(V), rtol=1e-15)
+    np.testing.assert_allclose(loss, np.log(V), rtol=1e-15)
+    # two tokens: direct summation without a shift
+    w = np.array([[1.0, 0.0], [0.0, 2.0]])
+    xx = np.array([[3.0, 4.0]])
+    f = xx / np.sqrt(np.mean(xx ** 2) + 1e-6)
+    lse, loss = od.lm_head_loss(xx, np.ones(2), w, 1e-6, [1], chunk=1)
+    z = np.array([f[0, 0], 2 * f[0, 1]])
+    assert abs(lse[0] - np.log(np.exp(z[0]) + np.exp(z[1]))) < 1e-14
+    assert abs(loss[0] - (lse[0] - z[1])) < 1e-14
