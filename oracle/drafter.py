@@ -147,7 +147,8 @@ def lm_head_loss(x, final_gain, w_lm, eps, targets, dtype="f64", chunk=16384):
 
     f = RMSNorm(x); z = W_lm f; lse = log sum_v exp(z_v);
     loss = lse - z[target] (the negative log-probability of the target
-    token), 0 where target < 0 (an ignored row).  [RFC] "Separate Ablation:
+    token), 0 where the target is outside [0, V) (an ignored row: no logit
+    exists for it).  [RFC] "Separate Ablation:
     StreamingLLM & The 32K Wall": at long sequences the [T, V] logits tensor,
     not attention, exhausts memory, which a loss computed slice by slice
     avoids.  ``w_lm`` is upcast to float64 one vocabulary slice at a time;
@@ -172,7 +173,7 @@ def lm_head_loss(x, final_gain, w_lm, eps, targets, dtype="f64", chunk=16384):
         rows = np.nonzero(inside)[0]
         zt[rows] = z[rows, targets[rows] - s]
     lse = m + np.log(ssum)
-    loss = np.where(targets >= 0, lse - zt, 0.0)
+    loss = np.where((targets >= 0) & (targets < V), lse - zt, 0.0)
     return lse, loss
 
 

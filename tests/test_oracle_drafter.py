@@ -160,6 +160,11 @@ def test_lm_head_loss_against_torch_cross_entropy():
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
     np.testing.assert_allclose(loss, ref, rtol=1e-12, atol=1e-13)
     assert loss[3] == 0.0
+    # a target past the vocabulary has no logit: an ignored row like -1
+    t2 = targets.copy()
+    t2[5] = V + 2
+    _, loss2 = od.lm_head_loss(x, gain, w, 1e-6, t2, chunk=300)
+    assert loss2[5] == 0.0 and np.array_equal(np.delete(loss2, 5), np.delete(loss, 5))
 
 
 def test_lm_head_loss_closed_forms():
