@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--attention-only", type=int, choices=(3, 4, 5, 6), default=0,
                     help="time only the COD (3), parallel-group (4), random-anchor (5) or windowed "
                          "parallel-group (6) attention workload and print its line")
+    ap.add_argument("--loss-only", action="store_true",
+                    help="time only the fused LM-head loss on a training-sized batch and print its line")
     ap.add_argument("--decode64-only", action="store_true",
                     help="time only the c=64 decode step and print its line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -208,6 +210,37 @@ def measure_anchor(steps, stream):
             "mfma_frac": fl / (msa * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "launches": 1}
 
 
+def measure_loss(dims, steps, stream):
+    """LM-head log-sum-exp + cross-entropy over a training-sized batch (the
+    COD N=4096 layout's 7,794 rows) without materialising the logits."""
+    import numpy as np
+    import torch
+    from drafter_pe_build_amd import _lib as L
+    from drafter_pe_build_amd.step import to_device
+    from synth import inputs as si
+    n = si.cod_config(3, draw_qkv=False)["T"]
+    log("fused LM-head loss, %d rows" % n)
+    W = si.drafter_weights(dims, 1, skip=("embed", "w_fc", "w_qkv", "w_o", "w_gate", "w_up", "w_down", "h_shared"))
+    cd = L.dims_struct(dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn, dims.vocab,
+                       dims.mask_token_id, dims.eps, dims.dtype)
+    cw = L.weights_struct({"w_lm": L.pe_pack_weight(to_device(W["w_lm"], "cuda")),
+                           "final_gain": to_device(W["final_gain"], "cuda")})
+    g = np.random.default_rng(7)
+    x = torch.from_numpy(g.standard_normal((n, dims.hidden)).astype(np.float32)).cuda()
+    t = torch.from_numpy(g.integers(0, dims.vocab, n).astype(np.int32)).cuda()
+    lse = torch.empty(n, dtype=torch.float32, device="cuda")
+    loss = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.pe_lm_head_loss_workspace(cd, n), dtype=torch.uint8, device="cuda")
+    ms = time_sustained(lambda: L.pe_lm_head_loss(cd, cw, n, x, t, lse, loss, workspace=ws), steps, stream)
+    fl = 2.0 * n * dims.vocab * dims.hidden
+    log("  %.1f us, %.0f TFLOP/s" % (ms * 1e3, fl / (ms * 1e-3) / 1e12))
+    del cw, x, t, lse, loss, ws
+    torch.cuda.empty_cache()
+    return {"rows": n, "ms": ms, "rows_per_s": n / (ms * 1e-3), "tflops": fl / (ms * 1e-3) / 1e12,
+            "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "logits_bytes_avoided": n * dims.vocab * 4}
+
+
 def measure_decode64(dims, W, steps, stream):
     """The c=64 decode step (64 requests x 7 slots, ragged caches), one graph
     replay per step: time, rate, HBM and matrix-core fractions."""
@@ -260,6 +293,11 @@ def main():
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
         return
     dims = si.GPTOSS_DIMS
+    if args.loss_only:
+        r = measure_loss(dims, args.steps, stream)
+        print(json.dumps({"metric": "lm_head_loss_rows_per_s", "value": r["rows_per_s"], "unit": "rows/s",
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
+        return
     if args.decode64_only:
         log("generating the drafter weights")
         r = measure_decode64(dims, si.drafter_weights(dims, 1), args.steps, stream)
@@ -342,6 +380,7 @@ def main():
             extra[name] = measure_attention(cfg, max(5, args.steps // 5), stream)
         extra["anchor_attention_n8192"] = measure_anchor(max(5, args.steps // 5), stream)
         extra["window_attention_n8192_chunked"] = measure_attention(6, max(5, args.steps // 5), stream)
+        extra["lm_head_loss_7794_rows"] = measure_loss(dims, max(5, args.steps // 5), stream)
         result["secondary"] = extra
 
     if not args.no_cpu:

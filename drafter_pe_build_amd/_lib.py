@@ -70,6 +70,9 @@ EXPORTS = {
     "pe_lm_head_argmax": (c_int, [POINTER(PeDims), POINTER(PeWeights), c_int32, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_size_t, c_void_p]),
     "pe_lm_head_argmax_workspace": (c_int, [POINTER(PeDims), c_int32, POINTER(c_size_t)]),
+    "pe_lm_head_loss": (c_int, [POINTER(PeDims), POINTER(PeWeights), c_int32, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_size_t, c_void_p]),
+    "pe_lm_head_loss_workspace": (c_int, [POINTER(PeDims), c_int32, POINTER(c_size_t)]),
 }
 
 _lib = None
@@ -227,6 +230,20 @@ def pe_lm_head_argmax_workspace(dims, n):
     m = c_size_t()
     _check("pe_lm_head_argmax_workspace", lib().pe_lm_head_argmax_workspace(ctypes.byref(dims), n, ctypes.byref(m)))
     return m.value
+
+
+def pe_lm_head_loss_workspace(dims, n):
+    m = c_size_t()
+    _check("pe_lm_head_loss_workspace", lib().pe_lm_head_loss_workspace(ctypes.byref(dims), n, ctypes.byref(m)))
+    return m.value
+
+
+def pe_lm_head_loss(dims, weights, n, x, targets, lse=None, loss=None, workspace=None, stream=None):
+    ws = _workspace(pe_lm_head_loss_workspace(dims, n), x.device, workspace)
+    w = weights if isinstance(weights, PeWeights) else weights_struct(weights)
+    _check("pe_lm_head_loss", lib().pe_lm_head_loss(
+        ctypes.byref(dims), ctypes.byref(w), n, ptr(x), ptr(targets), ptr(lse), ptr(loss), ptr(ws), ws.numel(),
+        stream_handle(stream)))
 
 
 def pe_lm_head_argmax(dims, weights, n, x, tokens, logits=None, workspace=None, stream=None):

@@ -235,23 +235,31 @@ FuseWs fuse_ws(const pe_drafter_dims* d, int T, void* base) {
   return w;
 }
 
-// Workspace of the LM head.
+// Workspace of the LM head (loss: the log-sum-exp partial sums and the
+// target logits instead of the argmax indices).
 struct LmWs {
   void* f;
   float* pv;
   int32_t* pi;
+  float* ps;
+  float* tgt;
   int* zero;
   int nzero;
   size_t total;
 };
 
-LmWs lm_ws(const pe_drafter_dims* d, int n, void* base) {
+LmWs lm_ws(const pe_drafter_dims* d, int n, void* base, bool loss = false) {
   LmWs w{};
   Carver c(base);
   const size_t P = (size_t)gemm_argmax_partials(n, d->vocab);
   w.f = c.take((size_t)((n + 15) / 16 * 16) * d->hidden * esize(d->dtype));  // rows padded to 16 (operand layout)
   w.pv = static_cast<float*>(c.take(P * n * 4));
-  w.pi = static_cast<int32_t*>(c.take(P * n * 4));
+  if (loss) {
+    w.ps = static_cast<float*>(c.take(P * n * 4));
+    w.tgt = static_cast<float*>(c.take((size_t)n * 4));
+  } else {
+    w.pi = static_cast<int32_t*>(c.take(P * n * 4));
+  }
   w.nzero = zero_ints((size_t)d->hidden * esize(d->dtype));
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
   w.total = c.off;
@@ -606,6 +614,55 @@ pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weight
   gp.epi.part_idx = lw.pi;
   const int used = launch_gemm(gp, bf, stream);
   launch_argmax_reduce(lw.pv, lw.pi, used, n, tokens, stream);
+  return launched();
+}
+
+pe_status pe_lm_head_loss_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes) {
+  pe_status st = check_dims(dims);
+  if (st != PE_OK) return st;
+  if (!bytes || n < 0) return PE_ERR_INVALID_ARG;
+  *bytes = lm_ws(dims, n, nullptr, true).total;
+  return PE_OK;
+}
+
+pe_status pe_lm_head_loss(const pe_drafter_dims* dims, const pe_drafter_weights* w, int32_t n, const float* x,
+                          const int32_t* targets, float* lse, float* loss, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  pe_status st = check_dims(dims);
+  if (st != PE_OK) return st;
+  if (!w || n < 0) return PE_ERR_INVALID_ARG;
+  if (n == 0) return PE_OK;
+  if (!x || !w->final_gain || !w->w_lm || !al16(w->w_lm) || !al16(x)) return PE_ERR_INVALID_ARG;
+  if (!lse && !loss) return PE_ERR_INVALID_ARG;
+  if (loss && !targets) return PE_ERR_INVALID_ARG;
+  if (!ws_ok(workspace, workspace_bytes, lm_ws(dims, n, nullptr, true).total)) return PE_ERR_INVALID_ARG;
+  const LmWs lw = lm_ws(dims, n, workspace, true);
+  const int d = dims->hidden;
+  const int bf = dims->dtype == PE_BF16;
+  // z = w_lm RMSNorm(x), streamed tile by tile: per tile (max, sum of exp) and the target's logit
+  GemmParams gp{};
+  gp.X = x;
+  gp.ldx = d;
+  gp.W = w->w_lm;
+  gp.M = n;
+  gp.N = dims->vocab;
+  gp.K = d;
+  gp.xzero = lw.zero;
+  gp.nrm.gain = w->final_gain;
+  gp.nrm.segs = 1;
+  gp.nrm.seg_len = d;
+  gp.nrm.eps = dims->eps;
+  gp.nrm.x_f32 = 1;
+  gp.nrm.tmp = lw.f;
+  gp.clear = lw.zero;
+  gp.nclear = lw.nzero;
+  gp.epi.kind = EPI_LSE;
+  gp.epi.part_val = lw.pv;
+  gp.epi.part_sum = lw.ps;
+  gp.epi.targets = targets;
+  gp.epi.tgt_logit = lw.tgt;
+  const int used = launch_gemm(gp, bf, stream);
+  launch_lse_reduce(lw.pv, lw.ps, used, n, dims->vocab, targets, lw.tgt, lse, loss, stream);
   return launched();
 }
 

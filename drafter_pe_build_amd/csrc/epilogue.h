@@ -5,6 +5,36 @@
 
 namespace pe {
 
+// Per-row reduction of the LM head over the features a lane, a wave, a tile
+// has seen: argmax (value v, lowest index i) or log-sum-exp (maximum v and
+// s = sum of exp(y - v)).  States merge in a fixed order, so the results do
+// not depend on timing.
+struct RowRed {
+  float v, s;
+  int i;
+  __device__ static RowRed init() { return RowRed{-INFINITY, 0.f, 0x7fffffff}; }
+  __device__ void add(bool lse, float y, int n) {
+    if (lse) {
+      if (y > v) { s = s * expf(v - y) + 1.f; v = y; }
+      else s += expf(y - v);
+    } else if (better(y, n, v, i)) { v = y; i = n; }
+  }
+  __device__ void merge(bool lse, float ov, int oi, float os) {
+    if (lse) {
+      if (ov > v) { s = s * expf(v - ov) + os; v = ov; }
+      else if (ov != -INFINITY) s += os * expf(ov - v);
+    } else if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+  // lanes 16 and 32 apart (the four lane groups that hold one row)
+  __device__ void merge_groups(bool lse) {
+    for (int o = 16; o < 64; o <<= 1) {
+      const float ov = __shfl_xor(v, o, 64), os = __shfl_xor(s, o, 64);
+      const int oi = __shfl_xor(i, o, 64);
+      merge(lse, ov, oi, os);
+    }
+  }
+};
+
 template <typename S>
 __device__ __forceinline__ void epi_store(const Epi& e, int m, int n, float y, float y2) {
   switch (e.kind) {

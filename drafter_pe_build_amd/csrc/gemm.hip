@@ -542,7 +542,7 @@ void gemm_stream_lds_kernel(GemmParams p) {
 #ifndef PE_LM_WPE
 #define PE_LM_WPE 4
 #endif
-template <typename S, int NFB, int KS, int U, bool XL, bool NORM>
+template <typename S, int NFB, int KS, int U, bool XL, bool NORM, bool LSE>
 __global__ __launch_bounds__(64 * NFB * KS) __attribute__((amdgpu_waves_per_eu(PE_LM_WPE)))
 void lm_argmax_stream_kernel(GemmParams p) {
   constexpr int CH = Storage<S>::CH;
@@ -603,8 +603,8 @@ void lm_argmax_stream_kernel(GemmParams p) {
     xstep = STEP * (int)sizeof(S);  // p.xzero holds >= K zeroed elements
   }
   __shared__ f32x4 red[KS > 1 ? NFB * (KS - 1) * 64 : 1];
-  float best = -INFINITY;
-  int bidx = 0x7fffffff;
+  RowRed rr = RowRed::init();  // argmax or (LSE) log-sum-exp state of row r over this lane's features
+  const int tgt = (LSE && p.epi.targets && xr) ? p.epi.targets[r] : -1;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int fb = tile * NFB + fbl;
     const bool active = fb < nfb;
@@ -641,26 +641,22 @@ void lm_argmax_stream_kernel(GemmParams p) {
         const int n = fb * 16 + 4 * g + j;
         if (n >= N) continue;
         if (p.epi.logits) p.epi.logits[(int64_t)r * N + n] = acc[j];
-        if (better(acc[j], n, best, bidx)) { best = acc[j]; bidx = n; }
+        if (LSE && n == tgt) p.epi.tgt_logit[r] = acc[j];
+        rr.add(LSE, acc[j], n);
       }
     }
   }
-  for (int o = 16; o < 64; o <<= 1) {
-    const float ov = __shfl_xor(best, o, 64);
-    const int oi = __shfl_xor(bidx, o, 64);
-    if (better(ov, oi, best, bidx)) { best = ov; bidx = oi; }
-  }
-  __shared__ float sbv[NW][16];
+  rr.merge_groups(LSE);
+  __shared__ float sbv[NW][16], sbs[NW][16];
   __shared__ int sbi[NW][16];
-  if (g == 0) { sbv[wave][r] = best; sbi[wave][r] = bidx; }
+  if (g == 0) { sbv[wave][r] = rr.v; sbi[wave][r] = rr.i; sbs[wave][r] = rr.s; }
   __syncthreads();
   if ((int)threadIdx.x < M) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int w = 0; w < NW; ++w)
-      if (better(sbv[w][threadIdx.x], sbi[w][threadIdx.x], bv, bi)) { bv = sbv[w][threadIdx.x]; bi = sbi[w][threadIdx.x]; }
-    p.epi.part_val[(int64_t)blockIdx.x * M + threadIdx.x] = bv;
-    p.epi.part_idx[(int64_t)blockIdx.x * M + threadIdx.x] = bi;
+    RowRed t = RowRed::init();
+    for (int w = 0; w < NW; ++w) t.merge(LSE, sbv[w][threadIdx.x], sbi[w][threadIdx.x], sbs[w][threadIdx.x]);
+    p.epi.part_val[(int64_t)blockIdx.x * M + threadIdx.x] = t.v;
+    if (LSE) p.epi.part_sum[(int64_t)blockIdx.x * M + threadIdx.x] = t.s;
+    else p.epi.part_idx[(int64_t)blockIdx.x * M + threadIdx.x] = t.i;
   }
 }
 
@@ -769,14 +765,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft,
   }
 
   if constexpr (ARGMAX) {
-    __shared__ float sbv[2][BM];
+    // argmax or log-sum-exp partials of this tile's rows (EPI_ARGMAX / EPI_LSE)
+    const bool lse = p.epi.kind == EPI_LSE;
+    __shared__ float sbv[2][BM], sbs[2][BM];
     __shared__ int sbi[2][BM];
 #pragma unroll
     for (int q = 0; q < RBW; ++q) {
       const int mloc = wm * (BM / 2) + q * 16 + r;
       const int m = m0 + mloc;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      const int tgt = (lse && p.epi.targets && m < M) ? p.epi.targets[m] : -1;
+      RowRed rr = RowRed::init();
 #pragma unroll
       for (int f = 0; f < FBW; ++f)
 #pragma unroll
@@ -785,23 +783,20 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft,
           if (n < N && m < M) {
             const float v = acc[f][q][j];
             if (p.epi.logits) p.epi.logits[(int64_t)m * N + n] = v;
-            if (better(v, n, bv, bi)) { bv = v; bi = n; }
+            if (n == tgt) p.epi.tgt_logit[m] = v;
+            rr.add(lse, v, n);
           }
         }
-      for (int o = 16; o < 64; o <<= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if (g == 0) { sbv[wn][mloc] = bv; sbi[wn][mloc] = bi; }
+      rr.merge_groups(lse);
+      if (g == 0) { sbv[wn][mloc] = rr.v; sbi[wn][mloc] = rr.i; sbs[wn][mloc] = rr.s; }
     }
     __syncthreads();
     if (tid < BM && m0 + tid < M) {
-      float bv = sbv[0][tid];
-      int bi = sbi[0][tid];
-      if (better(sbv[1][tid], sbi[1][tid], bv, bi)) { bv = sbv[1][tid]; bi = sbi[1][tid]; }
-      p.epi.part_val[(int64_t)ft * M + m0 + tid] = bv;
-      p.epi.part_idx[(int64_t)ft * M + m0 + tid] = bi;
+      RowRed rr{sbv[0][tid], sbs[0][tid], sbi[0][tid]};
+      rr.merge(lse, sbv[1][tid], sbi[1][tid], sbs[1][tid]);
+      p.epi.part_val[(int64_t)ft * M + m0 + tid] = rr.v;
+      if (lse) p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
+      else p.epi.part_idx[(int64_t)ft * M + m0 + tid] = rr.i;
     }
   } else {
 #pragma unroll
@@ -853,6 +848,35 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* pv, con
 
 void launch_argmax_reduce(const float* pv, const int32_t* pi, int P, int M, int32_t* tokens, hipStream_t s) {
   hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(256), 0, s, pv, pi, P, M, tokens);
+}
+
+// Log-sum-exp of each row from its P partial (maximum, sum of exp) pairs, merged
+// in a fixed order (thread strides, then lanes by xor distance, then waves),
+// and the cross-entropy lse - y[target] where the row has a target in [0, N).
+__global__ __launch_bounds__(256) void lse_reduce_kernel(const float* pv, const float* ps, int P, int M, int N,
+                                                         const int32_t* targets, const float* tgt, float* lse,
+                                                         float* loss) {
+  const int m = blockIdx.x;
+  RowRed rr = RowRed::init();
+  for (int q = threadIdx.x; q < P; q += 256) rr.merge(true, pv[(int64_t)q * M + m], 0, ps[(int64_t)q * M + m]);
+  for (int o = 1; o < 64; o <<= 1) {
+    const float ov = __shfl_xor(rr.v, o, 64), os = __shfl_xor(rr.s, o, 64);
+    rr.merge(true, ov, 0, os);
+  }
+  __shared__ float sv[4], ss[4];
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = rr.v; ss[threadIdx.x >> 6] = rr.s; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) rr.merge(true, sv[w], 0, ss[w]);
+    const float l = rr.v + logf(rr.s);
+    if (lse) lse[m] = l;
+    if (loss) loss[m] = (targets && targets[m] >= 0 && targets[m] < N) ? l - tgt[m] : 0.f;
+  }
+}
+
+void launch_lse_reduce(const float* pv, const float* ps, int P, int M, int N, const int32_t* targets,
+                       const float* tgt, float* lse, float* loss, hipStream_t s) {
+  hipLaunchKernelGGL(lse_reduce_kernel, dim3(M), dim3(256), 0, s, pv, ps, P, M, N, targets, tgt, lse, loss);
 }
 
 // ---------------------------------------------------------------------------
@@ -1021,10 +1045,42 @@ static GemmParams norm_first(const GemmParams& p, hipStream_t s, bool packed = f
   return q;
 }
 
+// The LM-head weight stream for M <= 16 rows (argmax or, LSE, log-sum-exp
+// partials): rows and their norm staged in LDS when they fit, else read from
+// global memory after a separate norm.  Returns the partial count.
+template <typename S, bool LSE>
+static int launch_lm_stream(const GemmParams& p0, bool norm, bool norm_fits, bool xf32, size_t lds, hipStream_t s) {
+  const int grid = gemm_argmax_partials(p0.M, p0.N);
+  const dim3 block(64 * kLmNFB * kLmKS);
+  if (lds <= (size_t)kLmXLds && norm_fits && (!norm || xf32)) {
+    if (norm) {
+      allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, true, LSE>>(kLmXLds);
+      hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, true, LSE>), dim3(grid), block, lds, s,
+                         p0);
+    } else {
+      allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false, LSE>>(kLmXLds);
+      hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false, LSE>), dim3(grid), block, lds,
+                         s, p0);
+    }
+    return grid;
+  }
+  const GemmParams p = norm ? norm_first<S>(p0, s, false) : p0;
+  if (lds <= (size_t)kLmXLds) {
+    allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false, LSE>>(kLmXLds);
+    hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false, LSE>), dim3(grid), block, lds, s,
+                       p);
+  } else {
+    hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, false, false, LSE>), dim3(grid), block, 0, s,
+                       p);
+  }
+  return grid;
+}
+
 template <typename S>
 static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
   const bool dual = p0.epi.kind == EPI_SWIGLU;
-  const bool am = p0.epi.kind == EPI_ARGMAX;
+  const bool am = epi_rowred(p0.epi.kind);
+  const bool lse = p0.epi.kind == EPI_LSE;
   const bool norm = p0.nrm.gain != nullptr;
   if (p0.M <= 16) {
     // activation rows + the zero chunk of the padding rows (+ the gains of a norm)
@@ -1037,30 +1093,8 @@ static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
     const bool norm_fits = !norm || (seg_bytes % 16 == 0 && seg_bytes / 16 <= 64 * (xf32 ? 12 : 6) &&
                                      (reinterpret_cast<uintptr_t>(p0.nrm.gain) & 15) == 0);
     if (am) {
-      const int grid = gemm_argmax_partials(p0.M, p0.N);
-      const dim3 block(64 * kLmNFB * kLmKS);
-      if (lds <= (size_t)kLmXLds && norm_fits && (!norm || xf32)) {
-        if (norm) {
-          allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, true>>(kLmXLds);
-          hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, true>), dim3(grid), block, lds, s,
-                             p0);
-        } else {
-          allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false>>(kLmXLds);
-          hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false>), dim3(grid), block, lds,
-                             s, p0);
-        }
-        return grid;
-      }
-      const GemmParams p = norm ? norm_first<S>(p0, s) : p0;
-      if (lds <= (size_t)kLmXLds) {
-        allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false>>(kLmXLds);
-        hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false>), dim3(grid), block, lds, s,
-                           p);
-      } else {
-        hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, false, false>), dim3(grid), block, 0, s,
-                           p);
-      }
-      return grid;
+      if (lse) return launch_lm_stream<S, true>(p0, norm, norm_fits, xf32, lds, s);
+      return launch_lm_stream<S, false>(p0, norm, norm_fits, xf32, lds, s);
     }
     const int fks = stream_ks(p0.K / (4 * Storage<S>::CH));
     const int fsteps = (p0.K / (4 * Storage<S>::CH) + fks - 1) / fks;

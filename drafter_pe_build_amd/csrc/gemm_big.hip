@@ -178,14 +178,16 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
 #undef PE_BIG_FRAGS
 
   if constexpr (ARGMAX) {
-    __shared__ float sbv[WN][BM];
+    // argmax or log-sum-exp partials of this tile's rows (EPI_ARGMAX / EPI_LSE)
+    const bool lse = p.epi.kind == EPI_LSE;
+    __shared__ float sbv[WN][BM], sbs[WN][BM];
     __shared__ int sbi[WN][BM];
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
       const int mloc = wm * (BM / 2) + q * 16 + r;
       const int m = m0 + mloc;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      const int tgt = (lse && p.epi.targets && m < M) ? p.epi.targets[m] : -1;
+      RowRed rr = RowRed::init();
 #pragma unroll
       for (int f = 0; f < FW; ++f)
 #pragma unroll
@@ -194,24 +196,20 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
           if (n < N && m < M) {
             const float v = acc[f][q][j];
             if (p.epi.logits) p.epi.logits[(int64_t)m * N + n] = v;
-            if (better(v, n, bv, bi)) { bv = v; bi = n; }
+            if (n == tgt) p.epi.tgt_logit[m] = v;
+            rr.add(lse, v, n);
           }
         }
-      for (int o = 16; o < 64; o <<= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if (g == 0) { sbv[wn][mloc] = bv; sbi[wn][mloc] = bi; }
+      rr.merge_groups(lse);
+      if (g == 0) { sbv[wn][mloc] = rr.v; sbi[wn][mloc] = rr.i; sbs[wn][mloc] = rr.s; }
     }
     __syncthreads();
     if (tid < BM && m0 + tid < M) {
-      float bv = sbv[0][tid];
-      int bi = sbi[0][tid];
-      for (int w = 1; w < WN; ++w)
-        if (better(sbv[w][tid], sbi[w][tid], bv, bi)) { bv = sbv[w][tid]; bi = sbi[w][tid]; }
-      p.epi.part_val[(int64_t)ft * M + m0 + tid] = bv;
-      p.epi.part_idx[(int64_t)ft * M + m0 + tid] = bi;
+      RowRed rr{sbv[0][tid], sbs[0][tid], sbi[0][tid]};
+      for (int w = 1; w < WN; ++w) rr.merge(lse, sbv[w][tid], sbi[w][tid], sbs[w][tid]);
+      p.epi.part_val[(int64_t)ft * M + m0 + tid] = rr.v;
+      if (lse) p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
+      else p.epi.part_idx[(int64_t)ft * M + m0 + tid] = rr.i;
     }
   } else if constexpr (SPLIT) {
     // partial tile of split y: [y][m][n] (the second matrix's after all splits)
@@ -304,7 +302,7 @@ static bool rows224(int M) { return ((M + 223) / 224) * 224 < ((M + 255) / 256) 
 int gemm_big_splits(const GemmParams& p) {
   // the gate/up pair measured faster on the 128 x 64 register-fed tiles
   // (67.6 us against 76 us split at 448 rows)
-  if (p.epi.kind == EPI_SWIGLU || p.epi.kind == EPI_ARGMAX) return 0;
+  if (p.epi.kind == EPI_SWIGLU || epi_rowred(p.epi.kind)) return 0;
   if (!p.split_ws || p.N % 4) return 0;
   const int bm = rows224(p.M) ? 224 : 256;
   const int tiles = ((p.N + 127) / 128) * ((p.M + bm - 1) / bm);
@@ -318,7 +316,7 @@ int gemm_big_splits(const GemmParams& p) {
 
 int launch_gemm_big(const GemmParams& p, hipStream_t s) {
   const bool r224 = rows224(p.M);
-  if (p.epi.kind == EPI_ARGMAX) {
+  if (epi_rowred(p.epi.kind)) {
     if (p.x_packed)
       return r224 ? launch_big<224, 128, 2, 3, false, true, false, true>(p, 1, s)
                   : launch_big<256, 128, 2, 3, false, true, false, true>(p, 1, s);

@@ -51,8 +51,10 @@ enum EpiKind {
                    // caches at slots[m] (skipped when slots[m] < 0)
   EPI_RESID = 2,   // out_f32[m][n] = y + res[res_rows ? res_rows[m] : m][n]
   EPI_SWIGLU = 3,  // out_s[m][n] = silu(y_gate) * y_up
-  EPI_ARGMAX = 4   // running (max, lowest index) per row; optional logits
+  EPI_ARGMAX = 4,  // running (max, lowest index) per row; optional logits
+  EPI_LSE = 5      // running (max m, sum exp(y - m)) per row and the target's logit
 };
+inline bool epi_rowred(int kind) { return kind == EPI_ARGMAX || kind == EPI_LSE; }
 
 struct Epi {
   int kind;
@@ -71,8 +73,11 @@ struct Epi {
   int q_cols, kv_cols, kv_rows;
   int embed_rows;
   float* logits;         // argmax: optional [M, N]
-  float* part_val;       // argmax: [P, M] partial maxima
+  float* part_val;       // argmax: [P, M] partial maxima; lse: partial maxima m
   int32_t* part_idx;     // argmax: [P, M] their indices
+  float* part_sum;       // lse: [P, M] partial sums of exp(y - m)
+  const int32_t* targets;  // lse: [M] target feature per row (< 0: none)
+  float* tgt_logit;      // lse: [M] y of the target feature (written by the one tile that holds it)
 };
 
 // RMSNorm applied to the activation rows on their way into a contraction
@@ -114,8 +119,8 @@ void launch_pack(const void* src, void* dst, int N, int row_bytes, hipStream_t s
 // W (and W2) are packed weights.  A requested RMSNorm (p.nrm.gain) is fused
 // into the activation staging of the streaming kernels when the rows fit in
 // LDS; otherwise rmsnorm_rows_kernel writes p.nrm.tmp first.
-// EPI_ARGMAX returns the number of partial rows P to reduce with
-// launch_argmax_reduce; every other kind returns 0.
+// EPI_ARGMAX (EPI_LSE) returns the number of partial rows P to reduce with
+// launch_argmax_reduce (launch_lse_reduce); every other kind returns 0.
 int launch_gemm(const GemmParams& p, int bf16, hipStream_t s);
 // Upper bound of P for an argmax GEMM of this shape.
 int gemm_argmax_partials(int M, int N);
@@ -133,6 +138,11 @@ int64_t gemm_split_bytes(int T, int nmax);
 int gemm_big_partials(int N);
 
 void launch_argmax_reduce(const float* pv, const int32_t* pi, int P, int M, int32_t* tokens, hipStream_t s);
+// lse[m] = log sum_v exp(y[m][v]) from the P partials of EPI_LSE, and
+// loss[m] = lse[m] - tgt[m] (0 where targets[m] is outside [0, N)); lse or
+// loss may be null.
+void launch_lse_reduce(const float* pv, const float* ps, int P, int M, int N, const int32_t* targets,
+                       const float* tgt, float* lse, float* loss, hipStream_t s);
 
 struct AttnParams {
   const void* q;

@@ -341,6 +341,28 @@ pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weight
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 pe_status pe_lm_head_argmax_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes);
 
+/*
+ * pe_lm_head_loss - the LM head's log-sum-exp and cross-entropy without the
+ * logits.
+ *
+ * "[RFC]: Add random anchor for p-eagle first position", section "Separate
+ * Ablation: StreamingLLM & The 32K Wall": at long sequences the logits tensor
+ * ([T, V], 9.4 GiB per sample at 32K x 151K in bf16), not attention, runs out
+ * of memory.  Here the logits are reduced tile by tile as they are produced.
+ * For each of the n rows of x [n, hidden] f32:
+ *   z = w_lm RMSNorm(x, final_gain);  lse[i] = log sum_v exp(z_v);
+ *   loss[i] = lse[i] - z[targets[i]]  (0 where targets[i] is outside [0, vocab))
+ * targets [n] int32 device (required with loss), lse and loss [n] f32
+ * device, either may be NULL but not both.  Results do not depend on timing:
+ * partial sums are merged in a fixed order.  Uses weights->final_gain and
+ * w_lm.  Workspace: pe_lm_head_loss_workspace (256-byte aligned).
+ */
+pe_status pe_lm_head_loss(const pe_drafter_dims* dims, const pe_drafter_weights* weights,
+                          int32_t n, const float* x, const int32_t* targets, float* lse,
+                          float* loss, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+pe_status pe_lm_head_loss_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -89,6 +89,14 @@ def test_entry_points_reject_before_launch():
     # empty inputs are valid no-ops
     assert lib.pe_fuse_hidden(ctypes.byref(d), ctypes.byref(w), 0, None, None, None, None, None, 0, None) == 0
     assert lib.pe_lm_head_argmax(ctypes.byref(d), ctypes.byref(w), 0, None, None, None, None, 0, None) == 0
+    # lm head loss: neither output, a loss without targets, workspace too small; empty is a no-op
+    big = 1 << 40
+    assert lib.pe_lm_head_loss(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, FAKE, None, None, FAKE, big, None) == 1
+    assert lib.pe_lm_head_loss(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, None, None, FAKE, FAKE, big, None) == 1
+    assert lib.pe_lm_head_loss(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 1
+    assert lib.pe_lm_head_loss(ctypes.byref(d), ctypes.byref(w), 0, None, None, None, None, None, 0, None) == 0
+    n = ctypes.c_size_t()
+    assert lib.pe_lm_head_loss_workspace(ctypes.byref(d), 7, ctypes.byref(n)) == 0 and n.value > 0
 
 
 def test_attention_validation_and_workspace():
