@@ -132,6 +132,48 @@ def attention(q, k, v, start, depth, queries=None, scale=None, q_by_query=False,
     return out, lse
 
 
+def attention_backward(q, k, v, start, depth, dout, queries=None, scale=None):
+    """Gradients of L = sum_t <out[t], dout[t]> for the queries listed (all rows
+    by default), the attention of attention() with the same predicate.
+
+    [PD] "Training on long sequences": the sequence partition keeps every
+    attention dependency across chunk boundaries, so a chunk of queries
+    contributes to the key and value gradients of rows in earlier chunks.
+    Per query t and head, with p = softmax(s), s = scale q.k over its visible
+    keys, o = sum p v:
+      dP = dout . v;  dS = p * (dP - sum(p dP));
+      dq = scale * sum dS k;  dk[j] += scale * dS_j q;  dv[j] += p_j dout.
+    q [T,Hq,Dh], k/v [T,Hkv,Dh], dout [nq,Hq,Dh] in query order (float64).
+    Returns (dq [nq,Hq,Dh], dk [T,Hkv,Dh], dv [T,Hkv,Dh]); dk and dv hold
+    only the listed queries' contributions.
+    """
+    T, Hq, Dh = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    if queries is None:
+        queries = np.arange(T)
+    dq = np.zeros((len(queries), Hq, Dh))
+    dk = np.zeros((T, Hkv, Dh))
+    dv = np.zeros((T, Hkv, Dh))
+    for n, t in enumerate(queries):
+        keys = np.nonzero(visible(start[t], depth[t], start, depth))[0]
+        for h in range(Hq):
+            kh = h // G
+            Ks = k[keys, kh]
+            Vs = v[keys, kh]
+            sc = (Ks @ q[t, h]) * scale
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            dp = Vs @ dout[n, h]
+            ds = p * (dp - np.dot(p, dp))
+            dq[n, h] = scale * (ds @ Ks)
+            dk[keys, kh] += scale * np.outer(ds, q[t, h])
+            dv[keys, kh] += np.outer(p, dout[n, h])
+    return dq, dk, dv
+
+
 def attention_chunked(q, k, v, start, depth, chunk_rows, scale=None):
     """The same attention, queries taken chunk by chunk of ``chunk_rows`` rows.
 

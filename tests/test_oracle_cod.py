@@ -19,6 +19,9 @@
 * StreamingLLM window: a hand-worked example, the per-query count in closed
   form, reduction to the plain predicate when the window spans the
   sequence, one depth against SDPA with a banded-plus-sink mask.
+* Backward: fp64 torch autograd through SDPA with the dense mask, central
+  finite differences, and query chunks whose key/value gradients sum to the
+  unchunked ones.
 """
 import itertools
 
@@ -344,3 +347,76 @@ def test_window_single_depth_is_banded_sdpa():
         torch.from_numpy(q).permute(1, 0, 2)[None], torch.from_numpy(k).permute(1, 0, 2)[None],
         torch.from_numpy(v).permute(1, 0, 2)[None], attn_mask=mask[None, None], enable_gqa=True)
     np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ---- attention backward (the training side of the sequence partition)
+
+def _grads_torch(q, k, v, start, depth, dout):
+    """fp64 autograd through SDPA with the dense boolean mask of the predicate."""
+    T = q.shape[0]
+    M = np.zeros((T, T), bool)
+    for t in range(T):
+        M[t] = oc.visible(start[t], depth[t], start, depth)
+    qt, kt, vt = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    o = F.scaled_dot_product_attention(qt.permute(1, 0, 2)[None], kt.permute(1, 0, 2)[None],
+                                       vt.permute(1, 0, 2)[None], attn_mask=torch.from_numpy(M)[None, None],
+                                       enable_gqa=True)[0].permute(1, 0, 2)
+    (o * torch.from_numpy(dout)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def test_backward_matches_torch_autograd():
+    L = _layout(21, 4, 0.7, 0.6, 13)
+    T = L["T"]
+    g = np.random.default_rng(14)
+    q = g.standard_normal((T, 4, 8))
+    k = g.standard_normal((T, 2, 8))
+    v = g.standard_normal((T, 2, 8))
+    dout = g.standard_normal((T, 4, 8))
+    dq, dk, dv = oc.attention_backward(q, k, v, L["start"], L["depth"], dout)
+    rq, rk, rv = _grads_torch(q, k, v, L["start"], L["depth"], dout)
+    for a, b in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_backward_finite_differences():
+    L = _layout(9, 3, 0.8, 1.0, 2)
+    T = L["T"]
+    g = np.random.default_rng(15)
+    q = g.standard_normal((T, 2, 4))
+    k = g.standard_normal((T, 1, 4))
+    v = g.standard_normal((T, 1, 4))
+    dout = g.standard_normal((T, 2, 4))
+    dq, dk, dv = oc.attention_backward(q, k, v, L["start"], L["depth"], dout)
+    loss = lambda q_, k_, v_: float(np.sum(oc.attention(q_, k_, v_, L["start"], L["depth"])[0] * dout))
+    h = 1e-6
+    for arr, grad, idx in ((q, dq, (3, 1, 2)), (k, dk, (0, 0, 1)), (v, dv, (2, 0, 3)), (k, dk, (T - 1, 0, 0))):
+        a1 = arr.copy(); a1[idx] += h
+        a2 = arr.copy(); a2[idx] -= h
+        args1 = [q, k, v]; args2 = [q, k, v]
+        which = 0 if arr is q else (1 if arr is k else 2)
+        args1[which] = a1; args2[which] = a2
+        fd = (loss(*args1) - loss(*args2)) / (2 * h)
+        assert abs(fd - grad[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+
+
+def test_backward_query_chunks_accumulate():
+    # the key/value gradients of a chunked pass are the sums of the chunks'
+    # contributions; each chunk's dq is its rows of the unchunked dq
+    L = _layout(30, 4, 0.7, 1.0, 4)
+    T = L["T"]
+    g = np.random.default_rng(16)
+    q = g.standard_normal((T, 4, 8))
+    k = g.standard_normal((T, 2, 8))
+    v = g.standard_normal((T, 2, 8))
+    dout = g.standard_normal((T, 4, 8))
+    dq, dk, dv = oc.attention_backward(q, k, v, L["start"], L["depth"], dout)
+    dk2, dv2 = np.zeros_like(dk), np.zeros_like(dv)
+    for c0 in range(0, T, 17):
+        rows = np.arange(c0, min(T, c0 + 17))
+        a, b, c = oc.attention_backward(q, k, v, L["start"], L["depth"], dout[rows], rows)
+        np.testing.assert_allclose(a, dq[rows], rtol=1e-13, atol=1e-14)
+        dk2 += b
+        dv2 += c
+    np.testing.assert_allclose(dk2, dk, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv2, dv, rtol=1e-12, atol=1e-13)
