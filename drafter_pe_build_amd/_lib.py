@@ -51,6 +51,14 @@ class PeAttnArgs(ctypes.Structure):
                 ("dbg_count", c_void_p), ("dbg_hash", c_void_p), ("window_sink", c_int32), ("window_len", c_int32)]
 
 
+class PeAttnBwdArgs(ctypes.Structure):
+    _fields_ = [("num_rows", c_int32), ("n_pos", c_int32), ("n_groups", c_int32), ("n_q_heads", c_int32),
+                ("n_kv_heads", c_int32), ("head_dim", c_int32), ("scale", c_float), ("dtype", c_int),
+                ("group_off", c_void_p), ("start", c_void_p), ("depth", c_void_p), ("q", c_void_p),
+                ("k", c_void_p), ("v", c_void_p), ("out", c_void_p), ("dout", c_void_p), ("lse", c_void_p),
+                ("q_begin", c_int32), ("q_end", c_int32), ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p)]
+
+
 EXPORTS = {
     "pe_status_string": (c_char_p, [c_int]),
     "pe_version": (c_char_p, []),
@@ -73,6 +81,8 @@ EXPORTS = {
     "pe_lm_head_loss": (c_int, [POINTER(PeDims), POINTER(PeWeights), c_int32, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "pe_lm_head_loss_workspace": (c_int, [POINTER(PeDims), c_int32, POINTER(c_size_t)]),
+    "pe_draft_attention_backward": (c_int, [POINTER(PeAttnBwdArgs), c_void_p, c_size_t, c_void_p]),
+    "pe_draft_attention_backward_workspace": (c_int, [POINTER(PeAttnBwdArgs), POINTER(c_size_t)]),
 }
 
 _lib = None
@@ -195,6 +205,34 @@ def attn_args(**kw):
             setattr(a, name, v)
     a._refs = refs
     return a
+
+
+def attn_bwd_args(**kw):
+    """pe_attn_bwd_args from keyword values (tensors become device pointers)."""
+    a = PeAttnBwdArgs()
+    refs = []
+    for name, _ in PeAttnBwdArgs._fields_:
+        if name in kw:
+            v = kw[name]
+            if isinstance(v, torch.Tensor):
+                refs.append(v)
+                v = ptr(v)
+            setattr(a, name, v)
+    a._refs = refs
+    return a
+
+
+def pe_draft_attention_backward_workspace(args):
+    n = c_size_t()
+    _check("pe_draft_attention_backward_workspace",
+           lib().pe_draft_attention_backward_workspace(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def pe_draft_attention_backward(args, device, workspace=None, stream=None):
+    ws = _workspace(pe_draft_attention_backward_workspace(args), device, workspace)
+    _check("pe_draft_attention_backward", lib().pe_draft_attention_backward(
+        ctypes.byref(args), ptr(ws), ws.numel(), stream_handle(stream)))
 
 
 def pe_draft_attention_workspace(args):

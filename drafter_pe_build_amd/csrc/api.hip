@@ -270,6 +270,30 @@ bool ws_ok(void* ws, size_t have, size_t need) {
   return ws && have >= need && (reinterpret_cast<uintptr_t>(ws) & 255) == 0;
 }
 
+pe_status check_attn_bwd(const pe_attn_bwd_args* a) {
+  if (!a) return PE_ERR_INVALID_ARG;
+  if (a->dtype != PE_BF16) return a->dtype == PE_F32 ? PE_ERR_UNSUPPORTED : PE_ERR_INVALID_ARG;
+  if (a->num_rows <= 0 || a->n_pos <= 0 || a->n_pos > a->num_rows) return PE_ERR_INVALID_ARG;
+  if (a->n_groups < 1 || a->n_groups > 16) return PE_ERR_UNSUPPORTED;
+  if (a->n_q_heads <= 0 || a->n_kv_heads <= 0 || a->n_q_heads % a->n_kv_heads) return PE_ERR_INVALID_ARG;
+  const int G = a->n_q_heads / a->n_kv_heads;
+  if (G > 64 || 64 % G) return PE_ERR_UNSUPPORTED;
+  if (a->head_dim != 64 && a->head_dim != 128) return PE_ERR_UNSUPPORTED;
+  if (!(a->scale > 0.f) || !isfinite(a->scale)) return PE_ERR_INVALID_ARG;
+  if (a->q_begin < 0 || a->q_end < a->q_begin || a->q_end > a->num_rows) return PE_ERR_INVALID_ARG;
+  if ((int64_t)a->num_rows * a->n_q_heads * a->head_dim >= ((int64_t)1 << 31)) return PE_ERR_INVALID_ARG;
+  if (!a->group_off || !a->start || !a->depth || !a->lse) return PE_ERR_INVALID_ARG;
+  if (!a->q || !a->k || !a->v || !a->out || !a->dout) return PE_ERR_INVALID_ARG;
+  if (!al16(a->q) || !al16(a->k) || !al16(a->v) || !al16(a->out) || !al16(a->dout)) return PE_ERR_INVALID_ARG;
+  if (a->q_end > a->q_begin && (!a->dq || !a->dk || !a->dv || !al16(a->dq) || !al16(a->dk) || !al16(a->dv)))
+    return PE_ERR_INVALID_ARG;
+  return PE_OK;
+}
+
+size_t attn_bwd_ws_bytes(const pe_attn_bwd_args* a) {
+  return up256((size_t)(a->q_end - a->q_begin) * a->n_q_heads * 4) + 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -663,6 +687,46 @@ pe_status pe_lm_head_loss(const pe_drafter_dims* dims, const pe_drafter_weights*
   gp.epi.tgt_logit = lw.tgt;
   const int used = launch_gemm(gp, bf, stream);
   launch_lse_reduce(lw.pv, lw.ps, used, n, dims->vocab, targets, lw.tgt, lse, loss, stream);
+  return launched();
+}
+
+pe_status pe_draft_attention_backward_workspace(const pe_attn_bwd_args* args, size_t* bytes) {
+  pe_status st = check_attn_bwd(args);
+  if (st != PE_OK) return st;
+  if (!bytes) return PE_ERR_INVALID_ARG;
+  *bytes = attn_bwd_ws_bytes(args);
+  return PE_OK;
+}
+
+pe_status pe_draft_attention_backward(const pe_attn_bwd_args* a, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  pe_status st = check_attn_bwd(a);
+  if (st != PE_OK) return st;
+  if (a->q_end == a->q_begin) return PE_OK;
+  if (!ws_ok(workspace, workspace_bytes, attn_bwd_ws_bytes(a))) return PE_ERR_INVALID_ARG;
+  AttnBwdParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.out = a->out;
+  p.dout = a->dout;
+  p.lse = a->lse;
+  p.start = a->start;
+  p.depth = a->depth;
+  p.group_off = a->group_off;
+  p.T = a->num_rows;
+  p.N = a->n_pos;
+  p.D = a->n_groups;
+  p.Hq = a->n_q_heads;
+  p.Hkv = a->n_kv_heads;
+  p.q_begin = a->q_begin;
+  p.q_end = a->q_end;
+  p.scale = a->scale;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  p.delta = static_cast<float*>(workspace);
+  launch_attention_backward(p, a->head_dim, stream);
   return launched();
 }
 

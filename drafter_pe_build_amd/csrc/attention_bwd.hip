@@ -1,0 +1,438 @@
+// Backward of the parallel-draft / COD masked GQA attention on gfx950, for the
+// depth-major training layout, bf16 operands and f32 gradients.
+//
+// "P-EAGLE: parallel speculative decoding in vLLM", "Training on long
+// sequences": the sequence partition splits the N*K positions into chunks of
+// queries while every attention dependency across chunk boundaries is kept,
+// so a chunk's queries also produce key and value gradients for rows of
+// earlier chunks.  Here a call takes the queries [q_begin, q_end), writes
+// their dQ and adds their contributions to dK and dV of every row.
+//
+// With the forward's log-sum-exp, P = exp(s - lse) is recomputed exactly (no
+// running maximum), dP = dO . v, dS = P (dP - delta) with delta = rowsum(dO o O)
+// per (query, head), and
+//   dQ = scale dS K,  dK += scale dS^T Q,  dV += P^T dO.
+// Layout facts used to enumerate work (no mask tensor, no atomics):
+//   * group 0 holds the original positions (row = start); group e >= 1 the
+//     depth-e chain rows sorted by start, so in every group the rows with
+//     starts in an interval are contiguous;
+//   * a query (s, d) sees the group-0 rows with start <= s and the rows
+//     (s, e) for 1 <= e <= d.
+// dQ kernel: one workgroup = 128 (query, head) columns of one kv head (4
+// waves x 32), walking the key tiles its queries can see: group 0 up to the
+// largest start, and each deeper group's rows whose starts lie in the
+// queries' start range.  dK/dV kernel: one workgroup = 64 key rows of one
+// group and one kv head (a wave per 16 keys, K and V in registers), walking
+// the query tiles that can see them: for a group-0 tile the rows of every
+// group with start >= the tile's first start, for a chain tile the rows of
+// the groups at least as deep whose starts lie in the tile's start range.
+// Each workgroup owns its outputs, so results do not depend on timing.
+#include <math.h>
+#include "kernels.h"
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+namespace pe {
+
+namespace {
+
+constexpr int BKT = 64;    // keys per tile (dQ) / per workgroup (dK, dV)
+constexpr int BCOL = 128;  // (query, head) columns per tile
+constexpr int BMAXG = 16;  // groups a layout may have
+
+// First row in [lo, hi) whose start is >= s (rows sorted by start).
+__device__ int lower_row(const int32_t* start, int lo, int hi, int s) {
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (start[mid] < s) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+// First row in [lo, hi) whose start is > s.
+__device__ int upper_row(const int32_t* start, int lo, int hi, int s) {
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (start[mid] <= s) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Rows of group e, clamped into [0, T] (a malformed layout cannot send a
+// search or a load outside the arrays).
+__device__ __forceinline__ void group_rows(const AttnBwdParams& p, int e, int& g0, int& g1) {
+  g0 = min(max(p.group_off[e], 0), p.T);
+  g1 = min(max(p.group_off[e + 1], g0), p.T);
+}
+
+__device__ __forceinline__ bool sees(int qs, int qd, int ks, int kd) {
+  return kd == 0 ? ks <= qs : (kd >= 1 && ks == qs && kd <= qd);
+}
+
+__device__ __forceinline__ u32x4 tr_pair(const char* p, int pitch) {
+  typedef __attribute__((address_space(3))) short4_t lds_s4;
+  const auto lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+  const auto hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p + 16 * pitch));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
+  return u32x4{l2.x, l2.y, h2.x, h2.y};
+}
+
+}  // namespace
+
+// delta[i][h] = sum_d dO[q_begin + i][h][d] O[q_begin + i][h][d]; one wave per (query, head).
+template <int DH>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(AttnBwdParams p) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t nqh = (int64_t)(p.q_end - p.q_begin) * p.Hq;
+  if (w >= nqh) return;
+  const int64_t row = (int64_t)p.q_begin * p.Hq + w;  // (query, head) row of out / dout
+  const uint16_t* o = reinterpret_cast<const uint16_t*>(p.out) + row * DH;
+  const uint16_t* d = reinterpret_cast<const uint16_t*>(p.dout) + row * DH;
+  float acc = 0.f;
+  for (int i = lane; i < DH; i += 64) acc += bf2f(o[i]) * bf2f(d[i]);
+  acc = wave_sum(acc);
+  if (lane == 0) p.delta[w] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: columns (query, head) of one kv head; per key tile S^T = K Q^T and
+// dP^T = V dO^T (B operands in registers), dQ^T += K^T dS^T (K^T read
+// transposed from LDS, dS^T from the score registers).
+template <int DH>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, int G, int n_qtiles) {
+  constexpr int NST = DH / 32;                  // 32-dim contraction steps
+  constexpr int NMB = DH / 16;                  // 16-dim output blocks
+  constexpr int KP = DH * 2 + 16;               // K / V row pitch (row reads)
+  constexpr int TP = DH * 2 + 32;               // K row pitch of the transposed copy
+  constexpr int CB = 2;                         // 16-column blocks per wave
+  __shared__ __attribute__((aligned(16))) char Ks[BKT * KP];
+  __shared__ __attribute__((aligned(16))) char Kt[BKT * TP];
+  __shared__ __attribute__((aligned(16))) char Vs[BKT * KP];
+  __shared__ int s_ks[BKT], s_kd[BKT];
+  __shared__ int s_rng[2 * BMAXG], s_red[12];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int kvh = blockIdx.x % p.Hkv, qt = blockIdx.x / p.Hkv;
+  if (qt >= n_qtiles) return;
+  const int QPW = BCOL / G;
+  const int qa = p.q_begin + qt * QPW;
+  const int qb = min(qa + QPW, p.q_end);
+  const float sl2 = p.scale * 1.4426950408889634f;
+
+  // this lane's columns
+  int cqi[CB], ch[CB], cs[CB], cd[CB];
+  float clse2[CB], cdel[CB];
+  u32x4 qreg[CB][NST], dreg[CB][NST];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int col = wave * 32 + cb * 16 + r;
+    const int qi = qa + col / G;
+    const int h = kvh * G + col % G;
+    const bool act = qi < qb;
+    cqi[cb] = act ? qi : -1;
+    ch[cb] = h;
+    cs[cb] = act ? p.start[qi] : -1;
+    cd[cb] = act ? p.depth[qi] : -1;
+    clse2[cb] = act ? p.lse[(int64_t)qi * p.Hq + h] * 1.4426950408889634f : 0.f;
+    cdel[cb] = act ? p.delta[(int64_t)(qi - p.q_begin) * p.Hq + h] : 0.f;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)(act ? qi : 0) * p.Hq + h) * DH;
+    const uint16_t* drow = reinterpret_cast<const uint16_t*>(p.dout) + ((int64_t)(act ? qi : p.q_begin) * p.Hq + h) * DH;
+#pragma unroll
+    for (int t = 0; t < NST; ++t) {
+      qreg[cb][t] = act ? ld16(qrow + t * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+      dreg[cb][t] = act ? ld16(drow + t * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // key ranges: group 0 rows [0, max start], then per deeper group the rows
+  // whose starts lie in [min start, max start] of the tile's queries
+  int mn = 0x7fffffff, mx = -1, md = 0;
+  if (tid < QPW && qa + tid < qb) {
+    mn = p.start[qa + tid];
+    mx = mn;
+    md = p.depth[qa + tid];
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, __shfl_xor(mn, o, 64));
+    mx = max(mx, __shfl_xor(mx, o, 64));
+    md = max(md, __shfl_xor(md, o, 64));
+  }
+  if (lane == 0) { s_red[wave] = mn; s_red[4 + wave] = mx; s_red[8 + wave] = md; }
+  __syncthreads();
+  const int qs_min = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
+  const int qs_max = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
+  const int qd_max = min(max(max(s_red[8], s_red[9]), max(s_red[10], s_red[11])), p.D - 1);
+  if (tid < BMAXG) {
+    int a = 0, b = 0;
+    if (qs_max >= 0) {
+      if (tid == 0) { a = 0; b = min(qs_max + 1, p.N); }
+      else if (tid <= qd_max) {
+        int g0, g1;
+        group_rows(p, tid, g0, g1);
+        a = lower_row(p.start, g0, g1, qs_min);
+        b = upper_row(p.start, g0, g1, qs_max);
+      }
+    }
+    s_rng[2 * tid] = a;
+    s_rng[2 * tid + 1] = b;
+  }
+  __syncthreads();
+
+  f32x4 acc[CB][NMB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int i = 0; i < NMB; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t rstride = (int64_t)p.Hkv * DH;
+  for (int e = 0; e <= qd_max; ++e) {
+    const int ra = s_rng[2 * e], rb = s_rng[2 * e + 1];
+    for (int k0 = ra; k0 < rb; k0 += BKT) {
+      const int nk = min(BKT, rb - k0);
+      // stage K (row and transposed pitch) and V; rows past the range repeat row k0
+      for (int c = tid; c < BKT * (DH / 8); c += 256) {
+        const int key = c / (DH / 8), ck = c % (DH / 8);
+        const int64_t row = k0 + (key < nk ? key : 0);
+        const u32x4 kv = ld16(reinterpret_cast<const uint16_t*>(p.k) + row * rstride + kvh * DH + ck * 8);
+        const u32x4 vv = ld16(reinterpret_cast<const uint16_t*>(p.v) + row * rstride + kvh * DH + ck * 8);
+        *reinterpret_cast<u32x4*>(Ks + key * KP + ck * 16) = kv;
+        *reinterpret_cast<u32x4*>(Kt + key * TP + ck * 16) = kv;
+        *reinterpret_cast<u32x4*>(Vs + key * KP + ck * 16) = vv;
+      }
+      if (tid < BKT) {
+        s_ks[tid] = tid < nk ? p.start[k0 + tid] : -1;
+        s_kd[tid] = tid < nk ? p.depth[k0 + tid] : -1;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {  // halves of 32 keys
+        f32x4 sacc[CB][2], pacc[CB][2];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) sacc[cb][0] = sacc[cb][1] = pacc[cb][0] = pacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int t = 0; t < NST; ++t) {
+            const int kr = 16 * (2 * h2 + bb) + r;
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + kr * KP + (4 * t + g) * 16);
+            const u32x4 va = *reinterpret_cast<const u32x4*>(Vs + kr * KP + (4 * t + g) * 16);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+              mma16(sacc[cb][bb], ka, qreg[cb][t], uint16_t());
+              mma16(pacc[cb][bb], va, dreg[cb][t], uint16_t());
+            }
+          }
+        // dS^T = P^T (dP^T - delta), P from the forward's log-sum-exp; packed as the B operand
+        u32x4 bop[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          float ds[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int bb = i >> 2, j = i & 3;
+            const int kk = 16 * (2 * h2 + bb) + 4 * g + j;
+            const bool vis = sees(cs[cb], cd[cb], s_ks[kk], s_kd[kk]);
+            const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[cb][bb][j], sl2, -clse2[cb])) : 0.f;
+            ds[i] = pv * (pacc[cb][bb][j] - cdel[cb]);
+          }
+          bop[cb] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                          pack_bf16x2(ds[6], ds[7])};
+        }
+        // dQ^T += K^T dS^T: lane r receives dim 16 mb + r of keys 32 h2 + 4 g + c and + 16
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const u32x4 aop = tr_pair(Kt + (32 * h2 + 4 * g + (r >> 2)) * TP + (16 * mb + 4 * (r & 3)) * 2, TP);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) mma16(acc[cb][mb], aop, bop[cb], uint16_t());
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // dQ = scale dQ^T: lane (g, r) holds dims 16 mb + 4 g + j of its column
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    if (cqi[cb] < 0) continue;
+    float* dq = p.dq + ((int64_t)(cqi[cb] - p.q_begin) * p.Hq + ch[cb]) * DH;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      *reinterpret_cast<f32x4*>(dq + 16 * mb + 4 * g) = acc[cb][mb] * p.scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 64 key rows of one group (a wave per 16, K and V as B operands in
+// registers) against the query tiles that can see them; per tile
+// S' = Q K^T, dP' = dO V^T (A operands from LDS), then dV^T += dO^T P' and
+// dK^T += Q^T dS' (A operands read transposed from LDS).
+template <int DH>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, int G) {
+  constexpr int NST = DH / 32;
+  constexpr int NMB = DH / 16;
+  constexpr int PP = DH * 2 + 32;  // Q / dO row pitch (row reads and transposed reads)
+  constexpr int NCB = BCOL / 16;   // 16-column blocks of a query tile
+  __shared__ __attribute__((aligned(16))) char Qs[BCOL * PP];
+  __shared__ __attribute__((aligned(16))) char Ds[BCOL * PP];
+  __shared__ __attribute__((aligned(16))) float s_lse2[BCOL], s_del[BCOL];
+  __shared__ __attribute__((aligned(16))) int s_cs[BCOL], s_cd[BCOL];
+  __shared__ int s_rng[2 * BMAXG], s_tile[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int kvh = blockIdx.x % p.Hkv;
+  int t = blockIdx.x / p.Hkv;
+  // which group and which 64 rows of it
+  if (tid == 0) {
+    int e = 0, r0 = -1, r1 = -1;
+    for (; e < p.D; ++e) {
+      int g0, g1;
+      group_rows(p, e, g0, g1);
+      const int nt = (g1 - g0 + BKT - 1) / BKT;
+      if (t < nt) { r0 = g0 + t * BKT; r1 = min(r0 + BKT, g1); break; }
+      t -= nt;
+    }
+    s_tile[0] = e;
+    s_tile[1] = r0;
+    s_tile[2] = r1;
+  }
+  __syncthreads();
+  const int ke = s_tile[0], kr0 = s_tile[1], kr1 = s_tile[2];
+  if (kr0 < 0) return;
+  const int QPW = BCOL / G;
+  const float sl2 = p.scale * 1.4426950408889634f;
+  const int64_t rstride = (int64_t)p.Hkv * DH;
+
+  // this lane's key (row kr0 + 16 wave + r) and its K, V operands
+  const int key = kr0 + 16 * wave + r;
+  const bool kact = key < kr1;
+  const int krow = kact ? key : kr0;
+  const int ks = kact ? p.start[key] : -1;
+  const int kd = kact ? p.depth[key] : -1;
+  u32x4 kreg[NST], vreg[NST];
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+    kreg[s] = ld16(reinterpret_cast<const uint16_t*>(p.k) + (int64_t)krow * rstride + kvh * DH + s * 32 + g * 8);
+    vreg[s] = ld16(reinterpret_cast<const uint16_t*>(p.v) + (int64_t)krow * rstride + kvh * DH + s * 32 + g * 8);
+  }
+
+  // query ranges per group that can see these keys, within [q_begin, q_end)
+  if (tid < BMAXG) {
+    int a = 0, b = 0;
+    if (tid < p.D && tid >= ke) {
+      int g0, g1;
+      group_rows(p, tid, g0, g1);
+      const int s_lo = p.start[kr0], s_hi = p.start[kr1 - 1];
+      a = lower_row(p.start, g0, g1, s_lo);
+      b = ke == 0 ? g1 : upper_row(p.start, g0, g1, s_hi);
+      a = max(a, p.q_begin);
+      b = min(b, p.q_end);
+    }
+    s_rng[2 * tid] = a;
+    s_rng[2 * tid + 1] = max(a, b);
+  }
+  __syncthreads();
+
+  f32x4 dka[NMB], dva[NMB];
+#pragma unroll
+  for (int i = 0; i < NMB; ++i) dka[i] = dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int d = ke; d < p.D; ++d) {
+    const int qa0 = s_rng[2 * d], qb0 = s_rng[2 * d + 1];
+    for (int qa = qa0; qa < qb0; qa += QPW) {
+      const int qb = min(qa + QPW, qb0);
+      // stage the tile's columns: Q and dO rows, labels, lse and delta
+      for (int c = tid; c < BCOL * (DH / 8); c += 256) {
+        const int col = c / (DH / 8), ck = c % (DH / 8);
+        const int qi = qa + col / G, h = kvh * G + col % G;
+        u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
+        if (qi < qb) {
+          qv = ld16(reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)qi * p.Hq + h) * DH + ck * 8);
+          dv = ld16(reinterpret_cast<const uint16_t*>(p.dout) + ((int64_t)qi * p.Hq + h) * DH + ck * 8);
+        }
+        *reinterpret_cast<u32x4*>(Qs + col * PP + ck * 16) = qv;
+        *reinterpret_cast<u32x4*>(Ds + col * PP + ck * 16) = dv;
+      }
+      if (tid < BCOL) {
+        const int qi = qa + tid / G, h = kvh * G + tid % G;
+        const bool act = qi < qb;
+        s_cs[tid] = act ? p.start[qi] : -1;
+        s_cd[tid] = act ? p.depth[qi] : -1;
+        s_lse2[tid] = act ? p.lse[(int64_t)qi * p.Hq + h] * 1.4426950408889634f : 0.f;
+        s_del[tid] = act ? p.delta[(int64_t)(qi - p.q_begin) * p.Hq + h] : 0.f;
+      }
+      __syncthreads();
+      // S' and dP' of the 8 column blocks: element j of lane (g, r) is column 16 cb + 4 g + j, key r
+      f32x4 sacc[NCB], pacc[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) sacc[cb] = pacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int s = 0; s < NST; ++s) {
+          const u32x4 qa_op = *reinterpret_cast<const u32x4*>(Qs + (16 * cb + r) * PP + (4 * s + g) * 16);
+          const u32x4 da_op = *reinterpret_cast<const u32x4*>(Ds + (16 * cb + r) * PP + (4 * s + g) * 16);
+          mma16(sacc[cb], qa_op, kreg[s], uint16_t());
+          mma16(pacc[cb], da_op, vreg[s], uint16_t());
+        }
+      // P' and dS' packed per 32-column step as B operands (columns 32 s + 4 g + j, then + 16)
+#pragma unroll
+      for (int s = 0; s < NCB / 2; ++s) {
+        float pv[8], ds[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int cb = 2 * s + (i >> 2), j = i & 3;
+          const int col = 16 * cb + 4 * g + j;
+          const bool vis = sees(s_cs[col], s_cd[col], ks, kd);
+          pv[i] = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[cb][j], sl2, -s_lse2[col])) : 0.f;
+          ds[i] = pv[i] * (pacc[cb][j] - s_del[col]);
+        }
+        const u32x4 pb = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                          pack_bf16x2(pv[6], pv[7])};
+        const u32x4 sb = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                          pack_bf16x2(ds[6], ds[7])};
+        // lane r receives dim 16 mb + r of columns 32 s + 4 g + c and + 16
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int off = (32 * s + 4 * g + (r >> 2)) * PP + (16 * mb + 4 * (r & 3)) * 2;
+          mma16(dva[mb], tr_pair(Ds + off, PP), pb, uint16_t());
+          mma16(dka[mb], tr_pair(Qs + off, PP), sb, uint16_t());
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // dK += scale dK^T, dV += dV^T: lane (g, r) holds dims 16 mb + 4 g + j of its key
+  if (kact) {
+    float* dk = p.dk + ((int64_t)key * p.Hkv + kvh) * DH;
+    float* dv = p.dv + ((int64_t)key * p.Hkv + kvh) * DH;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      f32x4* pk = reinterpret_cast<f32x4*>(dk + 16 * mb + 4 * g);
+      f32x4* pv = reinterpret_cast<f32x4*>(dv + 16 * mb + 4 * g);
+      *pk = *pk + dka[mb] * p.scale;
+      *pv = *pv + dva[mb];
+    }
+  }
+}
+
+template <int DH>
+static void launch_bwd_t(const AttnBwdParams& p, hipStream_t s) {
+  const int G = p.Hq / p.Hkv;
+  const int QPW = BCOL / G;
+  const int nq = p.q_end - p.q_begin;
+  if (nq <= 0) return;
+  const int64_t nqh = (int64_t)nq * p.Hq;
+  hipLaunchKernelGGL(attn_bwd_delta_kernel<DH>, dim3((unsigned)((nqh + 3) / 4)), dim3(256), 0, s, p);
+  const int n_qtiles = (nq + QPW - 1) / QPW;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<DH>, dim3((unsigned)(n_qtiles * p.Hkv)), dim3(256), 0, s, p, G, n_qtiles);
+  // key tiles: ceil(group size / 64) per group, at most ceil(T / 64) + D in all
+  const int n_ktiles = (p.T + BKT - 1) / BKT + p.D;
+  hipLaunchKernelGGL(attn_bwd_dkv_kernel<DH>, dim3((unsigned)(n_ktiles * p.Hkv)), dim3(256), 0, s, p, G);
+}
+
+void launch_attention_backward(const AttnBwdParams& p, int head_dim, hipStream_t s) {
+  if (head_dim == 64) launch_bwd_t<64>(p, s); else launch_bwd_t<128>(p, s);
+}
+
+}  // namespace pe

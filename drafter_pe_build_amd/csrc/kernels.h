@@ -164,6 +164,21 @@ struct AttnParams {
   int win_sink, win_len;  // StreamingLLM window over the prefix keys (win_len 0: none; never split)
 };
 void launch_attention(const AttnParams& p, int bf16, int head_dim, hipStream_t s);
+
+// Backward of the COD attention over the depth-major training layout (bf16
+// operands, f32 gradients): dq of the queries [q_begin, q_end), their dk and
+// dv contributions added to every row (attention_bwd.hip).
+struct AttnBwdParams {
+  const void *q, *k, *v, *out, *dout;     // bf16: q, out, dout [T, Hq, Dh]; k, v [T, Hkv, Dh]
+  const float* lse;                       // [T, Hq] natural-log sum-exp of the forward
+  const int32_t *start, *depth, *group_off;  // [T], [T], [D + 1]
+  int T, N, D, Hq, Hkv, q_begin, q_end;
+  float scale;
+  float* dq;                              // [q_end - q_begin, Hq, Dh]
+  float *dk, *dv;                         // [T, Hkv, Dh], accumulated
+  float* delta;                           // workspace [q_end - q_begin, Hq]
+};
+void launch_attention_backward(const AttnBwdParams& p, int head_dim, hipStream_t s);
 // Queries one attention workgroup takes: 128 (query, head) columns of one kv
 // head, i.e. 128 / (n_q_heads / n_kv_heads) queries.
 int attn_queries_per_workgroup(int G, int head_dim);

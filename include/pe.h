@@ -297,6 +297,55 @@ pe_status pe_draft_attention(const pe_attn_args* args, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 pe_status pe_draft_attention_workspace(const pe_attn_args* args, size_t* bytes);
 
+/* Arguments of pe_draft_attention_backward: the depth-major COD training
+ * layout of pe_draft_attention with every row a query (one segment,
+ * seg_kv_base 0): rows 0..n_pos-1 are the original positions (start = row,
+ * depth 0); group e (rows group_off[e]..group_off[e+1]-1, 1 <= e < n_groups)
+ * holds the depth-e chain rows sorted by start.  Row (s, d) sees the rows
+ * (j, 0) with j <= s and (s, e) with 1 <= e <= d.                           */
+typedef struct {
+    int32_t num_rows;       /* T                                             */
+    int32_t n_pos;          /* N = group_off[1]                              */
+    int32_t n_groups;       /* 1..16                                         */
+    int32_t n_q_heads, n_kv_heads, head_dim;   /* head_dim 64 or 128          */
+    float scale;
+    pe_dtype dtype;         /* PE_BF16                                       */
+    const int32_t* group_off;  /* [n_groups + 1] device                      */
+    const int32_t* start;      /* [T] device                                 */
+    const int32_t* depth;      /* [T] device                                 */
+    const void* q;          /* [T, Hq, Dh]                                   */
+    const void* k;          /* [T, Hkv, Dh]                                  */
+    const void* v;          /* [T, Hkv, Dh]                                  */
+    const void* out;        /* [T, Hq, Dh] forward output                    */
+    const void* dout;       /* [T, Hq, Dh] gradient of the output            */
+    const float* lse;       /* [T, Hq] forward natural-log sum-exp           */
+    int32_t q_begin, q_end; /* the query chunk [q_begin, q_end)              */
+    float* dq;              /* [q_end - q_begin, Hq, Dh] f32, written        */
+    float* dk;              /* [T, Hkv, Dh] f32, the chunk's part added      */
+    float* dv;              /* [T, Hkv, Dh] f32, the chunk's part added      */
+} pe_attn_bwd_args;
+
+/*
+ * pe_draft_attention_backward - gradients of the COD attention for a chunk of
+ * queries.
+ *
+ * "P-EAGLE: parallel speculative decoding in vLLM", section "Training on long
+ * sequences": the sequence partition trains chunk by chunk while keeping
+ * every attention dependency across chunk boundaries, so a chunk's queries
+ * contribute to the key and value gradients of earlier rows.  With
+ * P = exp(scale q.k - lse) over each query's visible rows:
+ *   dQ = scale dS K,  dK += scale dS^T Q,  dV += P^T dO,
+ *   dS = P (dO.v - rowsum(dO o O)).
+ * dq is written for the chunk's rows; dk and dv are accumulated (zero them
+ * before the first chunk of a pass); summed over chunks they equal one call
+ * over all rows up to rounding.  Each workgroup owns its outputs: results
+ * do not depend on timing.  Alignment: every tensor 16 bytes.
+ * Workspace: pe_draft_attention_backward_workspace (256-byte aligned).
+ */
+pe_status pe_draft_attention_backward(const pe_attn_bwd_args* args, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+pe_status pe_draft_attention_backward_workspace(const pe_attn_bwd_args* args, size_t* bytes);
+
 /*
  * pe_draft_layer - stage 3, one pre-norm decoder layer of the drafter.
  *

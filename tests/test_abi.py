@@ -125,6 +125,16 @@ def test_attention_validation_and_workspace():
                      (dict(window_sink=4, window_len=64, split_len=128), 2)):
         a3 = L.attn_args(**{**base, **kw})
         assert lib.pe_draft_attention(ctypes.byref(a3), None, 0, None) == code, kw
+    # backward: bad chunk bounds, f32, missing gradient buffers, too many groups
+    bw = dict(num_rows=100, n_pos=60, n_groups=3, n_q_heads=8, n_kv_heads=2, head_dim=128, scale=0.088,
+              dtype=L.PE_BF16, group_off=FAKE, start=FAKE, depth=FAKE, q=FAKE, k=FAKE, v=FAKE, out=FAKE,
+              dout=FAKE, lse=FAKE, q_begin=0, q_end=100, dq=FAKE, dk=FAKE, dv=FAKE)
+    for kw, code in ((dict(q_end=101), 1), (dict(q_begin=5, q_end=4), 1), (dict(dtype=L.PE_F32), 2),
+                     (dict(dk=None), 1), (dict(n_groups=17), 2), (dict(q=None), 1), (dict(head_dim=96), 2)):
+        b3 = L.attn_bwd_args(**{**bw, **kw})
+        assert lib.pe_draft_attention_backward(ctypes.byref(b3), FAKE, 1 << 20, None) == code, kw
+    assert lib.pe_draft_attention_backward(ctypes.byref(L.attn_bwd_args(**{**bw, "q_begin": 7, "q_end": 7})),
+                                           None, 0, None) == 0
     a4 = L.attn_args(**{**base, "window_sink": 256, "window_len": 2048})
     assert lib.pe_draft_attention_workspace(ctypes.byref(a4), ctypes.byref(n)) == 0
     assert n.value == 16
