@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--attention-only", type=int, choices=(3, 4, 5, 6), default=0,
                     help="time only the COD (3), parallel-group (4), random-anchor (5) or windowed "
                          "parallel-group (6) attention workload and print its line")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the COD attention backward (N=4096 layout) and print its line")
     ap.add_argument("--loss-only", action="store_true",
                     help="time only the fused LM-head loss on a training-sized batch and print its line")
     ap.add_argument("--decode64-only", action="store_true",
@@ -210,6 +212,53 @@ def measure_anchor(steps, stream):
             "mfma_frac": fl / (msa * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "launches": 1}
 
 
+def measure_backward(steps, stream):
+    """COD attention backward over the N=4096 training layout (one call over
+    all queries): delta, dQ and dK/dV kernels.  Algorithmic work: 10 Hq Dh
+    flops per visible pair (recomputed scores, dP, dV, dQ, dK)."""
+    import numpy as np
+    import torch
+    from drafter_pe_build_amd import _lib as L
+    from drafter_pe_build_amd.step import to_device
+    from synth import inputs as si
+    log("COD attention backward N=4096")
+    Lay = si.cod_config(3)
+    T = Lay["T"]
+    Hq, Hkv, Dh = Lay["heads"]
+    q, k, v = (to_device(Lay[n], "cuda") for n in ("q", "k", "v"))
+    start = to_device(Lay["start"].astype(np.int32), "cuda")
+    depth = to_device(Lay["depth"].astype(np.int32), "cuda")
+    parent = to_device(Lay["parent"].astype(np.int32), "cuda")
+    goff = to_device(Lay["group_off"].astype(np.int32), "cuda")
+    selfr = to_device(np.arange(T, dtype=np.int32), "cuda")
+    base = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, Hq, Dh), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    fa = L.attn_args(num_q=T, num_seg=1, q_per_seg=T, num_kv_rows=T, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=Dh,
+                     scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16, q=q, q_row_stride=Hq * Dh, k=k, v=v,
+                     seg_kv_base=base, q_start=start, q_depth=depth, q_self_row=selfr, kv_parent=parent,
+                     max_prefix=Lay["N"], out=out, lse=lse)
+    L.pe_draft_attention(fa, "cuda")
+    dout = torch.randn((T, Hq, Dh), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    dq = torch.empty((T, Hq, Dh), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((T, Hkv, Dh), dtype=torch.float32, device="cuda")
+    dv = torch.zeros((T, Hkv, Dh), dtype=torch.float32, device="cuda")
+    ba = L.attn_bwd_args(num_rows=T, n_pos=Lay["N"], n_groups=len(Lay["group_off"]) - 1, n_q_heads=Hq,
+                         n_kv_heads=Hkv, head_dim=Dh, scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16, group_off=goff,
+                         start=start, depth=depth, q=q, k=k, v=v, out=out, dout=dout, lse=lse, q_begin=0,
+                         q_end=T, dq=dq, dk=dk, dv=dv)
+    ws = torch.empty(L.pe_draft_attention_backward_workspace(ba), dtype=torch.uint8, device="cuda")
+    ms = time_sustained(lambda: L.pe_draft_attention_backward(ba, "cuda", workspace=ws), steps, stream)
+    pairs = int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
+    fl = pairs * Hq * 10 * Dh
+    log("  %.1f us, %.0f TFLOP/s" % (ms * 1e3, fl / (ms * 1e-3) / 1e12))
+    del q, k, v, out, dout, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {"T": T, "ms": ms, "positions_per_s": T / (ms * 1e-3), "visible_pairs": pairs,
+            "tflops": fl / (ms * 1e-3) / 1e12, "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "launches": 3}
+
+
 def measure_loss(dims, steps, stream, W=None):
     """LM-head log-sum-exp + cross-entropy over a training-sized batch (the
     COD N=4096 layout's 7,794 rows) without materialising the logits."""
@@ -295,6 +344,11 @@ def main():
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
         return
     dims = si.GPTOSS_DIMS
+    if args.backward_only:
+        r = measure_backward(args.steps, stream)
+        print(json.dumps({"metric": "cod_attention_backward_n4096", "value": r["tflops"], "unit": "TFLOP/s",
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
+        return
     if args.loss_only:
         r = measure_loss(dims, args.steps, stream)
         print(json.dumps({"metric": "lm_head_loss_rows_per_s", "value": r["rows_per_s"], "unit": "rows/s",
@@ -383,6 +437,7 @@ def main():
         extra["anchor_attention_n8192"] = measure_anchor(max(5, args.steps // 5), stream)
         extra["window_attention_n8192_chunked"] = measure_attention(6, max(5, args.steps // 5), stream)
         extra["lm_head_loss_7794_rows"] = measure_loss(dims, max(5, args.steps // 5), stream, W)
+        extra["cod_attention_backward_n4096"] = measure_backward(max(5, args.steps // 5), stream)
         result["secondary"] = extra
 
     if not args.no_cpu:
