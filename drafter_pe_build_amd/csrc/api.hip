@@ -291,7 +291,8 @@ pe_status check_attn_bwd(const pe_attn_bwd_args* a) {
 }
 
 size_t attn_bwd_ws_bytes(const pe_attn_bwd_args* a) {
-  return up256((size_t)(a->q_end - a->q_begin) * a->n_q_heads * 4) + 256;
+  const size_t part = up256((size_t)attn_bwd_part_floats(a->num_rows, a->n_groups, a->n_kv_heads, a->head_dim) * 4);
+  return up256((size_t)(a->q_end - a->q_begin) * a->n_q_heads * 4) + 2 * part + 256;
 }
 
 }  // namespace
@@ -725,7 +726,11 @@ pe_status pe_draft_attention_backward(const pe_attn_bwd_args* a, void* workspace
   p.dq = a->dq;
   p.dk = a->dk;
   p.dv = a->dv;
-  p.delta = static_cast<float*>(workspace);
+  Carver c(workspace);
+  p.delta = static_cast<float*>(c.take((size_t)(a->q_end - a->q_begin) * a->n_q_heads * 4));
+  const size_t part = (size_t)attn_bwd_part_floats(a->num_rows, a->n_groups, a->n_kv_heads, a->head_dim) * 4;
+  p.part_k = static_cast<float*>(c.take(part));
+  p.part_v = static_cast<float*>(c.take(part));
   launch_attention_backward(p, a->head_dim, stream);
   return launched();
 }

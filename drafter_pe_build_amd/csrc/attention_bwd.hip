@@ -25,8 +25,11 @@
 // group and one kv head (a wave per 16 keys, K and V in registers), walking
 // the query tiles that can see them: for a group-0 tile the rows of every
 // group with start >= the tile's first start, for a chain tile the rows of
-// the groups at least as deep whose starts lie in the tile's start range.
-// Each workgroup owns its outputs, so results do not depend on timing.
+// the groups at least as deep whose starts lie in the tile's start range;
+// the query tiles are shared out over BSPL workgroups (the first key tiles
+// are seen by every query), whose partial sums a reduce kernel adds in a
+// fixed order.  Each workgroup owns its outputs, so results do not depend on
+// timing.
 #include <math.h>
 #include "kernels.h"
 
@@ -39,6 +42,7 @@ namespace {
 constexpr int BKT = 64;    // keys per tile (dQ) / per workgroup (dK, dV)
 constexpr int BCOL = 128;  // (query, head) columns per tile
 constexpr int BMAXG = 16;  // groups a layout may have
+constexpr int BSPL = 4;    // dK/dV workgroups per key tile, each a share of its query tiles
 
 // First row in [lo, hi) whose start is >= s (rows sorted by start).
 __device__ int lower_row(const int32_t* start, int lo, int hi, int s) {
@@ -276,12 +280,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
   __shared__ __attribute__((aligned(16))) char Ds[BCOL * PP];
   __shared__ __attribute__((aligned(16))) float s_lse2[BCOL], s_del[BCOL];
   __shared__ __attribute__((aligned(16))) int s_cs[BCOL], s_cd[BCOL];
-  __shared__ int s_rng[2 * BMAXG], s_tile[4];
+  __shared__ int s_rng[2 * BMAXG], s_tile[4], s_tpre[BMAXG + 1], s_piece[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int kvh = blockIdx.x % p.Hkv;
-  int t = blockIdx.x / p.Hkv;
+  const int piece = (blockIdx.x / p.Hkv) % BSPL;
+  const int kt = blockIdx.x / p.Hkv / BSPL;  // flat key-tile index over the groups
+  int t = kt;
   // which group and which 64 rows of it
   if (tid == 0) {
     int e = 0, r0 = -1, r1 = -1;
@@ -332,6 +338,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
     s_rng[2 * tid + 1] = max(a, b);
   }
   __syncthreads();
+  // this workgroup's share of the key tile's query tiles (in group order)
+  if (tid == 0) {
+    int tot = 0;
+    for (int d = 0; d < BMAXG; ++d) {
+      s_tpre[d] = tot;
+      tot += (s_rng[2 * d + 1] - s_rng[2 * d] + QPW - 1) / QPW;
+    }
+    s_tpre[BMAXG] = tot;
+    s_piece[0] = (int)((int64_t)tot * piece / BSPL);
+    s_piece[1] = (int)((int64_t)tot * (piece + 1) / BSPL);
+  }
+  __syncthreads();
+  const int tlo = s_piece[0], thi = s_piece[1];
 
   f32x4 dka[NMB], dva[NMB];
 #pragma unroll
@@ -339,7 +358,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
 
   for (int d = ke; d < p.D; ++d) {
     const int qa0 = s_rng[2 * d], qb0 = s_rng[2 * d + 1];
-    for (int qa = qa0; qa < qb0; qa += QPW) {
+    for (int i = 0, qa = qa0; qa < qb0; ++i, qa += QPW) {
+      if (s_tpre[d] + i < tlo) continue;
+      if (s_tpre[d] + i >= thi) break;
       const int qb = min(qa + QPW, qb0);
       // stage the tile's columns: Q and dO rows, labels, lse and delta
       for (int c = tid; c < BCOL * (DH / 8); c += 256) {
@@ -402,18 +423,51 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
       __syncthreads();
     }
   }
-  // dK += scale dK^T, dV += dV^T: lane (g, r) holds dims 16 mb + 4 g + j of its key
+  // this share's partial dK = scale dK^T and dV = dV^T (lane (g, r) holds dims
+  // 16 mb + 4 g + j of its key), summed into dk, dv by attn_bwd_dkv_reduce_kernel
   if (kact) {
-    float* dk = p.dk + ((int64_t)key * p.Hkv + kvh) * DH;
-    float* dv = p.dv + ((int64_t)key * p.Hkv + kvh) * DH;
+    const int64_t base = (((int64_t)kt * p.Hkv + kvh) * BSPL + piece) * BKT * DH + (int64_t)(16 * wave + r) * DH;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
-      f32x4* pk = reinterpret_cast<f32x4*>(dk + 16 * mb + 4 * g);
-      f32x4* pv = reinterpret_cast<f32x4*>(dv + 16 * mb + 4 * g);
-      *pk = *pk + dka[mb] * p.scale;
-      *pv = *pv + dva[mb];
+      *reinterpret_cast<f32x4*>(p.part_k + base + 16 * mb + 4 * g) = dka[mb] * p.scale;
+      *reinterpret_cast<f32x4*>(p.part_v + base + 16 * mb + 4 * g) = dva[mb];
     }
   }
+}
+
+// dk[j] += sum of the BSPL shares of row j's key tile, in share order; one
+// thread per 4 dims of one (row, kv head).
+template <int DH>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_reduce_kernel(AttnBwdParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)p.T * p.Hkv * (DH / 4)) return;
+  const int c4 = (int)(i % (DH / 4));
+  const int64_t rh = i / (DH / 4);
+  const int h = (int)(rh % p.Hkv);
+  const int j = (int)(rh / p.Hkv);
+  int kt = 0, e = 0, g0 = 0, g1 = 0;
+  for (; e < p.D; ++e) {
+    group_rows(p, e, g0, g1);
+    if (j < g1) break;
+    kt += (g1 - g0 + BKT - 1) / BKT;
+  }
+  if (e == p.D || j < g0) return;  // not a row of any group
+  kt += (j - g0) / BKT;
+  const int kl = (j - g0) % BKT;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int pc = 0; pc < BSPL; ++pc) {
+    const int64_t b = (((int64_t)kt * p.Hkv + h) * BSPL + pc) * BKT * DH + (int64_t)kl * DH + 4 * c4;
+    sk += *reinterpret_cast<const f32x4*>(p.part_k + b);
+    sv += *reinterpret_cast<const f32x4*>(p.part_v + b);
+  }
+  f32x4* pk = reinterpret_cast<f32x4*>(p.dk + ((int64_t)j * p.Hkv + h) * DH + 4 * c4);
+  f32x4* pv = reinterpret_cast<f32x4*>(p.dv + ((int64_t)j * p.Hkv + h) * DH + 4 * c4);
+  *pk = *pk + sk;
+  *pv = *pv + sv;
+}
+
+int64_t attn_bwd_part_floats(int T, int D, int Hkv, int head_dim) {
+  return ((int64_t)(T + BKT - 1) / BKT + D) * Hkv * BSPL * BKT * head_dim;
 }
 
 template <int DH>
@@ -428,7 +482,9 @@ static void launch_bwd_t(const AttnBwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL(attn_bwd_dq_kernel<DH>, dim3((unsigned)(n_qtiles * p.Hkv)), dim3(256), 0, s, p, G, n_qtiles);
   // key tiles: ceil(group size / 64) per group, at most ceil(T / 64) + D in all
   const int n_ktiles = (p.T + BKT - 1) / BKT + p.D;
-  hipLaunchKernelGGL(attn_bwd_dkv_kernel<DH>, dim3((unsigned)(n_ktiles * p.Hkv)), dim3(256), 0, s, p, G);
+  hipLaunchKernelGGL(attn_bwd_dkv_kernel<DH>, dim3((unsigned)(n_ktiles * p.Hkv * BSPL)), dim3(256), 0, s, p, G);
+  const int64_t nr = (int64_t)p.T * p.Hkv * (DH / 4);
+  hipLaunchKernelGGL(attn_bwd_dkv_reduce_kernel<DH>, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, s, p);
 }
 
 void launch_attention_backward(const AttnBwdParams& p, int head_dim, hipStream_t s) {

@@ -177,8 +177,10 @@ struct AttnBwdParams {
   float* dq;                              // [q_end - q_begin, Hq, Dh]
   float *dk, *dv;                         // [T, Hkv, Dh], accumulated
   float* delta;                           // workspace [q_end - q_begin, Hq]
+  float *part_k, *part_v;                 // workspace: attn_bwd_part_floats each (shares of dK, dV)
 };
 void launch_attention_backward(const AttnBwdParams& p, int head_dim, hipStream_t s);
+int64_t attn_bwd_part_floats(int T, int D, int Hkv, int head_dim);
 // Queries one attention workgroup takes: 128 (query, head) columns of one kv
 // head, i.e. 128 / (n_q_heads / n_kv_heads) queries.
 int attn_queries_per_workgroup(int G, int head_dim);
