@@ -40,7 +40,8 @@ namespace pe {
 namespace {
 
 constexpr int BKT = 64;    // keys per tile (dQ) / per workgroup (dK, dV)
-constexpr int BCOL = 128;  // (query, head) columns per tile
+constexpr int BCOL = 128;  // (query, head) columns per tile (dQ)
+constexpr int BCOLK = 64;  // (query, head) columns per tile (dK, dV)
 constexpr int BMAXG = 16;  // groups a layout may have
 constexpr int BSPL = 4;    // dK/dV workgroups per key tile, each a share of its query tiles
 
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
   __shared__ __attribute__((aligned(16))) char Kt[BKT * TP];
   __shared__ __attribute__((aligned(16))) char Vs[BKT * KP];
   __shared__ int s_ks[BKT], s_kd[BKT];
-  __shared__ int s_rng[2 * BMAXG], s_red[12];
+  __shared__ int s_rng[2 * BMAXG], s_red[12], s_tp[BMAXG + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -189,26 +190,64 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
 #pragma unroll
     for (int i = 0; i < NMB; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // the key tiles in one list: range e's tiles follow range e - 1's
+  if (tid == 0) {
+    int tot = 0;
+    for (int e = 0; e < BMAXG; ++e) {
+      s_tp[e] = tot;
+      if (e <= qd_max) tot += max(0, s_rng[2 * e + 1] - s_rng[2 * e] + BKT - 1) / BKT;
+    }
+    s_tp[BMAXG] = tot;
+  }
+  __syncthreads();
+  const int ntile = s_tp[BMAXG];
+  auto tile_at = [&](int tt, int& k0, int& nk) {
+    int e = 0;
+    while (e < qd_max && tt >= s_tp[e + 1]) ++e;
+    k0 = s_rng[2 * e] + (tt - s_tp[e]) * BKT;
+    nk = min(BKT, s_rng[2 * e + 1] - k0);
+  };
+  // the next tile's K, V and labels are loaded into registers while this one
+  // is multiplied; rows past a range repeat its first row (masked out)
   const int64_t rstride = (int64_t)p.Hkv * DH;
-  for (int e = 0; e <= qd_max; ++e) {
-    const int ra = s_rng[2 * e], rb = s_rng[2 * e + 1];
-    for (int k0 = ra; k0 < rb; k0 += BKT) {
-      const int nk = min(BKT, rb - k0);
-      // stage K (row and transposed pitch) and V; rows past the range repeat row k0
-      for (int c = tid; c < BKT * (DH / 8); c += 256) {
-        const int key = c / (DH / 8), ck = c % (DH / 8);
-        const int64_t row = k0 + (key < nk ? key : 0);
-        const u32x4 kv = ld16(reinterpret_cast<const uint16_t*>(p.k) + row * rstride + kvh * DH + ck * 8);
-        const u32x4 vv = ld16(reinterpret_cast<const uint16_t*>(p.v) + row * rstride + kvh * DH + ck * 8);
-        *reinterpret_cast<u32x4*>(Ks + key * KP + ck * 16) = kv;
-        *reinterpret_cast<u32x4*>(Kt + key * TP + ck * 16) = kv;
-        *reinterpret_cast<u32x4*>(Vs + key * KP + ck * 16) = vv;
-      }
-      if (tid < BKT) {
-        s_ks[tid] = tid < nk ? p.start[k0 + tid] : -1;
-        s_kd[tid] = tid < nk ? p.depth[k0 + tid] : -1;
-      }
-      __syncthreads();
+  constexpr int NPF = BKT * (DH / 8) / 256;
+  static_assert(NPF * 256 == BKT * (DH / 8), "whole 16-byte chunks per thread");
+  u32x4 pk[NPF], pv[NPF];
+  int pls = -1, pld = -1;
+  auto prefetch = [&](int tt) {
+    int k0, nk;
+    tile_at(tt, k0, nk);
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c / (DH / 8), ck = c % (DH / 8);
+      const int64_t row = k0 + (key < nk ? key : 0);
+      pk[i] = ld16(reinterpret_cast<const uint16_t*>(p.k) + row * rstride + kvh * DH + ck * 8);
+      pv[i] = ld16(reinterpret_cast<const uint16_t*>(p.v) + row * rstride + kvh * DH + ck * 8);
+    }
+    if (tid < BKT) {
+      pls = tid < nk ? p.start[k0 + tid] : -1;
+      pld = tid < nk ? p.depth[k0 + tid] : -1;
+    }
+  };
+  if (ntile > 0) prefetch(0);
+  for (int tt = 0; tt < ntile; ++tt) {
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c / (DH / 8), ck = c % (DH / 8);
+      *reinterpret_cast<u32x4*>(Ks + key * KP + ck * 16) = pk[i];
+      *reinterpret_cast<u32x4*>(Kt + key * TP + ck * 16) = pk[i];
+      *reinterpret_cast<u32x4*>(Vs + key * KP + ck * 16) = pv[i];
+    }
+    if (tid < BKT) {
+      s_ks[tid] = pls;
+      s_kd[tid] = pld;
+    }
+    __syncthreads();
+    if (tt + 1 < ntile) prefetch(tt + 1);
+    {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {  // halves of 32 keys
         f32x4 sacc[CB][2], pacc[CB][2];
@@ -237,8 +276,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
             const int bb = i >> 2, j = i & 3;
             const int kk = 16 * (2 * h2 + bb) + 4 * g + j;
             const bool vis = sees(cs[cb], cd[cb], s_ks[kk], s_kd[kk]);
-            const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[cb][bb][j], sl2, -clse2[cb])) : 0.f;
-            ds[i] = pv * (pacc[cb][bb][j] - cdel[cb]);
+            const float pv_ = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[cb][bb][j], sl2, -clse2[cb])) : 0.f;
+            ds[i] = pv_ * (pacc[cb][bb][j] - cdel[cb]);
           }
           bop[cb] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
                           pack_bf16x2(ds[6], ds[7])};
@@ -251,7 +290,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
           for (int cb = 0; cb < CB; ++cb) mma16(acc[cb][mb], aop, bop[cb], uint16_t());
         }
       }
-      __syncthreads();
     }
   }
   // dQ = scale dQ^T: lane (g, r) holds dims 16 mb + 4 g + j of its column
@@ -275,11 +313,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
   constexpr int NST = DH / 32;
   constexpr int NMB = DH / 16;
   constexpr int PP = DH * 2 + 32;  // Q / dO row pitch (row reads and transposed reads)
-  constexpr int NCB = BCOL / 16;   // 16-column blocks of a query tile
-  __shared__ __attribute__((aligned(16))) char Qs[BCOL * PP];
-  __shared__ __attribute__((aligned(16))) char Ds[BCOL * PP];
-  __shared__ __attribute__((aligned(16))) float s_lse2[BCOL], s_del[BCOL];
-  __shared__ __attribute__((aligned(16))) int s_cs[BCOL], s_cd[BCOL];
+  constexpr int NCB = BCOLK / 16;  // 16-column blocks of a query tile
+  __shared__ __attribute__((aligned(16))) char Qs[BCOLK * PP];
+  __shared__ __attribute__((aligned(16))) char Ds[BCOLK * PP];
+  __shared__ __attribute__((aligned(16))) float s_lse2[BCOLK], s_del[BCOLK];
+  __shared__ __attribute__((aligned(16))) int s_cs[BCOLK], s_cd[BCOLK];
   __shared__ int s_rng[2 * BMAXG], s_tile[4], s_tpre[BMAXG + 1], s_piece[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -305,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
   __syncthreads();
   const int ke = s_tile[0], kr0 = s_tile[1], kr1 = s_tile[2];
   if (kr0 < 0) return;
-  const int QPW = BCOL / G;
+  const int QPW = BCOLK / G;
   const float sl2 = p.scale * 1.4426950408889634f;
   const int64_t rstride = (int64_t)p.Hkv * DH;
 
@@ -356,34 +394,62 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
 #pragma unroll
   for (int i = 0; i < NMB; ++i) dka[i] = dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int d = ke; d < p.D; ++d) {
-    const int qa0 = s_rng[2 * d], qb0 = s_rng[2 * d + 1];
-    for (int i = 0, qa = qa0; qa < qb0; ++i, qa += QPW) {
-      if (s_tpre[d] + i < tlo) continue;
-      if (s_tpre[d] + i >= thi) break;
-      const int qb = min(qa + QPW, qb0);
-      // stage the tile's columns: Q and dO rows, labels, lse and delta
-      for (int c = tid; c < BCOL * (DH / 8); c += 256) {
-        const int col = c / (DH / 8), ck = c % (DH / 8);
-        const int qi = qa + col / G, h = kvh * G + col % G;
-        u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
-        if (qi < qb) {
-          qv = ld16(reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)qi * p.Hq + h) * DH + ck * 8);
-          dv = ld16(reinterpret_cast<const uint16_t*>(p.dout) + ((int64_t)qi * p.Hq + h) * DH + ck * 8);
-        }
-        *reinterpret_cast<u32x4*>(Qs + col * PP + ck * 16) = qv;
-        *reinterpret_cast<u32x4*>(Ds + col * PP + ck * 16) = dv;
+  // the share's query tiles in one list; the next tile's Q, dO and labels are
+  // loaded into registers while this one is multiplied
+  auto tile_at = [&](int tt, int& qa, int& qb) {
+    int d = 0;
+    while (d < BMAXG - 1 && tt >= s_tpre[d + 1]) ++d;
+    qa = s_rng[2 * d] + (tt - s_tpre[d]) * QPW;
+    qb = min(qa + QPW, s_rng[2 * d + 1]);
+  };
+  constexpr int NPF = BCOLK * (DH / 8) / 256;
+  static_assert(NPF * 256 == BCOLK * (DH / 8), "whole 16-byte chunks per thread");
+  u32x4 pq[NPF], pd[NPF];
+  int pcs = -1, pcd = -1;
+  float plse = 0.f, pdel = 0.f;
+  auto prefetch = [&](int tt) {
+    int qa, qb;
+    tile_at(tt, qa, qb);
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int c = tid + 256 * i;
+      const int col = c / (DH / 8), ck = c % (DH / 8);
+      const int qi = qa + col / G, h = kvh * G + col % G;
+      pq[i] = pd[i] = u32x4{0u, 0u, 0u, 0u};
+      if (qi < qb) {
+        pq[i] = ld16(reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)qi * p.Hq + h) * DH + ck * 8);
+        pd[i] = ld16(reinterpret_cast<const uint16_t*>(p.dout) + ((int64_t)qi * p.Hq + h) * DH + ck * 8);
       }
-      if (tid < BCOL) {
-        const int qi = qa + tid / G, h = kvh * G + tid % G;
-        const bool act = qi < qb;
-        s_cs[tid] = act ? p.start[qi] : -1;
-        s_cd[tid] = act ? p.depth[qi] : -1;
-        s_lse2[tid] = act ? p.lse[(int64_t)qi * p.Hq + h] * 1.4426950408889634f : 0.f;
-        s_del[tid] = act ? p.delta[(int64_t)(qi - p.q_begin) * p.Hq + h] : 0.f;
-      }
-      __syncthreads();
-      // S' and dP' of the 8 column blocks: element j of lane (g, r) is column 16 cb + 4 g + j, key r
+    }
+    if (tid < BCOLK) {
+      const int qi = qa + tid / G, h = kvh * G + tid % G;
+      const bool act = qi < qb;
+      pcs = act ? p.start[qi] : -1;
+      pcd = act ? p.depth[qi] : -1;
+      plse = act ? p.lse[(int64_t)qi * p.Hq + h] * 1.4426950408889634f : 0.f;
+      pdel = act ? p.delta[(int64_t)(qi - p.q_begin) * p.Hq + h] : 0.f;
+    }
+  };
+  if (tlo < thi) prefetch(tlo);
+  for (int tt = tlo; tt < thi; ++tt) {
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int c = tid + 256 * i;
+      const int col = c / (DH / 8), ck = c % (DH / 8);
+      *reinterpret_cast<u32x4*>(Qs + col * PP + ck * 16) = pq[i];
+      *reinterpret_cast<u32x4*>(Ds + col * PP + ck * 16) = pd[i];
+    }
+    if (tid < BCOLK) {
+      s_cs[tid] = pcs;
+      s_cd[tid] = pcd;
+      s_lse2[tid] = plse;
+      s_del[tid] = pdel;
+    }
+    __syncthreads();
+    if (tt + 1 < thi) prefetch(tt + 1);
+    {
+      // S' and dP' of the column blocks: element j of lane (g, r) is column 16 cb + 4 g + j, key r
       f32x4 sacc[NCB], pacc[NCB];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) sacc[cb] = pacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -420,7 +486,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
           mma16(dka[mb], tr_pair(Qs + off, PP), sb, uint16_t());
         }
       }
-      __syncthreads();
     }
   }
   // this share's partial dK = scale dK^T and dV = dV^T (lane (g, r) holds dims
