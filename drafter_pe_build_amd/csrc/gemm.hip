@@ -661,7 +661,7 @@ void lm_argmax_stream_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-template <typename S, int BM, int BN, bool DUAL, bool ARGMAX>
+template <typename S, int BM, int BN, bool DUAL, bool ARGMAX, bool LSE = false>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft, int n_mt) {
   constexpr int CH = Storage<S>::CH;
   constexpr int BKC = 8;             // 16-byte chunks per activation row per k-tile (two steps)
@@ -765,15 +765,15 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft,
   }
 
   if constexpr (ARGMAX) {
-    // argmax or log-sum-exp partials of this tile's rows (EPI_ARGMAX / EPI_LSE)
-    const bool lse = p.epi.kind == EPI_LSE;
+    // argmax (EPI_ARGMAX) or log-sum-exp (EPI_LSE, LSE set) partials of this tile's rows
     __shared__ float sbv[2][BM], sbs[2][BM];
     __shared__ int sbi[2][BM];
 #pragma unroll
     for (int q = 0; q < RBW; ++q) {
       const int mloc = wm * (BM / 2) + q * 16 + r;
       const int m = m0 + mloc;
-      const int tgt = (lse && p.epi.targets && m < M) ? p.epi.targets[m] : -1;
+      int tgt = -1;
+      if constexpr (LSE) tgt = (p.epi.targets && m < M) ? p.epi.targets[m] : -1;
       RowRed rr = RowRed::init();
 #pragma unroll
       for (int f = 0; f < FBW; ++f)
@@ -783,19 +783,25 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft,
           if (n < N && m < M) {
             const float v = acc[f][q][j];
             if (p.epi.logits) p.epi.logits[(int64_t)m * N + n] = v;
-            if (n == tgt) p.epi.tgt_logit[m] = v;
-            rr.add(lse, v, n);
+            if constexpr (LSE) {
+              if (n == tgt) p.epi.tgt_logit[m] = v;
+            }
+            rr.add(LSE, v, n);
           }
         }
-      rr.merge_groups(lse);
-      if (g == 0) { sbv[wn][mloc] = rr.v; sbi[wn][mloc] = rr.i; sbs[wn][mloc] = rr.s; }
+      rr.merge_groups(LSE);
+      if (g == 0) {
+        sbv[wn][mloc] = rr.v;
+        if constexpr (LSE) sbs[wn][mloc] = rr.s;
+        else sbi[wn][mloc] = rr.i;
+      }
     }
     __syncthreads();
     if (tid < BM && m0 + tid < M) {
-      RowRed rr{sbv[0][tid], sbs[0][tid], sbi[0][tid]};
-      rr.merge(lse, sbv[1][tid], sbi[1][tid], sbs[1][tid]);
+      RowRed rr{sbv[0][tid], LSE ? sbs[0][tid] : 0.f, LSE ? 0 : sbi[0][tid]};
+      rr.merge(LSE, sbv[1][tid], LSE ? 0 : sbi[1][tid], LSE ? sbs[1][tid] : 0.f);
       p.epi.part_val[(int64_t)ft * M + m0 + tid] = rr.v;
-      if (lse) p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
+      if constexpr (LSE) p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
       else p.epi.part_idx[(int64_t)ft * M + m0 + tid] = rr.i;
     }
   } else {
@@ -916,11 +922,11 @@ int gemm_argmax_partials(int M, int N) {
   return (N + 63) / 64;  // largest count over the tiled configurations (BN >= 64)
 }
 
-template <typename S, int BM, int BN, bool DUAL, bool ARGMAX>
+template <typename S, int BM, int BN, bool DUAL, bool ARGMAX, bool LSE = false>
 static int launch_tiled(const GemmParams& p, hipStream_t s) {
   const int n_ft = (p.N + BN - 1) / BN, n_mt = (p.M + BM - 1) / BM;
   const int grid = ((n_ft + 7) / 8) * 8 * n_mt;
-  hipLaunchKernelGGL((gemm_tiled_kernel<S, BM, BN, DUAL, ARGMAX>), dim3(grid), dim3(256), 0, s, p, n_ft, n_mt);
+  hipLaunchKernelGGL((gemm_tiled_kernel<S, BM, BN, DUAL, ARGMAX, LSE>), dim3(grid), dim3(256), 0, s, p, n_ft, n_mt);
   return n_ft;
 }
 
@@ -1128,6 +1134,8 @@ static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
     const int r = launch_gemm_big(p, s);
     if (r >= 0) return r;
   }
+  if (am && p.epi.kind == EPI_LSE)
+    return big ? launch_tiled<S, 128, 128, false, true, true>(p, s) : launch_tiled<S, 64, 64, false, true, true>(p, s);
   if (am) return big ? launch_tiled<S, 128, 128, false, true>(p, s) : launch_tiled<S, 64, 64, false, true>(p, s);
   // the gate/up pair keeps 128 x 64 tiles from 256 rows on (two weight streams per tile)
   if (dual) { if (p.M >= 256) launch_tiled<S, 128, 64, true, false>(p, s); else launch_tiled<S, 64, 64, true, false>(p, s); }

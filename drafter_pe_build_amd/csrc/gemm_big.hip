@@ -37,7 +37,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Two waves per SIMD: two 4-wave workgroups (or one 8-wave one) per CU.
-template <int BM, int BN, int WN, int D, bool DUAL, bool ARGMAX, bool SPLIT, bool PX>
+template <int BM, int BN, int WN, int D, bool DUAL, bool ARGMAX, bool SPLIT, bool PX, bool LSE>
 __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   constexpr int NW = 2 * WN;           // waves: 2 along the rows x WN along the features
@@ -178,15 +178,15 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
 #undef PE_BIG_FRAGS
 
   if constexpr (ARGMAX) {
-    // argmax or log-sum-exp partials of this tile's rows (EPI_ARGMAX / EPI_LSE)
-    const bool lse = p.epi.kind == EPI_LSE;
+    // argmax (EPI_ARGMAX) or log-sum-exp (EPI_LSE, LSE set) partials of this tile's rows
     __shared__ float sbv[WN][BM], sbs[WN][BM];
     __shared__ int sbi[WN][BM];
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
       const int mloc = wm * (BM / 2) + q * 16 + r;
       const int m = m0 + mloc;
-      const int tgt = (lse && p.epi.targets && m < M) ? p.epi.targets[m] : -1;
+      int tgt = -1;
+      if constexpr (LSE) tgt = (p.epi.targets && m < M) ? p.epi.targets[m] : -1;
       RowRed rr = RowRed::init();
 #pragma unroll
       for (int f = 0; f < FW; ++f)
@@ -196,19 +196,25 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
           if (n < N && m < M) {
             const float v = acc[f][q][j];
             if (p.epi.logits) p.epi.logits[(int64_t)m * N + n] = v;
-            if (n == tgt) p.epi.tgt_logit[m] = v;
-            rr.add(lse, v, n);
+            if constexpr (LSE) {
+              if (n == tgt) p.epi.tgt_logit[m] = v;
+            }
+            rr.add(LSE, v, n);
           }
         }
-      rr.merge_groups(lse);
-      if (g == 0) { sbv[wn][mloc] = rr.v; sbi[wn][mloc] = rr.i; sbs[wn][mloc] = rr.s; }
+      rr.merge_groups(LSE);
+      if (g == 0) {
+        sbv[wn][mloc] = rr.v;
+        if constexpr (LSE) sbs[wn][mloc] = rr.s;
+        else sbi[wn][mloc] = rr.i;
+      }
     }
     __syncthreads();
     if (tid < BM && m0 + tid < M) {
-      RowRed rr{sbv[0][tid], sbs[0][tid], sbi[0][tid]};
-      for (int w = 1; w < WN; ++w) rr.merge(lse, sbv[w][tid], sbi[w][tid], sbs[w][tid]);
+      RowRed rr{sbv[0][tid], LSE ? sbs[0][tid] : 0.f, LSE ? 0 : sbi[0][tid]};
+      for (int w = 1; w < WN; ++w) rr.merge(LSE, sbv[w][tid], LSE ? 0 : sbi[w][tid], LSE ? sbs[w][tid] : 0.f);
       p.epi.part_val[(int64_t)ft * M + m0 + tid] = rr.v;
-      if (lse) p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
+      if constexpr (LSE) p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
       else p.epi.part_idx[(int64_t)ft * M + m0 + tid] = rr.i;
     }
   } else if constexpr (SPLIT) {
@@ -258,18 +264,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int sp
   for (int j = 0; j < 4; ++j) epi_store<uint16_t>(p.epi, m, n + j, y[j], y2[j]);
 }
 
-template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX, bool SPLIT, bool PX = false>
+template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX, bool SPLIT, bool PX = false, bool LSE = false>
 static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
   constexpr int STAGE = (BN / 16) * 1024 * (DUAL ? 2 : 1) + BM * 64;
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX>),
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX, LSE>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, STAGES * STAGE);
     attr = true;
   }
   const int n_ft = (p.N + BN - 1) / BN, n_mt = (p.M + BM - 1) / BM;
   const int grid = ((n_ft + 7) / 8) * 8 * n_mt;
-  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX>), dim3(grid, splits), dim3(128 * WN),
+  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX, LSE>), dim3(grid, splits), dim3(128 * WN),
                      STAGES * STAGE, s, p, n_ft, n_mt);
   return n_ft;
 }
@@ -317,6 +323,13 @@ int gemm_big_splits(const GemmParams& p) {
 int launch_gemm_big(const GemmParams& p, hipStream_t s) {
   const bool r224 = rows224(p.M);
   if (epi_rowred(p.epi.kind)) {
+    if (p.epi.kind == EPI_LSE) {
+      if (p.x_packed)
+        return r224 ? launch_big<224, 128, 2, 3, false, true, false, true, true>(p, 1, s)
+                    : launch_big<256, 128, 2, 3, false, true, false, true, true>(p, 1, s);
+      return r224 ? launch_big<224, 128, 2, 3, false, true, false, false, true>(p, 1, s)
+                  : launch_big<256, 128, 2, 3, false, true, false, false, true>(p, 1, s);
+    }
     if (p.x_packed)
       return r224 ? launch_big<224, 128, 2, 3, false, true, false, true>(p, 1, s)
                   : launch_big<256, 128, 2, 3, false, true, false, true>(p, 1, s);
