@@ -31,6 +31,7 @@
 // fixed order.  Each workgroup owns its outputs, so results do not depend on
 // timing.
 #include <math.h>
+#include <type_traits>
 #include "kernels.h"
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -201,8 +202,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
   }
   __syncthreads();
   const int ntile = s_tp[BMAXG];
-  auto tile_at = [&](int tt, int& k0, int& nk) {
-    int e = 0;
+  auto tile_at = [&](int tt, int& k0, int& nk, int& e) {
+    e = 0;
     while (e < qd_max && tt >= s_tp[e + 1]) ++e;
     k0 = s_rng[2 * e] + (tt - s_tp[e]) * BKT;
     nk = min(BKT, s_rng[2 * e + 1] - k0);
@@ -213,10 +214,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
   constexpr int NPF = BKT * (DH / 8) / 256;
   static_assert(NPF * 256 == BKT * (DH / 8), "whole 16-byte chunks per thread");
   u32x4 pk[NPF], pv[NPF];
-  int pls = -1, pld = -1;
+  int pls = -1, pld = -1, pfull = 0;
   auto prefetch = [&](int tt) {
-    int k0, nk;
-    tile_at(tt, k0, nk);
+    int k0, nk, e;
+    tile_at(tt, k0, nk, e);
+    // every query of the workgroup sees the whole tile: 64 group-0 keys whose
+    // largest start is at most the smallest query start
+    pfull = __builtin_amdgcn_readfirstlane(e == 0 && nk == BKT && p.start[k0 + BKT - 1] <= qs_min);
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
       const int c = tid + 256 * i;
@@ -245,6 +249,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
       s_ks[tid] = pls;
       s_kd[tid] = pld;
     }
+    const bool full = pfull;
     __syncthreads();
     if (tt + 1 < ntile) prefetch(tt + 1);
     {
@@ -266,22 +271,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
               mma16(pacc[cb][bb], va, dreg[cb][t], uint16_t());
             }
           }
-        // dS^T = P^T (dP^T - delta), P from the forward's log-sum-exp; packed as the B operand
+        // dS^T = P^T (dP^T - delta), P from the forward's log-sum-exp; packed as
+        // the B operand.  FULL skips the visibility test (inactive columns have
+        // zero Q and dO rows, so their dS is zero either way).
         u32x4 bop[CB];
+        auto make_ds = [&](auto full_c) {
+          constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          float ds[8];
+          for (int cb = 0; cb < CB; ++cb) {
+            float ds[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int bb = i >> 2, j = i & 3;
-            const int kk = 16 * (2 * h2 + bb) + 4 * g + j;
-            const bool vis = sees(cs[cb], cd[cb], s_ks[kk], s_kd[kk]);
-            const float pv_ = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[cb][bb][j], sl2, -clse2[cb])) : 0.f;
-            ds[i] = pv_ * (pacc[cb][bb][j] - cdel[cb]);
+            for (int i = 0; i < 8; ++i) {
+              const int bb = i >> 2, j = i & 3;
+              const int kk = 16 * (2 * h2 + bb) + 4 * g + j;
+              const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][bb][j], sl2, -clse2[cb]));
+              const float pv_ = (FULL || sees(cs[cb], cd[cb], s_ks[kk], s_kd[kk])) ? e2 : 0.f;
+              ds[i] = pv_ * (pacc[cb][bb][j] - cdel[cb]);
+            }
+            bop[cb] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                            pack_bf16x2(ds[6], ds[7])};
           }
-          bop[cb] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
-                          pack_bf16x2(ds[6], ds[7])};
-        }
+        };
+        if (full) make_ds(std::true_type{});
+        else make_ds(std::false_type{});
         // dQ^T += K^T dS^T: lane r receives dim 16 mb + r of keys 32 h2 + 4 g + c and + 16
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
@@ -402,14 +414,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
     qa = s_rng[2 * d] + (tt - s_tpre[d]) * QPW;
     qb = min(qa + QPW, s_rng[2 * d + 1]);
   };
+  // largest start of the workgroup's keys (a group's rows are sorted by start)
+  const int kmax_s = p.start[kr1 - 1];
   constexpr int NPF = BCOLK * (DH / 8) / 256;
   static_assert(NPF * 256 == BCOLK * (DH / 8), "whole 16-byte chunks per thread");
   u32x4 pq[NPF], pd[NPF];
-  int pcs = -1, pcd = -1;
+  int pcs = -1, pcd = -1, pfull = 0;
   float plse = 0.f, pdel = 0.f;
   auto prefetch = [&](int tt) {
     int qa, qb;
     tile_at(tt, qa, qb);
+    // every column sees every key: group-0 keys, and the tile's first (smallest)
+    // query start at least the keys' largest start
+    pfull = __builtin_amdgcn_readfirstlane(ke == 0 && p.start[qa] >= kmax_s);
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
       const int c = tid + 256 * i;
@@ -446,6 +463,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
       s_lse2[tid] = plse;
       s_del[tid] = pdel;
     }
+    const bool full = pfull;
     __syncthreads();
     if (tt + 1 < thi) prefetch(tt + 1);
     {
@@ -465,19 +483,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
       // P' and dS' packed per 32-column step as B operands (columns 32 s + 4 g + j, then + 16)
 #pragma unroll
       for (int s = 0; s < NCB / 2; ++s) {
-        float pv[8], ds[8];
+        // FULL skips the visibility test (padding keys only feed their own,
+        // unwritten, accumulator columns; inactive columns have zero Q and dO rows)
+        u32x4 pb, sb;
+        auto make_ps = [&](auto full_c) {
+          constexpr bool FULL = decltype(full_c)::value;
+          float pv[8], ds[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int cb = 2 * s + (i >> 2), j = i & 3;
-          const int col = 16 * cb + 4 * g + j;
-          const bool vis = sees(s_cs[col], s_cd[col], ks, kd);
-          pv[i] = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[cb][j], sl2, -s_lse2[col])) : 0.f;
-          ds[i] = pv[i] * (pacc[cb][j] - s_del[col]);
-        }
-        const u32x4 pb = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                          pack_bf16x2(pv[6], pv[7])};
-        const u32x4 sb = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
-                          pack_bf16x2(ds[6], ds[7])};
+          for (int i = 0; i < 8; ++i) {
+            const int cb = 2 * s + (i >> 2), j = i & 3;
+            const int col = 16 * cb + 4 * g + j;
+            const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][j], sl2, -s_lse2[col]));
+            pv[i] = (FULL || sees(s_cs[col], s_cd[col], ks, kd)) ? e2 : 0.f;
+            ds[i] = pv[i] * (pacc[cb][j] - s_del[col]);
+          }
+          pb = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                     pack_bf16x2(pv[6], pv[7])};
+          sb = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                     pack_bf16x2(ds[6], ds[7])};
+        };
+        if (full) make_ps(std::true_type{});
+        else make_ps(std::false_type{});
         // lane r receives dim 16 mb + r of columns 32 s + 4 g + c and + 16
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
