@@ -103,18 +103,21 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(AttnBwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: columns (query, head) of one kv head; per key tile S^T = K Q^T and
 // dP^T = V dO^T (B operands in registers), dQ^T += K^T dS^T (K^T read
-// transposed from LDS, dS^T from the score registers).
+// transposed from the same LDS copy of K, dS^T from the score registers).
+// Key tiles are double-buffered in LDS and copied there straight from global
+// memory one tile ahead, with one barrier per tile.
 template <int DH>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, int G, int n_qtiles) {
   constexpr int NST = DH / 32;                  // 32-dim contraction steps
   constexpr int NMB = DH / 16;                  // 16-dim output blocks
-  constexpr int KP = DH * 2 + 16;               // K / V row pitch (row reads)
-  constexpr int TP = DH * 2 + 32;               // K row pitch of the transposed copy
+  constexpr int KP = DH * 2 + 16;               // V row pitch (row reads)
+  constexpr int TP = DH * 2 + 32;               // K row pitch (row and transposed reads)
   constexpr int CB = 2;                         // 16-column blocks per wave
-  __shared__ __attribute__((aligned(16))) char Ks[BKT * KP];
-  __shared__ __attribute__((aligned(16))) char Kt[BKT * TP];
-  __shared__ __attribute__((aligned(16))) char Vs[BKT * KP];
-  __shared__ int s_ks[BKT], s_kd[BKT];
+  // two tile buffers: K once, at the pitch of the transposed reads (its row
+  // reads use the same copy), V at the row pitch, and the labels
+  __shared__ __attribute__((aligned(16))) char Ks[2][BKT * TP];
+  __shared__ __attribute__((aligned(16))) char Vs[2][BKT * KP];
+  __shared__ int s_ks[2][BKT], s_kd[2][BKT];
   __shared__ int s_rng[2 * BMAXG], s_red[12], s_tp[BMAXG + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -208,101 +211,157 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
     k0 = s_rng[2 * e] + (tt - s_tp[e]) * BKT;
     nk = min(BKT, s_rng[2 * e + 1] - k0);
   };
-  // the next tile's K, V and labels are loaded into registers while this one
-  // is multiplied; rows past a range repeat its first row (masked out)
+  // The next tile is copied from global memory straight into the other LDS
+  // buffer (that buffer's previous tile was released by the barrier that ends
+  // every tile) while this one is multiplied: one 64-lane copy fills 64
+  // consecutive 16-byte slots of the padded layout (lane l -> slot l), the
+  // copies spread round-robin over the waves; slots of row padding load
+  // chunk 0 of their row (never read back), and keys past a range repeat the
+  // range's first row (masked out).  The labels go through registers.
   const int64_t rstride = (int64_t)p.Hkv * DH;
-  constexpr int NPF = BKT * (DH / 8) / 256;
-  static_assert(NPF * 256 == BKT * (DH / 8), "whole 16-byte chunks per thread");
-  u32x4 pk[NPF], pv[NPF];
+  constexpr int KSL = TP / 16, VSL = KP / 16;                    // slots per padded row
+  constexpr int NKC = BKT * KSL / 64, NVC = BKT * VSL / 64;      // 1 KB copies per tile
+  static_assert(NKC * 64 == BKT * KSL && NVC * 64 == BKT * VSL, "whole copies per tile");
+  constexpr int NCP = NKC + NVC, NCW = (NCP + 3) / 4;           // copies in all, per wave
+  // key and chunk of copy q of this lane
+  auto cslot = [&](int q, int& key, int& ck) {
+    const int j = wave + 4 * q;
+    const bool isv = j >= NKC;
+    const int sl = isv ? VSL : KSL;
+    const int slot = (isv ? j - NKC : j) * 64 + lane;
+    key = slot / sl;
+    ck = slot % sl < DH / 8 ? slot % sl : 0;
+  };
+  uint32_t coff[NCW];  // element offset of copy q within a tile of 64 rows
+#pragma unroll
+  for (int q = 0; q < NCW; ++q) {
+    int key, ck;
+    cslot(q, key, ck);
+    coff[q] = (uint32_t)key * (uint32_t)rstride + (uint32_t)(ck * 8);
+  }
   int pls = -1, pld = -1, pfull = 0;
-  auto prefetch = [&](int tt) {
+  auto prefetch = [&](int tt, int b) {
     int k0, nk, e;
     tile_at(tt, k0, nk, e);
     // every query of the workgroup sees the whole tile: 64 group-0 keys whose
     // largest start is at most the smallest query start
     pfull = __builtin_amdgcn_readfirstlane(e == 0 && nk == BKT && p.start[k0 + BKT - 1] <= qs_min);
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)k0 * rstride + kvh * DH;
+    const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)k0 * rstride + kvh * DH;
 #pragma unroll
-    for (int i = 0; i < NPF; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (DH / 8), ck = c % (DH / 8);
-      const int64_t row = k0 + (key < nk ? key : 0);
-      pk[i] = ld16(reinterpret_cast<const uint16_t*>(p.k) + row * rstride + kvh * DH + ck * 8);
-      pv[i] = ld16(reinterpret_cast<const uint16_t*>(p.v) + row * rstride + kvh * DH + ck * 8);
+    for (int q = 0; q < NCW; ++q) {
+      const int j = wave + 4 * q;
+      if (j >= NCP) break;
+      const bool isv = j >= NKC;
+      uint32_t off = coff[q];
+      if (nk < BKT) {
+        int key, ck;
+        cslot(q, key, ck);
+        off = (uint32_t)(key < nk ? key : 0) * (uint32_t)rstride + (uint32_t)(ck * 8);
+      }
+      char* dst = isv ? Vs[b] + (j - NKC) * 1024 : Ks[b] + j * 1024;
+      copy16_to_lds((isv ? vb : kb) + off, dst);
     }
     if (tid < BKT) {
       pls = tid < nk ? p.start[k0 + tid] : -1;
       pld = tid < nk ? p.depth[k0 + tid] : -1;
     }
   };
-  if (ntile > 0) prefetch(0);
-  for (int tt = 0; tt < ntile; ++tt) {
-    __syncthreads();  // every wave is done with the previous tile
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (DH / 8), ck = c % (DH / 8);
-      *reinterpret_cast<u32x4*>(Ks + key * KP + ck * 16) = pk[i];
-      *reinterpret_cast<u32x4*>(Kt + key * TP + ck * 16) = pk[i];
-      *reinterpret_cast<u32x4*>(Vs + key * KP + ck * 16) = pv[i];
-    }
+  auto store_labels = [&](int b) {
     if (tid < BKT) {
-      s_ks[tid] = pls;
-      s_kd[tid] = pld;
+      s_ks[b][tid] = pls;
+      s_kd[b][tid] = pld;
     }
-    const bool full = pfull;
-    __syncthreads();
-    if (tt + 1 < ntile) prefetch(tt + 1);
-    {
+  };
+
+  // per-half steps (a half is 32 keys; this lane holds keys 32 h + 16 bb + 4 g + j
+  // of its two columns)
+  typedef f32x4 HalfS[CB][2];
+  typedef u32x4 HalfB[CB];
+  // S^T = K Q^T and dP^T = V dO^T (Q, dO in registers)
+  auto s_half = [&](const char* Kb, const char* Vb, int h, HalfS& sacc, HalfS& pacc) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {  // halves of 32 keys
-        f32x4 sacc[CB][2], pacc[CB][2];
+    for (int cb = 0; cb < CB; ++cb) sacc[cb][0] = sacc[cb][1] = pacc[cb][0] = pacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) sacc[cb][0] = sacc[cb][1] = pacc[cb][0] = pacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+      for (int t = 0; t < NST; ++t) {
+        const int kr = 16 * (2 * h + bb) + r;
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(Kb + kr * TP + (4 * t + g) * 16);
+        const u32x4 va = *reinterpret_cast<const u32x4*>(Vb + kr * KP + (4 * t + g) * 16);
 #pragma unroll
-          for (int t = 0; t < NST; ++t) {
-            const int kr = 16 * (2 * h2 + bb) + r;
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(Ks + kr * KP + (4 * t + g) * 16);
-            const u32x4 va = *reinterpret_cast<const u32x4*>(Vs + kr * KP + (4 * t + g) * 16);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-              mma16(sacc[cb][bb], ka, qreg[cb][t], uint16_t());
-              mma16(pacc[cb][bb], va, dreg[cb][t], uint16_t());
-            }
-          }
-        // dS^T = P^T (dP^T - delta), P from the forward's log-sum-exp; packed as
-        // the B operand.  FULL skips the visibility test (inactive columns have
-        // zero Q and dO rows, so their dS is zero either way).
-        u32x4 bop[CB];
-        auto make_ds = [&](auto full_c) {
-          constexpr bool FULL = decltype(full_c)::value;
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            float ds[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int bb = i >> 2, j = i & 3;
-              const int kk = 16 * (2 * h2 + bb) + 4 * g + j;
-              const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[cb][bb][j], sl2, -clse2[cb]));
-              const float pv_ = (FULL || sees(cs[cb], cd[cb], s_ks[kk], s_kd[kk])) ? e2 : 0.f;
-              ds[i] = pv_ * (pacc[cb][bb][j] - cdel[cb]);
-            }
-            bop[cb] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
-                            pack_bf16x2(ds[6], ds[7])};
-          }
-        };
-        if (full) make_ds(std::true_type{});
-        else make_ds(std::false_type{});
-        // dQ^T += K^T dS^T: lane r receives dim 16 mb + r of keys 32 h2 + 4 g + c and + 16
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const u32x4 aop = tr_pair(Kt + (32 * h2 + 4 * g + (r >> 2)) * TP + (16 * mb + 4 * (r & 3)) * 2, TP);
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) mma16(acc[cb][mb], aop, bop[cb], uint16_t());
+        for (int cb = 0; cb < CB; ++cb) {
+          mma16(sacc[cb][bb], ka, qreg[cb][t], uint16_t());
+          mma16(pacc[cb][bb], va, dreg[cb][t], uint16_t());
         }
       }
+  };
+  // scores of keys a column does not see become -inf (tiles some column sees
+  // only in part)
+  auto mask_half = [&](int b, int h, HalfS& sacc) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = 16 * (2 * h + bb) + 4 * g + j;
+        const int ks = s_ks[b][kk], kd = s_kd[b][kk];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          sacc[cb][bb][j] = sees(cs[cb], cd[cb], ks, kd) ? sacc[cb][bb][j] : -INFINITY;
+      }
+  };
+  // dS^T = P^T (dP^T - delta) with P from the forward's log-sum-exp, packed as
+  // the B operand (inactive columns have zero Q and dO rows: dS = 0)
+  auto ds_half = [&](const HalfS& sacc, const HalfS& pacc, HalfB& bop) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float ds[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int bb = i >> 2, j = i & 3;
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[cb][bb][j], sl2, -clse2[cb]));
+        ds[i] = pe * (pacc[cb][bb][j] - cdel[cb]);
+      }
+      bop[cb] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                      pack_bf16x2(ds[6], ds[7])};
     }
+  };
+  // dQ^T += K^T dS^T: lane r receives dim 16 mb + r of keys 32 h + 4 g + c and + 16
+  auto dq_half = [&](const char* Kb, int h, const HalfB& bop) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const u32x4 aop = tr_pair(Kb + (32 * h + 4 * g + (r >> 2)) * TP + (16 * mb + 4 * (r & 3)) * 2, TP);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) mma16(acc[cb][mb], aop, bop[cb], uint16_t());
+    }
+  };
+  // Per tile: copy next | per half S, mask, dS, dQ | wait for the copies, barrier.
+  if (ntile > 0) {
+    prefetch(0, 0);
+    store_labels(0);
+  }
+  bool full = pfull;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of the first tile
+  __syncthreads();
+  for (int tt = 0; tt < ntile; ++tt) {
+    const int b = tt & 1;
+    const bool more = tt + 1 < ntile;
+    if (more) prefetch(tt + 1, b ^ 1);
+    const char* Kb = Ks[b];
+    const char* Vb = Vs[b];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      HalfS s0, p0;
+      HalfB b0;
+      s_half(Kb, Vb, h, s0, p0);
+      if (!full) mask_half(b, h, s0);
+      ds_half(s0, p0, b0);
+      dq_half(Kb, h, b0);
+    }
+    if (more) store_labels(b ^ 1);
+    full = pfull;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of the next tile
+    __syncthreads();  // the next tile is in place; this one's buffer is free
   }
   // dQ = scale dQ^T: lane (g, r) holds dims 16 mb + 4 g + j of its column
 #pragma unroll
