@@ -84,20 +84,30 @@ __device__ __forceinline__ u32x4 tr_pair(const char* p, int pitch) {
 
 }  // namespace
 
-// delta[i][h] = sum_d dO[q_begin + i][h][d] O[q_begin + i][h][d]; one wave per (query, head).
+// delta[i][h] = sum_d dO[q_begin + i][h][d] O[q_begin + i][h][d]; DH / 8 lanes
+// per (query, head) row, 16 bytes of each tensor per lane, summed across the
+// row's lanes in a fixed order.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(AttnBwdParams p) {
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  constexpr int LPR = DH / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t w = i / LPR;
+  const int c = (int)(i % LPR);
   const int64_t nqh = (int64_t)(p.q_end - p.q_begin) * p.Hq;
-  if (w >= nqh) return;
-  const int64_t row = (int64_t)p.q_begin * p.Hq + w;  // (query, head) row of out / dout
-  const uint16_t* o = reinterpret_cast<const uint16_t*>(p.out) + row * DH;
-  const uint16_t* d = reinterpret_cast<const uint16_t*>(p.dout) + row * DH;
   float acc = 0.f;
-  for (int i = lane; i < DH; i += 64) acc += bf2f(o[i]) * bf2f(d[i]);
-  acc = wave_sum(acc);
-  if (lane == 0) p.delta[w] = acc;
+  if (w < nqh) {
+    const int64_t off = ((int64_t)p.q_begin * p.Hq + w) * DH + c * 8;  // (query, head) row of out / dout
+    const u32x4 o = ld16(reinterpret_cast<const uint16_t*>(p.out) + off);
+    const u32x4 d = ld16(reinterpret_cast<const uint16_t*>(p.dout) + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf2f((uint16_t)(o[e] & 0xffffu)), bf2f((uint16_t)(d[e] & 0xffffu)), acc);
+      acc = fmaf(bf2f((uint16_t)(o[e] >> 16)), bf2f((uint16_t)(d[e] >> 16)), acc);
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (w < nqh && c == 0) p.delta[w] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -627,7 +637,7 @@ static void launch_bwd_t(const AttnBwdParams& p, hipStream_t s) {
   const int nq = p.q_end - p.q_begin;
   if (nq <= 0) return;
   const int64_t nqh = (int64_t)nq * p.Hq;
-  hipLaunchKernelGGL(attn_bwd_delta_kernel<DH>, dim3((unsigned)((nqh + 3) / 4)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(attn_bwd_delta_kernel<DH>, dim3((unsigned)((nqh * (DH / 8) + 255) / 256)), dim3(256), 0, s, p);
   const int n_qtiles = (nq + QPW - 1) / QPW;
   hipLaunchKernelGGL(attn_bwd_dq_kernel<DH>, dim3((unsigned)(n_qtiles * p.Hkv)), dim3(256), 0, s, p, G, n_qtiles);
   // key tiles: ceil(group size / 64) per group, at most ceil(T / 64) + D in all
