@@ -295,8 +295,11 @@ static bool rows224(int M) { return ((M + 223) / 224) * 224 < ((M + 255) / 256) 
 #ifndef PE_SPLIT_SLOTS
 #define PE_SPLIT_SLOTS 512
 #endif
+// At most 4 shares: the partial sums are written and read once more per
+// share (c=64 step: 991 us with up to 8, 961 us with up to 4, 992 / 1,006 us
+// with 3 / 6).
 #ifndef PE_SPLIT_MAX
-#define PE_SPLIT_MAX 8
+#define PE_SPLIT_MAX 4
 #endif
 #ifndef PE_SPLIT_MINSTEPS
 #define PE_SPLIT_MINSTEPS 16
