@@ -284,7 +284,7 @@ static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
 // 896 = 4 x 224) x 128 features, four waves and a three-stage ring, for
 // single contractions and the LM head (the eight-wave gate/up variant is kept
 // but not dispatched).  Contractions with too few tiles to give every CU two
-// workgroups split K over up to 8 workgroups (at least 16 k-steps each) when
+// workgroups split K over up to 4 workgroups (at least 16 k-steps each) when
 // the caller's workspace holds the partial products (gemm_big_splits); without
 // a split launch_gemm_big returns -1 and launches nothing.
 static bool rows224(int M) { return ((M + 223) / 224) * 224 < ((M + 255) / 256) * 256; }
