@@ -61,13 +61,18 @@ pe_status launched() { return hipGetLastError() == hipSuccess ? PE_OK : PE_ERR_D
 #ifndef PE_ATTN_NOSPLIT_GROUPS
 #define PE_ATTN_NOSPLIT_GROUPS 512
 #endif
+// Below that, the prefix is split so that about PE_ATTN_SPLIT_TARGET
+// workgroups run (at most 64 shares of at least one 64-key tile).
+#ifndef PE_ATTN_SPLIT_TARGET
+#define PE_ATTN_SPLIT_TARGET 2048
+#endif
 void choose_split(int base_groups, int max_prefix, int split_req, int* n_splits, int* split_len) {
   const int mp = max_prefix > 1 ? max_prefix : 1;
   int sl;
   if (split_req > 0) {
     sl = up64(split_req);
   } else {
-    int want = base_groups >= PE_ATTN_NOSPLIT_GROUPS ? 1 : (2048 + base_groups - 1) / base_groups;
+    int want = base_groups >= PE_ATTN_NOSPLIT_GROUPS ? 1 : (PE_ATTN_SPLIT_TARGET + base_groups - 1) / base_groups;
     const int maxs = (mp + 63) / 64;
     if (want > maxs) want = maxs;
     if (want > 64) want = 64;
