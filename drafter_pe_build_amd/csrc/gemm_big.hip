@@ -282,8 +282,10 @@ static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
 
 // Tile shapes: 256 or 224 rows (whichever pads M less: 448 = 2 x 224,
 // 896 = 4 x 224) x 128 features, four waves and a three-stage ring, for
-// single contractions and the LM head (the eight-wave gate/up variant is kept
-// but not dispatched).  Contractions with too few tiles to give every CU two
+// single contractions and the LM head.  The template also takes the gate/up
+// pair (DUAL: two weight streams, two accumulator sets), which measured
+// slower than the 128 x 64 register-fed tiles of gemm.hip and is not
+// dispatched.  Contractions with too few tiles to give every CU two
 // workgroups split K over up to 4 workgroups (at least 16 k-steps each) when
 // the caller's workspace holds the partial products (gemm_big_splits); without
 // a split launch_gemm_big returns -1 and launches nothing.
