@@ -87,8 +87,10 @@ __device__ __forceinline__ float colgroup_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Two workgroups per CU, except the f32 operands at head_dim 128, whose Q
+// columns and output blocks take one workgroup's worth of registers.
 template <typename S, int DH, bool DBG, bool WIN>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnParams p, int G, int tps) {
+__global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void attn_kernel(AttnParams p, int G, int tps) {
   constexpr bool BF = sizeof(S) == 2;
   constexpr int CH = Storage<S>::CH;
   constexpr int STEP = 4 * CH;

@@ -930,15 +930,14 @@ static int launch_tiled(const GemmParams& p, hipStream_t s) {
   return n_ft;
 }
 
-// Raises kernel K's dynamic LDS limit once (the default may be below what
-// the activation block needs); one flag per kernel.
+// Raises kernel K's dynamic LDS limit once per process (the default may be
+// below what the activation block needs); the static's initialisation is
+// thread-safe, and a failure shows up as a failed launch.
 template <auto K>
 static void allow_lds(int bytes) {
-  static bool done = false;
-  if (!done) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(K), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    done = true;
-  }
+  static const hipError_t st =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(K), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  (void)st;
 }
 
 template <typename S, bool DUAL>

@@ -267,12 +267,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int sp
 template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX, bool SPLIT, bool PX = false, bool LSE = false>
 static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
   constexpr int STAGE = (BN / 16) * 1024 * (DUAL ? 2 : 1) + BM * 64;
-  static bool attr = false;
-  if (!attr) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX, LSE>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, STAGES * STAGE);
-    attr = true;
-  }
+  // once per process (thread-safe initialisation; a failure shows up as a failed launch)
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX, LSE>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, STAGES * STAGE);
+  (void)attr;
   const int n_ft = (p.N + BN - 1) / BN, n_mt = (p.M + BM - 1) / BM;
   const int grid = ((n_ft + 7) / 8) * 8 * n_mt;
   hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WN, STAGES, DUAL, ARGMAX, SPLIT, PX, LSE>), dim3(grid, splits), dim3(128 * WN),

@@ -158,13 +158,14 @@ void launch_rmsnorm_rows(const NormParams& p, int in_bf16, int out_bf16, hipStre
     shares = shares < p.d / 32 ? shares : p.d / 32;
     const dim3 grid((p.n + 15) / 16, p.segs, shares);
     const size_t lds = (size_t)16 * (64 * ((p.d / 32 + shares - 1) / shares) + 16);
-    static bool attr[2] = {false, false};
-    if (!attr[in_bf16]) {
-      hipFuncSetAttribute(in_bf16 ? reinterpret_cast<const void*>(&rmsnorm_packed_kernel<uint16_t>)
-                                  : reinterpret_cast<const void*>(&rmsnorm_packed_kernel<float>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr[in_bf16] = true;
-    }
+    // once per process per kernel (thread-safe initialisation; a failure
+    // shows up as a failed launch)
+    static const hipError_t attr_bf = hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_packed_kernel<uint16_t>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    static const hipError_t attr_f = hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_packed_kernel<float>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)attr_bf;
+    (void)attr_f;
     if (in_bf16) hipLaunchKernelGGL(rmsnorm_packed_kernel<uint16_t>, grid, dim3(1024), lds, s, p);
     else hipLaunchKernelGGL(rmsnorm_packed_kernel<float>, grid, dim3(1024), lds, s, p);
     return;
