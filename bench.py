@@ -322,7 +322,7 @@ def measure_decode64(dims, W, steps, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np
