@@ -880,9 +880,36 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(const float* pv, const 
   }
 }
 
+// Large batches: 64 rows per workgroup (lane = row, so every load reads 64
+// consecutive rows of one partial), 16 waves taking partials w, w + 16, ...
+// in order, then the waves merged in order through LDS.
+__global__ __launch_bounds__(1024) void lse_reduce_rows_kernel(const float* pv, const float* ps, int P, int M, int N,
+                                                               const int32_t* targets, const float* tgt, float* lse,
+                                                               float* loss) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = blockIdx.x * 64 + lane;
+  const int mc = m < M ? m : M - 1;
+  RowRed rr = RowRed::init();
+  for (int q = wave; q < P; q += 16) rr.merge(true, pv[(int64_t)q * M + mc], 0, ps[(int64_t)q * M + mc]);
+  __shared__ float sv[16][64], ss[16][64];
+  sv[wave][lane] = rr.v;
+  ss[wave][lane] = rr.s;
+  __syncthreads();
+  if (wave == 0 && m < M) {
+    for (int w = 1; w < 16; ++w) rr.merge(true, sv[w][lane], 0, ss[w][lane]);
+    const float l = rr.v + logf(rr.s);
+    if (lse) lse[m] = l;
+    if (loss) loss[m] = (targets && targets[m] >= 0 && targets[m] < N) ? l - tgt[m] : 0.f;
+  }
+}
+
 void launch_lse_reduce(const float* pv, const float* ps, int P, int M, int N, const int32_t* targets,
                        const float* tgt, float* lse, float* loss, hipStream_t s) {
-  hipLaunchKernelGGL(lse_reduce_kernel, dim3(M), dim3(256), 0, s, pv, ps, P, M, N, targets, tgt, lse, loss);
+  if (M >= 1024)
+    hipLaunchKernelGGL(lse_reduce_rows_kernel, dim3((M + 63) / 64), dim3(1024), 0, s, pv, ps, P, M, N, targets, tgt,
+                       lse, loss);
+  else
+    hipLaunchKernelGGL(lse_reduce_kernel, dim3(M), dim3(256), 0, s, pv, ps, P, M, N, targets, tgt, lse, loss);
 }
 
 // ---------------------------------------------------------------------------
