@@ -26,7 +26,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch of the LM-head stage measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE, scaled by a 1 GiB copy (profiles/decode_c1_lm_head_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
-LM_STAGE_TRAFFIC = {"fingerprint": "98805790fd93a1c0", "bytes": 1164121627}
+LM_STAGE_TRAFFIC = {"fingerprint": "9f0dc7ce5bc13bd2", "bytes": 1164103022}
 LM_SOURCES = ("gemm.hip", "norm.hip", "common.h", "kernels.h", "epilogue.h")
 
 

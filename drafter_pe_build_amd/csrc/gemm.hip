@@ -890,7 +890,18 @@ __global__ __launch_bounds__(1024) void lse_reduce_rows_kernel(const float* pv, 
   const int m = blockIdx.x * 64 + lane;
   const int mc = m < M ? m : M - 1;
   RowRed rr = RowRed::init();
-  for (int q = wave; q < P; q += 16) rr.merge(true, pv[(int64_t)q * M + mc], 0, ps[(int64_t)q * M + mc]);
+  // eight partials loaded before they are merged (in partial order)
+  for (int q = wave; q < P; q += 16 * 8) {
+    float v[8], t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int qq = q + 16 * u;
+      v[u] = qq < P ? pv[(int64_t)qq * M + mc] : -INFINITY;
+      t[u] = qq < P ? ps[(int64_t)qq * M + mc] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rr.merge(true, v[u], 0, t[u]);
+  }
   __shared__ float sv[16][64], ss[16][64];
   sv[wave][lane] = rr.v;
   ss[wave][lane] = rr.s;
