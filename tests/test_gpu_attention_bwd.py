@@ -148,3 +148,18 @@ def test_backward_empty_chunk_is_noop():
     L.pe_draft_attention_backward(a, "cuda")
     torch.cuda.synchronize()
     assert bool((dk == 7.0).all()) and bool((dv == 7.0).all())
+
+
+def test_backward_repeats_bit_for_bit():
+    """No atomics and fixed-order reduces: two calls on the same inputs (an
+    N=1,024 layout; every key tile's query tiles are shared by four dK/dV
+    workgroups whose partial sums are added in order) give the same bits."""
+    Lay = si.cod_case(1024, 5, 0.7, 0.5, 31, heads=(32, 8, 128), dtype="bf16")
+    T = Lay["T"]
+    say("bwd repeat N=1024 T=%d" % T)
+    Dv, _ = _upload(Lay, 32)
+    out, lse = _forward(Dv, Lay)
+    a = _backward(Dv, Lay, out, lse, [(0, T)])
+    b = _backward(Dv, Lay, out, lse, [(0, T)])
+    for nm, x, y in zip(("dq", "dk", "dv"), a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32)), nm
