@@ -152,7 +152,7 @@ def measure_attention(cfg, steps, stream):
                            q=q[c0:c1], q_row_stride=Hq * Dh, k=k, v=v, seg_kv_base=base,
                            q_start=start[c0:c1], q_depth=depth[c0:c1], q_self_row=selfr[c0:c1],
                            kv_parent=parent, max_prefix=Lay["N"], out=out[c0:c1], window_sink=sink,
-                           window_len=window) for c0, c1 in chunks]
+                           window_len=window, max_depth=max(1, int(Lay["depth"].max()))) for c0, c1 in chunks]
     wsb = max(L.pe_draft_attention_workspace(a) for a in arglist)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
 
@@ -199,7 +199,7 @@ def measure_anchor(steps, stream):
     a = L.attn_args(num_q=nq, num_seg=1, q_per_seg=nq, num_kv_rows=T, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=Dh,
                     scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16, q=q, q_row_stride=Hq * Dh, k=k, v=v,
                     seg_kv_base=base, q_start=q_start, q_depth=q_depth, q_self_row=q_self, kv_parent=parent,
-                    max_prefix=A["N"], out=out)
+                    max_prefix=A["N"], out=out, max_depth=max(1, int(A["depth"].max())))
     ws = torch.empty(max(L.pe_draft_attention_workspace(a), 256), dtype=torch.uint8, device="cuda")
     msa = time_sustained(lambda: L.pe_draft_attention(a, "cuda", workspace=ws), steps, stream)
     pairs = int(np.sum(A["start"][qr].astype(np.int64) + 1 + A["depth"][qr]))
@@ -237,7 +237,7 @@ def measure_backward(steps, stream):
     fa = L.attn_args(num_q=T, num_seg=1, q_per_seg=T, num_kv_rows=T, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=Dh,
                      scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16, q=q, q_row_stride=Hq * Dh, k=k, v=v,
                      seg_kv_base=base, q_start=start, q_depth=depth, q_self_row=selfr, kv_parent=parent,
-                     max_prefix=Lay["N"], out=out, lse=lse)
+                     max_prefix=Lay["N"], out=out, lse=lse, max_depth=max(1, int(Lay["depth"].max())))
     L.pe_draft_attention(fa, "cuda")
     dout = torch.randn((T, Hq, Dh), dtype=torch.float32, device="cuda").to(torch.bfloat16)
     dq = torch.empty((T, Hq, Dh), dtype=torch.float32, device="cuda")

@@ -48,7 +48,8 @@ class PeAttnArgs(ctypes.Structure):
                 ("k", c_void_p), ("v", c_void_p), ("seg_kv_base", c_void_p), ("q_start", c_void_p),
                 ("q_depth", c_void_p), ("q_self_row", c_void_p), ("kv_parent", c_void_p),
                 ("max_prefix", c_int32), ("split_len", c_int32), ("out", c_void_p), ("lse", c_void_p),
-                ("dbg_count", c_void_p), ("dbg_hash", c_void_p), ("window_sink", c_int32), ("window_len", c_int32)]
+                ("dbg_count", c_void_p), ("dbg_hash", c_void_p), ("window_sink", c_int32), ("window_len", c_int32),
+                ("max_depth", c_int32)]
 
 
 class PeAttnBwdArgs(ctypes.Structure):

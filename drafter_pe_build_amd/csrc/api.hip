@@ -98,7 +98,10 @@ pe_status check_attn(const pe_attn_args* a) {
   if (a->window_len > 0 && a->split_len > 0) return PE_ERR_UNSUPPORTED;  // a window is never split
   if (a->num_q == 0) return PE_OK;
   if (!a->q || !a->k || !a->v || !a->seg_kv_base || !a->q_start || !a->out) return PE_ERR_INVALID_ARG;
-  if (a->q_depth && (!a->q_self_row || !a->kv_parent)) return PE_ERR_INVALID_ARG;
+  if (a->q_depth) {
+    if (!a->q_self_row || !a->kv_parent || a->max_depth < 1) return PE_ERR_INVALID_ARG;
+    if (a->max_depth > attn_max_depth(G)) return PE_ERR_UNSUPPORTED;
+  }
   if ((a->dbg_count == nullptr) != (a->dbg_hash == nullptr)) return PE_ERR_INVALID_ARG;
   if (a->q_row_stride < (int64_t)a->n_q_heads * a->head_dim) return PE_ERR_INVALID_ARG;
   const int ch = a->dtype == PE_BF16 ? 8 : 4;
@@ -151,6 +154,7 @@ pe_status run_attention(const pe_attn_args* a, void* ws, size_t ws_bytes, int me
   p.q_depth = a->q_depth;
   p.q_self_row = a->q_self_row;
   p.kv_parent = a->kv_parent;
+  p.max_depth = a->q_depth ? a->max_depth : 0;
   p.n_splits = n_splits;
   p.split_len = split_len;
   p.win_sink = a->window_sink;

@@ -55,6 +55,7 @@ constexpr int MAXD = 16;        // deepest chain walked per query
 constexpr int ANC_MAX = 1024;   // chain rows gathered per workgroup
 
 int attn_queries_per_workgroup(int G, int) { return QMAX / G; }
+int attn_max_depth(int G) { return MAXD < ANC_MAX / (QMAX / G) ? MAXD : ANC_MAX / (QMAX / G); }
 
 // Maxima of scores, which are products or -inf and never signalling NaNs:
 // the plain instructions, without the quieting copies the compiler adds to
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   const int r = lane & 15, g = lane >> 4;
   const int Hkv = p.Hkv, Hq = p.Hq;
   const int QPW = QMAX / G;
-  const int maxd = min(MAXD, ANC_MAX / QPW);
+  const int maxd = min(p.max_depth, min(MAXD, ANC_MAX / QPW));  // the host checked the bound
 
   int bid = blockIdx.x;
   const int kvh = bid % Hkv;

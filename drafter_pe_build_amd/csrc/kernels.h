@@ -153,6 +153,7 @@ struct AttnParams {
   int num_q, num_seg, q_per_seg, num_kv_rows, Hq, Hkv;
   float scale, scale_log2;
   const int32_t *seg_kv_base, *q_start, *q_depth, *q_self_row, *kv_parent;
+  int max_depth;  // chain rows walked per query at most (<= attn_max_depth(G))
   int n_splits, split_len;
   void* out;
   float* lse;
@@ -184,5 +185,8 @@ int64_t attn_bwd_part_floats(int T, int D, int Hkv, int head_dim);
 // Queries one attention workgroup takes: 128 (query, head) columns of one kv
 // head, i.e. 128 / (n_q_heads / n_kv_heads) queries.
 int attn_queries_per_workgroup(int G, int head_dim);
+// Deepest chain one query may walk: 16, or fewer when a workgroup's queries
+// could gather more chain rows than its LDS list holds (8 at G = 1).
+int attn_max_depth(int G);
 
 }  // namespace pe

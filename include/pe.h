@@ -250,9 +250,8 @@ typedef struct {
     const void* v;          /* [num_kv_rows, Hkv, Dh]                          */
     const int32_t* seg_kv_base;  /* [num_seg]                                  */
     const int32_t* q_start;      /* [num_q] last prefix offset (-1 = none)     */
-    const int32_t* q_depth;      /* [num_q] or NULL (all 0); at most 16 (8 when
-                                    n_q_heads == n_kv_heads); deeper chains
-                                    are cut at that depth                      */
+    const int32_t* q_depth;      /* [num_q] or NULL (all 0); each value at
+                                    most max_depth                             */
     const int32_t* q_self_row;   /* [num_q] or NULL when q_depth is NULL       */
     const int32_t* kv_parent;    /* [num_kv_rows] or NULL when q_depth is NULL */
     int32_t max_prefix;     /* host bound on 1 + max q_start (work split only;
@@ -274,6 +273,17 @@ typedef struct {
                                is never split (split_len must be 0, else
                                PE_ERR_UNSUPPORTED).                          */
     int32_t window_len;
+    int32_t max_depth;      /* host bound on every q_depth[i] (ignored when
+                               q_depth is NULL): the kernel walks at most
+                               max_depth chain rows per query.  Required in
+                               1..16 with q_depth (1..8 when n_q_heads ==
+                               n_kv_heads: a workgroup of 128 single-head
+                               queries gathers at most 1,024 chain rows);
+                               0 or negative with q_depth is
+                               PE_ERR_INVALID_ARG, above the kernel's bound
+                               PE_ERR_UNSUPPORTED.  A q_depth[i] above the
+                               stated bound breaks this contract: its walk
+                               stops at max_depth rows.                      */
 } pe_attn_args;
 
 /*

@@ -15,8 +15,8 @@ Sources cited in this package, by title:
         CUDA graphs).
 * [RFC] vllm-project/speculators issue #567, "[RFC]: Add random anchor for
         p-eagle first position": "Motivation", "Proposed Change", the
-        "Random Anchor Subsampling" note that depth 0 is always the full
-        sequence, and the "Experiment Setup" table.
+        "Random Anchor Subsampling" note (every original position is a
+        depth-0 row), and the "Experiment Setup" table.
 * [AD]  "Attention Drift: what autoregressive speculative-decoding models
         learn" (arXiv 2605.09992): section 2 (EAGLE-3 drafter: fc fusion into
         one pre-norm decoder layer), section 4.1 (RMS = ||x||_2 / sqrt(d)) and

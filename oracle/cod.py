@@ -4,7 +4,7 @@
 position, then the token after that for a kept fraction of those chains
 (e.g. 70%), then the third token for the kept fraction of those, and so on;
 the layout therefore holds N * sum_{n<D} p^n positions.  [RFC] "Random
-Anchor Subsampling": depth 0 is always the full sequence.  [RFC] "Proposed
+Anchor Subsampling": every original position is a depth-0 query and key.  [RFC] "Proposed
 Change": only loss-mask=1 positions start chains at depth >= 1.
 [RFC] "Proposed Change" (max_anchors): chains start only from a random
 subset of the loss-mask=1 positions and only those anchors' rows are

@@ -135,6 +135,18 @@ def test_attention_validation_and_workspace():
         assert lib.pe_draft_attention_backward(ctypes.byref(b3), FAKE, 1 << 20, None) == code, kw
     assert lib.pe_draft_attention_backward(ctypes.byref(L.attn_bwd_args(**{**bw, "q_begin": 7, "q_end": 7})),
                                            None, 0, None) == 0
+    # chain depth: a host bound is required with q_depth and must fit the kernel's
+    # chain list (16 rows, 8 when every query head has its own kv head)
+    chain = dict(q_depth=FAKE, q_self_row=FAKE, kv_parent=FAKE)
+    for kw, code in ((dict(max_depth=0), 1), (dict(max_depth=-2), 1), (dict(max_depth=17), 2),
+                     (dict(max_depth=16), 0), (dict(max_depth=1), 0),
+                     (dict(max_depth=9, n_q_heads=8, n_kv_heads=8, q_row_stride=512), 2),
+                     (dict(max_depth=8, n_q_heads=8, n_kv_heads=8, q_row_stride=512), 0),
+                     (dict(max_depth=16, n_q_heads=16, n_kv_heads=8, q_row_stride=1024), 0)):
+        a5 = L.attn_args(**{**base, **chain, **kw})
+        assert lib.pe_draft_attention_workspace(ctypes.byref(a5), ctypes.byref(n)) == code, kw
+        if code:
+            assert lib.pe_draft_attention(ctypes.byref(a5), FAKE, 1 << 30, None) == code, kw
     a4 = L.attn_args(**{**base, "window_sink": 256, "window_len": 2048})
     assert lib.pe_draft_attention_workspace(ctypes.byref(a4), ctypes.byref(n)) == 0
     assert n.value == 16

@@ -69,7 +69,8 @@ def run_cod(D, Lay, c0=0, c1=None, out=None, lse=None, dbg=True, split_len=0, si
                     q=D["q"][c0:c1], q_row_stride=Hq * Dh, k=D["k"], v=D["v"], seg_kv_base=D["base"],
                     q_start=D["start"][c0:c1], q_depth=D["depth"][c0:c1], q_self_row=D["self_row"][c0:c1],
                     kv_parent=D["parent"], max_prefix=Lay["N"], split_len=split_len, out=out, lse=lse,
-                    dbg_count=cnt, dbg_hash=hsh, window_sink=sink, window_len=window)
+                    dbg_count=cnt, dbg_hash=hsh, window_sink=sink, window_len=window,
+                    max_depth=max(1, int(Lay["depth"].max())))
     L.pe_draft_attention(a, "cuda")
     return out, lse, cnt, hsh
 
@@ -218,7 +219,8 @@ def run_anchor(D, A, dbg=True, split_len=0):
                     scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16 if D["dtype"] == "bf16" else L.PE_F32,
                     q=D["q"], q_row_stride=Hq * Dh, k=D["k"], v=D["v"], seg_kv_base=D["base"],
                     q_start=D["q_start"], q_depth=D["q_depth"], q_self_row=D["q_self"], kv_parent=D["parent"],
-                    max_prefix=A["N"], split_len=split_len, out=out, lse=lse, dbg_count=cnt, dbg_hash=hsh)
+                    max_prefix=A["N"], split_len=split_len, out=out, lse=lse, dbg_count=cnt, dbg_hash=hsh,
+                    max_depth=max(1, int(A["depth"].max())))
     L.pe_draft_attention(a, "cuda")
     return out, lse, cnt, hsh
 

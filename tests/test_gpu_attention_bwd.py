@@ -45,7 +45,8 @@ def _forward(D, Lay):
     a = L.attn_args(num_q=T, num_seg=1, q_per_seg=T, num_kv_rows=T, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=Dh,
                     scale=1.0 / np.sqrt(Dh), dtype=L.PE_BF16, q=D["q"], q_row_stride=Hq * Dh, k=D["k"], v=D["v"],
                     seg_kv_base=D["base"], q_start=D["start"], q_depth=D["depth"], q_self_row=D["self_row"],
-                    kv_parent=D["parent"], max_prefix=Lay["N"], out=out, lse=lse)
+                    kv_parent=D["parent"], max_prefix=Lay["N"], out=out, lse=lse,
+                    max_depth=max(1, int(Lay["depth"].max())))
     L.pe_draft_attention(a, "cuda")
     return out, lse
 

@@ -220,6 +220,30 @@ def test_mix64_reference_values():
     assert [hex(int(x)) for x in outs] == ["0xe220a8397b1dcdaf", "0x6e789e6aa1b965f4", "0x6c45d188009454f"]
 
 
+def _mix64_int(x):
+    """SplitMix64 output in Python integers (mod 2^64), written out apart from oc.mix64."""
+    m = (1 << 64) - 1
+    z = (x + 0x9E3779B97F4A7C15) & m
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & m
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+    return z ^ (z >> 31)
+
+
+@pytest.mark.parametrize("seg_base,P", [(0, 0), (0, 5), (37, 0), (37, 12), (1000, 63), (123456, 64)])
+def test_region_index_stats_pinned(seg_base, P):
+    # A decode query at position P sees rows seg_base + 0..P of its region:
+    # count P + 1, and the hash equals the predicate-based index_stats of a
+    # one-depth layout (start j at row j, the same keys by the visibility
+    # predicate) placed at row offset seg_base, and a Python-integer sum.
+    cnt, hsh = oc.region_index_stats(seg_base, P)
+    assert cnt == P + 1
+    L = P + 3                                     # rows after P must stay invisible
+    c2, h2 = oc.index_stats(np.arange(L), np.zeros(L, int), queries=[P], row_offset=seg_base)
+    assert int(c2[0]) == cnt and h2[0] == hsh
+    ref = sum(_mix64_int(seg_base + j) for j in range(P + 1)) & ((1 << 64) - 1)
+    assert int(hsh) == ref
+
+
 # ---- random anchors (max_anchors): a query subset against the full sequence
 
 def test_anchor_rows_hand_example():
