@@ -182,7 +182,7 @@ int zero_ints(size_t max_k_bytes) { return (int)((max_k_bytes + 255) / 256 * 64)
 
 // Workspace of the drafter layer.
 struct LayerWs {
-  void *a, *q, *o, *b, *h, *attn;
+  void *a, *q, *o, *b, *h, *h_lo, *attn;
   float* x1;
   float* split;  // K-split partial products of the large-M contractions
   int64_t split_bytes;
@@ -206,6 +206,9 @@ LayerWs layer_ws(const pe_drafter_dims* d, int T, int R, int K, int max_pos, voi
   w.x1 = static_cast<float*>(c.take((size_t)RK * d->hidden * 4));
   w.b = c.take((size_t)RK * d->hidden * e);
   w.h = c.take((size_t)RK * d->ffn * e);
+  // remainder of the SwiGLU output: the down projection's second operand part
+  // (weight-streaming batches of bf16 rows only)
+  w.h_lo = (RK <= 16 && d->dtype == PE_BF16) ? c.take((size_t)RK * d->ffn * e) : nullptr;
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
   const int G = d->n_q_heads / d->n_kv_heads;
   const int QPW = attn_queries_per_workgroup(G, d->head_dim);
@@ -225,6 +228,7 @@ LayerWs layer_ws(const pe_drafter_dims* d, int T, int R, int K, int max_pos, voi
 // Workspace of the fc fusion.
 struct FuseWs {
   void* u;
+  float* inv;  // deferred 1 / rms per (row, stream) when a norm kernel runs first
   float* split;  // K-split partial products of a large-M fc
   int64_t split_bytes;
   int* zero;
@@ -237,6 +241,7 @@ FuseWs fuse_ws(const pe_drafter_dims* d, int T, void* base) {
   Carver c(base);
   w.nzero = zero_ints((size_t)3 * d->hidden * esize(d->dtype));
   w.u = c.take((size_t)((T + 15) / 16 * 16) * 3 * d->hidden * esize(d->dtype));  // rows padded to 16
+  w.inv = static_cast<float*>(c.take((size_t)T * 3 * 4));
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
   w.split_bytes = d->dtype == PE_BF16 ? gemm_split_bytes(T, d->hidden) : 0;
   w.split = static_cast<float*>(c.take((size_t)w.split_bytes));
@@ -249,7 +254,7 @@ FuseWs fuse_ws(const pe_drafter_dims* d, int T, void* base) {
 struct LmWs {
   void* f;
   float* pv;
-  int32_t* pi;
+  u32x4* top2;
   float* ps;
   float* tgt;
   int* zero;
@@ -262,12 +267,12 @@ LmWs lm_ws(const pe_drafter_dims* d, int n, void* base, bool loss = false) {
   Carver c(base);
   const size_t P = (size_t)gemm_argmax_partials(n, d->vocab);
   w.f = c.take((size_t)((n + 15) / 16 * 16) * d->hidden * esize(d->dtype));  // rows padded to 16 (operand layout)
-  w.pv = static_cast<float*>(c.take(P * n * 4));
   if (loss) {
+    w.pv = static_cast<float*>(c.take(P * n * 4));
     w.ps = static_cast<float*>(c.take(P * n * 4));
     w.tgt = static_cast<float*>(c.take((size_t)n * 4));
   } else {
-    w.pi = static_cast<int32_t*>(c.take(P * n * 4));
+    w.top2 = static_cast<u32x4*>(c.take(P * n * 16));
   }
   w.nzero = zero_ints((size_t)d->hidden * esize(d->dtype));
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
@@ -424,6 +429,11 @@ pe_status pe_fuse_hidden(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.nrm.eps = dims->eps;
   gp.nrm.skip = rejected;
   gp.nrm.tmp = fw.u;
+  // each stream's 1 / rms scales its share of the sum after the contraction:
+  // the operand is then the captured bf16 rows times their gains (the rows
+  // themselves for unit gains), with no rounding of the normalised values
+  gp.nrm.defer = 1;
+  gp.nrm.inv_tmp = fw.inv;
   gp.clear = fw.zero;
   gp.nclear = fw.nzero;
   gp.split_ws = fw.split;
@@ -580,14 +590,19 @@ pe_status pe_draft_layer(const pe_drafter_dims* dims, const pe_drafter_weights* 
   gp.nrm.eps = dims->eps;
   gp.nrm.x_f32 = 1;
   gp.nrm.tmp = lw.b;
+  // weight-streaming batches: the normalised rows and their remainder as two
+  // bf16 operand parts, and the output's remainder for the down projection
+  gp.x_split = lw.h_lo != nullptr;
   gp.epi.kind = EPI_SWIGLU;
   gp.epi.out_s = lw.h;
+  gp.epi.out_s_lo = lw.h_lo;
   gp.epi.ld_out = F;
   launch_gemm(gp, bf, stream);
 
   // x_out = x1 + W_down h
   gp = GemmParams{};
   gp.X = lw.h;
+  gp.x_lo = lw.h_lo;
   gp.ldx = F;
   gp.W = w->w_down;
   gp.M = RK;
@@ -620,7 +635,8 @@ pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weight
   if (st != PE_OK) return st;
   if (!w || n < 0) return PE_ERR_INVALID_ARG;
   if (n == 0) return PE_OK;
-  if (!x || !tokens || !w->final_gain || !w->w_lm || !al16(w->w_lm) || !al16(x)) return PE_ERR_INVALID_ARG;
+  if (!x || !tokens || !w->final_gain || !w->w_lm || !al16(w->w_lm) || !al16(x) || !al16(w->final_gain))
+    return PE_ERR_INVALID_ARG;
   if (!ws_ok(workspace, workspace_bytes, lm_ws(dims, n, nullptr).total)) return PE_ERR_INVALID_ARG;
   const LmWs lw = lm_ws(dims, n, workspace);
   const int d = dims->hidden;
@@ -644,10 +660,10 @@ pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weight
   gp.nclear = lw.nzero;
   gp.epi.kind = EPI_ARGMAX;
   gp.epi.logits = logits;
-  gp.epi.part_val = lw.pv;
-  gp.epi.part_idx = lw.pi;
+  gp.epi.part_top2 = lw.top2;
   const int used = launch_gemm(gp, bf, stream);
-  launch_argmax_reduce(lw.pv, lw.pi, used, n, tokens, stream);
+  // the two leading tokens of each row, scored again in fp32 from x
+  launch_argmax_rescore(lw.top2, used, n, x, d, w->final_gain, dims->eps, w->w_lm, d, bf, tokens, stream);
   return launched();
 }
 

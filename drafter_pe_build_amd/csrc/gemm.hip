@@ -121,7 +121,9 @@ struct CopyStage {
 // The gains (segs * seg_len floats) are copied to LDS at xg by all threads
 // in the same first round.  All global reads are unconditional 16-byte loads
 // (indices clamped), so none of them waits behind a branch.  finish() has a
-// barrier between the gain copy and its use.
+// barrier between the gain copy and its use.  With p.nrm.defer the rows are
+// written as x * g and each (row, segment)'s 1 / rms goes to the float array
+// after the gains (index row * segs + seg), for the contraction to apply.
 template <typename S, typename XT, int NC>
 struct NormStage {
   static constexpr int CI = 16 / sizeof(XT);  // elements per chunk
@@ -167,7 +169,10 @@ struct NormStage {
       }
     }
     ss = wave_sum(ss);
-    const float inv = skip ? 0.f : 1.0f / sqrtf(ss / (float)sl + p.nrm.eps);
+    const float inv0 = skip ? 0.f : 1.0f / sqrtf(ss / (float)sl + p.nrm.eps);
+    if (p.nrm.defer && lane == 0)
+      reinterpret_cast<float*>(const_cast<char*>(xg) + segs * sl * 4)[row * segs + seg] = inv0;
+    const float inv = p.nrm.defer ? 1.f : inv0;
     char* dst = xs + row * xp + seg * sl * (int)sizeof(S);
     const char* gsrc = xg + seg * sl * 4;
 #pragma unroll
@@ -239,8 +244,16 @@ __device__ __forceinline__ void clear_ints(const GemmParams& p) {
 // the loop has no data-dependent branch.  The KS partial tiles are summed
 // through LDS in ks order.  No cross-workgroup reduction: a device-scope
 // fence on MI355X writes back the XCD's L2 and stalls the stream.
-template <typename S, int KS, int U, bool DUAL>
+// LOM: the operand is X + p.x_lo.  1: each weight chunk multiplied by both
+// parts; 2 (M <= 8): the remainder rows take columns 8..15 of the 16-row
+// operand (lane r >= 8 reads row r - 8 of x_lo), one matrix-core step per
+// chunk, and the two halves of the result tile are added at the end.
+// p.xinv: deferred 1 / rms per (row, segment); KS is then a multiple of the
+// segment count, so every wave's steps lie in one segment and its partial
+// tile is scaled before the reduction.
+template <typename S, int KS, int U, bool DUAL, int LOM>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmParams p) {
+  constexpr bool LO = LOM == 1;
   constexpr int CH = Storage<S>::CH;
   constexpr int STEP = 4 * CH;
   const int lane = threadIdx.x & 63;
@@ -251,29 +264,44 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmParams p) {
   const int fb = blockIdx.x;
   const int s0 = (int)((int64_t)nsteps * ks / KS);
   const int s1 = (int)((int64_t)nsteps * (ks + 1) / KS);
-  const bool xr = r < M;
+  const int rm = LOM == 2 ? (r & 7) : r;  // activation row of this lane
+  const bool xr = rm < M;
   // padding rows of the 16-row B operand read a zeroed buffer: no branch in the loop
-  const S* xrow = (xr ? reinterpret_cast<const S*>(p.X) + (int64_t)r * p.ldx : reinterpret_cast<const S*>(p.xzero)) + g * CH;
+  const S* xsrc = reinterpret_cast<const S*>(LOM == 2 && r >= 8 ? p.x_lo : p.X);
+  const S* xrow = (xr ? xsrc + (int64_t)rm * p.ldx : reinterpret_cast<const S*>(p.xzero)) + g * CH;
+  const S* xlrow = (xr && LO ? reinterpret_cast<const S*>(p.x_lo) + (int64_t)r * p.ldx : reinterpret_cast<const S*>(p.xzero)) + g * CH;
   const char* wb = reinterpret_cast<const char*>(p.W) + (int64_t)fb * nsteps * 1024 + lane * 16;
   const char* wb2 = reinterpret_cast<const char*>(p.W2) + (int64_t)fb * nsteps * 1024 + lane * 16;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
   for (int s = s0; s < s1; s += U) {
-    u32x4 wv[U], w2v[U], xv[U];
+    u32x4 wv[U], w2v[U], xv[U], xl[LO ? U : 1];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int su = min(s + u, s1 - 1);
       wv[u] = ld16(wb + (int64_t)su * 1024);
       if constexpr (DUAL) w2v[u] = ld16(wb2 + (int64_t)su * 1024);
       xv[u] = ld16(xrow + su * STEP);
+      if constexpr (LO) xl[u] = ld16(xlrow + su * STEP);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s + u < s1) {
         mma16(acc, wv[u], xv[u], S());
         if constexpr (DUAL) mma16(acc2, w2v[u], xv[u], S());
+        if constexpr (LO) {
+          mma16(acc, wv[u], xl[u], S());
+          if constexpr (DUAL) mma16(acc2, w2v[u], xl[u], S());
+        }
       }
     }
+  }
+  if (p.xinv) {
+    // the segment of this wave's steps (all of them lie in one)
+    const int seg = min(s0 * STEP / (K / p.xinv_segs), p.xinv_segs - 1);
+    const float sc = xr ? p.xinv[r * p.xinv_segs + seg] : 0.f;
+    acc *= sc;
+    acc2 *= sc;
   }
   if constexpr (KS > 1) {
     __shared__ f32x4 red[(KS - 1) * 64 * (DUAL ? 2 : 1)];
@@ -289,7 +317,15 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmParams p) {
       if constexpr (DUAL) acc2 += red[((KS - 1) + k) * 64 + lane];
     }
   }
-  if (xr) {
+  if constexpr (LOM == 2) {
+    // column r + 8 holds the remainder part of row r
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] += __shfl_down(acc[j], 8, 64);
+      if constexpr (DUAL) acc2[j] += __shfl_down(acc2[j], 8, 64);
+    }
+  }
+  if (r < M) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = fb * 16 + 4 * g + j;
@@ -308,8 +344,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmParams p) {
 // the sum of squares of its elements, and the workgroup sums the partial
 // tiles and partial sums of squares through LDS in a fixed order before the
 // epilogue scales by inv.  The gain reads go out before the first weight
-// batch, so waiting for them never waits for it.
-template <typename S, int KS, int U, bool DUAL>
+// batch, so waiting for them never waits for it.  HL (bf16): the operand is
+// X * g as a bf16 value plus the bf16 of its remainder, two matrix-core
+// steps per weight chunk, so the rounding of the float rows drops from 2^-9
+// to about 2^-17 relative.
+template <typename S, int KS, int U, bool DUAL, bool HL>
 __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(4)))
 void gemm_stream_fnorm_kernel(GemmParams p) {
   constexpr int CH = Storage<S>::CH;  // operand elements per lane per step
@@ -388,6 +427,17 @@ void gemm_stream_fnorm_kernel(GemmParams p) {
         if (skip) b = u32x4{0u, 0u, 0u, 0u};  // rejected rows contribute zeros whatever they hold
         mma16(acc, wv[u], b, S());
         if constexpr (DUAL) mma16(acc2, w2v[u], b, S());
+        if constexpr (HL && CH == 8) {
+          // remainder y - bf16(y) of each element (exact in fp32), rounded to bf16
+          float lo[CH];
+#pragma unroll
+          for (int e = 0; e < CH; ++e) lo[e] = y[e] - bf2f((uint16_t)(b[e >> 1] >> (16 * (e & 1))));
+          u32x4 bl = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]),
+                      pack_bf16x2(lo[6], lo[7])};
+          if (skip) bl = u32x4{0u, 0u, 0u, 0u};
+          mma16(acc, wv[u], bl, S());
+          if constexpr (DUAL) mma16(acc2, w2v[u], bl, S());
+        }
       }
     }
     s += U;
@@ -433,7 +483,10 @@ void gemm_stream_fnorm_kernel(GemmParams p) {
 // the registers allow), so the staging hides under the weight stream's first
 // round trip; afterwards batch j+2 is in flight while batch j is multiplied.
 // At most 128 registers per lane: two 512-thread workgroups per CU, so the
-// 320-640 workgroups of the wide projections are resident at once.
+// 320-640 workgroups of the wide projections are resident at once.  With a
+// deferred norm (p.nrm.defer) KS is a multiple of the segment count, every
+// wave's steps lie in one segment, and its partial tile is scaled by that
+// segment's 1 / rms before the reduction.
 template <typename S, typename XT, int KS, int U, bool DUAL, bool NORM, bool EARLY2>
 __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(4)))
 void gemm_stream_lds_kernel(GemmParams p) {
@@ -480,6 +533,12 @@ void gemm_stream_lds_kernel(GemmParams p) {
   const bool xr = r < M;
   const char* xrow = xr ? xs + r * xp + g * 16 : xs + M * xp;  // padding rows: the zero chunk
   const int xstep = xr ? STEP * (int)sizeof(S) : 0;
+  float sc = 1.f;  // deferred 1 / rms of this wave's segment
+  if (NORM && p.nrm.defer) {
+    const int segs = p.nrm.segs;
+    const float* sinv = reinterpret_cast<const float*>(xs + M * xp + 16 + segs * p.nrm.seg_len * 4);
+    sc = xr ? sinv[r * segs + min(s0 * STEP / p.nrm.seg_len, segs - 1)] : 0.f;
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
   auto batch = [&](int j, int slot) {
 #pragma unroll
@@ -499,6 +558,10 @@ void gemm_stream_lds_kernel(GemmParams p) {
       batch(j + 1, 1);
       if (j + 3 < nb) wload(j + 3, 1);
     }
+  }
+  if (NORM && p.nrm.defer) {
+    acc *= sc;
+    acc2 *= sc;
   }
   if constexpr (KS > 1) {
     // the K-split partial tiles reuse the staged rows' LDS once every wave is done with them
@@ -647,16 +710,22 @@ void lm_argmax_stream_kernel(GemmParams p) {
     }
   }
   rr.merge_groups(LSE);
-  __shared__ float sbv[NW][16], sbs[NW][16];
-  __shared__ int sbi[NW][16];
-  if (g == 0) { sbv[wave][r] = rr.v; sbi[wave][r] = rr.i; sbs[wave][r] = rr.s; }
+  __shared__ u32x4 sb[NW][16];  // per wave and row: (v, s) or the top-2 list
+  if (g == 0) sb[wave][r] = LSE ? u32x4{__float_as_uint(rr.v), 0u, __float_as_uint(rr.s), 0u} : rr.pack2();
   __syncthreads();
   if ((int)threadIdx.x < M) {
     RowRed t = RowRed::init();
-    for (int w = 0; w < NW; ++w) t.merge(LSE, sbv[w][threadIdx.x], sbi[w][threadIdx.x], sbs[w][threadIdx.x]);
-    p.epi.part_val[(int64_t)blockIdx.x * M + threadIdx.x] = t.v;
-    if (LSE) p.epi.part_sum[(int64_t)blockIdx.x * M + threadIdx.x] = t.s;
-    else p.epi.part_idx[(int64_t)blockIdx.x * M + threadIdx.x] = t.i;
+    for (int w = 0; w < NW; ++w) {
+      const u32x4 o = sb[w][threadIdx.x];
+      if (LSE) t.merge(true, __uint_as_float(o[0]), 0, __uint_as_float(o[2]));
+      else t.merge_packed(o);
+    }
+    if (LSE) {
+      p.epi.part_val[(int64_t)blockIdx.x * M + threadIdx.x] = t.v;
+      p.epi.part_sum[(int64_t)blockIdx.x * M + threadIdx.x] = t.s;
+    } else {
+      p.epi.part_top2[(int64_t)blockIdx.x * M + threadIdx.x] = t.pack2();
+    }
   }
 }
 
@@ -766,8 +835,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft,
 
   if constexpr (ARGMAX) {
     // argmax (EPI_ARGMAX) or log-sum-exp (EPI_LSE, LSE set) partials of this tile's rows
-    __shared__ float sbv[2][BM], sbs[2][BM];
-    __shared__ int sbi[2][BM];
+    __shared__ u32x4 sb[2][BM];  // per wave column and row: (v, s) or the top-2 list
 #pragma unroll
     for (int q = 0; q < RBW; ++q) {
       const int mloc = wm * (BM / 2) + q * 16 + r;
@@ -785,24 +853,29 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft,
             if (p.epi.logits) p.epi.logits[(int64_t)m * N + n] = v;
             if constexpr (LSE) {
               if (n == tgt) p.epi.tgt_logit[m] = v;
+              rr.add(true, v, n);
+            } else {
+              rr.add1(v, n);  // the lane's largest; the merges keep the top two of those
             }
-            rr.add(LSE, v, n);
           }
         }
       rr.merge_groups(LSE);
-      if (g == 0) {
-        sbv[wn][mloc] = rr.v;
-        if constexpr (LSE) sbs[wn][mloc] = rr.s;
-        else sbi[wn][mloc] = rr.i;
-      }
+      if (g == 0) sb[wn][mloc] = LSE ? u32x4{__float_as_uint(rr.v), 0u, __float_as_uint(rr.s), 0u} : rr.pack2();
     }
     __syncthreads();
     if (tid < BM && m0 + tid < M) {
-      RowRed rr{sbv[0][tid], LSE ? sbs[0][tid] : 0.f, LSE ? 0 : sbi[0][tid]};
-      rr.merge(LSE, sbv[1][tid], LSE ? 0 : sbi[1][tid], LSE ? sbs[1][tid] : 0.f);
-      p.epi.part_val[(int64_t)ft * M + m0 + tid] = rr.v;
-      if constexpr (LSE) p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
-      else p.epi.part_idx[(int64_t)ft * M + m0 + tid] = rr.i;
+      RowRed rr = RowRed::init();
+      for (int w = 0; w < 2; ++w) {
+        const u32x4 o = sb[w][tid];
+        if constexpr (LSE) rr.merge(true, __uint_as_float(o[0]), 0, __uint_as_float(o[2]));
+        else rr.merge_packed(o);
+      }
+      if constexpr (LSE) {
+        p.epi.part_val[(int64_t)ft * M + m0 + tid] = rr.v;
+        p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
+      } else {
+        p.epi.part_top2[(int64_t)ft * M + m0 + tid] = rr.pack2();
+      }
     }
   } else {
 #pragma unroll
@@ -818,42 +891,132 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft,
   }
 }
 
-__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* pv, const int32_t* pi, int P, int M,
-                                                            int32_t* tokens) {
-  const int m = blockIdx.x;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int q = threadIdx.x; q < P; q += 4 * 256) {
-    float v[4];
-    int ix[4];
+// Greedy token of row m (one workgroup per row).  The partial lists are
+// merged into the row's two leading kernel logits; the order is total (value,
+// then lower index), so the result does not depend on the merge order.  The
+// weight-streaming kernel's lists are the exact two largest of its features;
+// the tiled kernels keep the two largest of their lanes' maxima (16 features
+// per lane and row), so the pair is the row's two largest unless both of
+// those share one lane of one tile, where the first alone decides.  The
+// kernel's logits use the normalised row rounded to the operand type; the two
+// candidates are scored again here in fp32 from the float row,
+//   z_c = inv * sum_k W[c][k] * (x[k] * g[k]),  inv = 1 / sqrt(mean_k x[k]^2 + eps),
+// with every sum taken in a fixed order, and the larger (lower index on a tie)
+// is the token.  The rounding of the operand moves a bf16 logit by about
+// 2e-3 at hidden 2880 and unit-scale rows; the re-score removes that part of
+// the error from the decision between the two leading tokens.
+template <typename S>
+__global__ __launch_bounds__(256) void argmax_rescore_kernel(const u32x4* part, int P, int M, const float* x,
+                                                             int64_t ldx, const float* gain, float eps,
+                                                             const char* W, int K, int32_t* tokens) {
+  constexpr int CH = Storage<S>::CH;  // elements per 16-byte chunk
+  constexpr int STEP = 4 * CH;        // elements per packed 1 KB step of a 16-row block
+  constexpr int NPRE = 2;             // chunks per thread held from before the merge (K <= 512 CH)
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = K / CH;
+  const float* xr = x + (int64_t)m * ldx;
+  // the row and its gains first, so that their loads overlap the partials'
+  f32x4 xv[NPRE][CH / 4], gv[NPRE][CH / 4];
+  float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+  for (int c = 0; c < NPRE; ++c) {
+    const int ch = tid + 256 * c;
+#pragma unroll
+    for (int q = 0; q < CH / 4; ++q) {
+      xv[c][q] = ch < nch ? *reinterpret_cast<const f32x4*>(xr + ch * CH + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+      gv[c][q] = ch < nch ? *reinterpret_cast<const f32x4*>(gain + ch * CH + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  const u32x4 none = {__float_as_uint(-INFINITY), 0x7fffffffu, __float_as_uint(-INFINITY), 0x7fffffffu};
+  RowRed rr = RowRed::init();
+  for (int q = tid; q < P; q += 8 * 256) {  // up to 2,048 partials in one round of loads
+    u32x4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
       const int qq = q + 256 * u;
-      v[u] = qq < P ? pv[(int64_t)qq * M + m] : -INFINITY;
-      ix[u] = qq < P ? pi[(int64_t)qq * M + m] : 0x7fffffff;
+      t[u] = qq < P ? part[(int64_t)qq * M + m] : none;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (better(v[u], ix[u], bv, bi)) { bv = v[u]; bi = ix[u]; }
+    for (int u = 0; u < 8; ++u) rr.merge_packed(t[u]);
   }
+#pragma unroll
+  for (int c = 0; c < NPRE; ++c)
+#pragma unroll
+    for (int q = 0; q < CH / 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += xv[c][q][e] * xv[c][q][e];
+  for (int ch = tid + 256 * NPRE; ch < nch; ch += 256)
+#pragma unroll
+    for (int e = 0; e < CH; ++e) ss += xr[ch * CH + e] * xr[ch * CH + e];
   for (int o = 1; o < 64; o <<= 1) {
-    const float ov = __shfl_xor(bv, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    const u32x4 t = {__float_as_uint(__shfl_xor(rr.v, o, 64)), (uint32_t)__shfl_xor(rr.i, o, 64),
+                     __float_as_uint(__shfl_xor(rr.v2, o, 64)), (uint32_t)__shfl_xor(rr.i2, o, 64)};
+    rr.merge_packed(t);
   }
-  __shared__ float sv[4];
-  __shared__ int si[4];
-  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
+  __shared__ u32x4 sw[4];
+  __shared__ float sred[3][4];
+  if (lane == 0) sw[wave] = rr.pack2();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
-      if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
-    tokens[m] = (bi == 0x7fffffff) ? -1 : bi;
+  RowRed best = RowRed::init();
+  for (int w = 0; w < 4; ++w) best.merge_packed(sw[w]);
+  const int c1 = best.i, c2 = best.i2;
+  const bool has1 = c1 != 0x7fffffff, has2 = c2 != 0x7fffffff;
+  // the two candidates' products with x * g
+  const int steps = K / STEP;
+  const char* w1 = W + (int64_t)(has1 ? c1 >> 4 : 0) * steps * 1024 + (has1 ? c1 & 15 : 0) * 16;
+  const char* w2 = W + (int64_t)(has2 ? c2 >> 4 : 0) * steps * 1024 + (has2 ? c2 & 15 : 0) * 16;
+  auto woff = [&](int ch) {  // k-step, then the lane group of the chunk
+    const int k0 = ch * CH;
+    return (int64_t)(k0 / STEP) * 1024 + ((k0 % STEP) / CH) * 256;
+  };
+  float d1 = 0.f, d2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < NPRE; ++c) {
+    const int ch = tid + 256 * c;
+    if (ch < nch) {
+      const u32x4 a = ld16(w1 + woff(ch)), b = ld16(w2 + woff(ch));
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xg = xv[c][q][e] * gv[c][q][e];
+          d1 += chunk_elem<S>(a, 4 * q + e) * xg;
+          d2 += chunk_elem<S>(b, 4 * q + e) * xg;
+        }
+    }
+  }
+  for (int ch = tid + 256 * NPRE; ch < nch; ch += 256) {
+    const u32x4 a = ld16(w1 + woff(ch)), b = ld16(w2 + woff(ch));
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const float xg = xr[ch * CH + e] * gain[ch * CH + e];
+      d1 += chunk_elem<S>(a, e) * xg;
+      d2 += chunk_elem<S>(b, e) * xg;
+    }
+  }
+  ss = wave_sum(ss);
+  d1 = wave_sum(d1);
+  d2 = wave_sum(d2);
+  if (lane == 0) { sred[0][wave] = ss; sred[1][wave] = d1; sred[2][wave] = d2; }
+  __syncthreads();
+  if (tid == 0) {
+    const float tss = (sred[0][0] + sred[0][1]) + (sred[0][2] + sred[0][3]);
+    const float inv = 1.0f / sqrtf(tss / (float)K + eps);
+    const float z1 = ((sred[1][0] + sred[1][1]) + (sred[1][2] + sred[1][3])) * inv;
+    const float z2 = ((sred[2][0] + sred[2][1]) + (sred[2][2] + sred[2][3])) * inv;
+    tokens[m] = !has1 ? -1 : (has2 && better(z2, c2, z1, c1)) ? c2 : c1;
   }
 }
 
-void launch_argmax_reduce(const float* pv, const int32_t* pi, int P, int M, int32_t* tokens, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(256), 0, s, pv, pi, P, M, tokens);
+void launch_argmax_rescore(const u32x4* part, int P, int M, const float* x, int64_t ldx, const float* gain,
+                           float eps, const void* W, int K, int w_bf16, int32_t* tokens, hipStream_t s) {
+  const char* w = reinterpret_cast<const char*>(W);
+  if (w_bf16)
+    hipLaunchKernelGGL(argmax_rescore_kernel<uint16_t>, dim3(M), dim3(256), 0, s, part, P, M, x, ldx, gain, eps, w, K,
+                       tokens);
+  else
+    hipLaunchKernelGGL(argmax_rescore_kernel<float>, dim3(M), dim3(256), 0, s, part, P, M, x, ldx, gain, eps, w, K,
+                       tokens);
 }
 
 // Log-sum-exp of each row from its P partial (maximum, sum of exp) pairs, merged
@@ -951,6 +1114,14 @@ static int stream_ks(int nsteps) {
   while (ks > 1 && nsteps / ks < kStreamU) ks >>= 1;
   return ks;
 }
+// The same with a deferred norm over segs segments (1 or 3): a multiple of
+// segs, so that every wave's steps lie in one segment.
+static int stream_ks_segs(int nsteps, int segs) {
+  if (segs == 1) return stream_ks(nsteps);
+  if (nsteps / 15 >= kStreamU) return 15;
+  if (nsteps / 6 >= kStreamU) return 6;
+  return 3;
+}
 
 int gemm_argmax_partials(int M, int N) {
   if (M <= 16) {
@@ -978,15 +1149,22 @@ static void allow_lds(int bytes) {
   (void)st;
 }
 
-template <typename S, bool DUAL>
+template <typename S, bool DUAL, int LOM>
 static void launch_stream(const GemmParams& p, hipStream_t s) {
   const dim3 grid((p.N + 15) / 16);
-  switch (stream_ks(p.K / (4 * Storage<S>::CH))) {
-    case 16: hipLaunchKernelGGL((gemm_stream_kernel<S, 16, kStreamU, DUAL>), grid, dim3(1024), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((gemm_stream_kernel<S, 8, kStreamU, DUAL>), grid, dim3(512), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((gemm_stream_kernel<S, 4, kStreamU, DUAL>), grid, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gemm_stream_kernel<S, 2, kStreamU, DUAL>), grid, dim3(128), 0, s, p); break;
-    default: hipLaunchKernelGGL((gemm_stream_kernel<S, 1, kStreamU, DUAL>), grid, dim3(64), 0, s, p); break;
+  const int nsteps = p.K / (4 * Storage<S>::CH);
+  const int ks = p.xinv ? stream_ks_segs(nsteps, p.xinv_segs) : stream_ks(nsteps);
+  if constexpr (!DUAL && LOM == 0) {  // deferred three-segment norms (the fc fusion)
+    if (ks == 15) { hipLaunchKernelGGL((gemm_stream_kernel<S, 15, kStreamU, false, 0>), grid, dim3(960), 0, s, p); return; }
+    if (ks == 6) { hipLaunchKernelGGL((gemm_stream_kernel<S, 6, kStreamU, false, 0>), grid, dim3(384), 0, s, p); return; }
+    if (ks == 3) { hipLaunchKernelGGL((gemm_stream_kernel<S, 3, kStreamU, false, 0>), grid, dim3(192), 0, s, p); return; }
+  }
+  switch (ks) {
+    case 16: hipLaunchKernelGGL((gemm_stream_kernel<S, 16, kStreamU, DUAL, LOM>), grid, dim3(1024), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((gemm_stream_kernel<S, 8, kStreamU, DUAL, LOM>), grid, dim3(512), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_stream_kernel<S, 4, kStreamU, DUAL, LOM>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_kernel<S, 2, kStreamU, DUAL, LOM>), grid, dim3(128), 0, s, p); break;
+    default: hipLaunchKernelGGL((gemm_stream_kernel<S, 1, kStreamU, DUAL, LOM>), grid, dim3(64), 0, s, p); break;
   }
 }
 
@@ -1016,7 +1194,18 @@ static void launch_stream_lds_ks(const GemmParams& p, size_t lds, hipStream_t s)
 
 template <typename S, typename XT, bool DUAL, bool NORM>
 static void launch_stream_lds(const GemmParams& p, size_t lds, hipStream_t s) {
-  switch (stream_ks(p.K / (4 * Storage<S>::CH))) {
+  const int nsteps = p.K / (4 * Storage<S>::CH);
+  if constexpr (NORM && !DUAL) {
+    if (p.nrm.defer) {  // every wave inside one segment
+      switch (stream_ks_segs(nsteps, p.nrm.segs)) {
+        case 15: launch_stream_lds_ks<S, XT, 15, false, true>(p, lds, s); return;
+        case 6: launch_stream_lds_ks<S, XT, 6, false, true>(p, lds, s); return;
+        case 3: launch_stream_lds_ks<S, XT, 3, false, true>(p, lds, s); return;
+        default: break;  // one segment: any split
+      }
+    }
+  }
+  switch (stream_ks(nsteps)) {
     case 16: launch_stream_lds_ks<S, XT, 16, DUAL, NORM>(p, lds, s); break;
     case 8: launch_stream_lds_ks<S, XT, 8, DUAL, NORM>(p, lds, s); break;
     case 4: launch_stream_lds_ks<S, XT, 4, DUAL, NORM>(p, lds, s); break;
@@ -1043,17 +1232,17 @@ static void launch_stream_lds(const GemmParams& p, size_t lds, hipStream_t s) {
 #ifndef PE_FNORM_KINDS
 #define PE_FNORM_KINDS 3
 #endif
-template <typename S, bool DUAL>
+template <typename S, bool DUAL, bool HL>
 static void launch_stream_fnorm(const GemmParams& p, int ks, hipStream_t s) {
   constexpr int U = DUAL ? PE_FNORM_DUAL_U : PE_FNORM_U;
   const dim3 grid((p.N + 15) / 16);
   const size_t lds = (size_t)ks * (kFnormMaxSteps * 4 * Storage<S>::CH * 4) + (size_t)ks * 64 * 4;
   switch (ks) {
-    case 16: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 16, U, DUAL>), grid, dim3(1024), lds, s, p); break;
-    case 8: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 8, U, DUAL>), grid, dim3(512), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 4, U, DUAL>), grid, dim3(256), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 2, U, DUAL>), grid, dim3(128), lds, s, p); break;
-    default: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 1, U, DUAL>), grid, dim3(64), lds, s, p); break;
+    case 16: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 16, U, DUAL, HL>), grid, dim3(1024), lds, s, p); break;
+    case 8: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 8, U, DUAL, HL>), grid, dim3(512), lds, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 4, U, DUAL, HL>), grid, dim3(256), lds, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 2, U, DUAL, HL>), grid, dim3(128), lds, s, p); break;
+    default: hipLaunchKernelGGL((gemm_stream_fnorm_kernel<S, 1, U, DUAL, HL>), grid, dim3(64), lds, s, p); break;
   }
 }
 
@@ -1061,8 +1250,9 @@ static void launch_stream_fnorm(const GemmParams& p, int ks, hipStream_t s) {
 // p.clear); returns the parameters of the contraction over the normalised rows.
 // packed: p.nrm.tmp receives the operand layout (rows rounded up to 16).
 template <typename S>
-static GemmParams norm_first(const GemmParams& p, hipStream_t s, bool packed = false) {
+static GemmParams norm_first(const GemmParams& p, hipStream_t s, bool packed = false, bool defer = false) {
   NormParams np{};
+  np.inv_out = defer ? p.nrm.inv_tmp : nullptr;
   np.in = p.X;
   np.ld_in = p.ldx;
   np.skip = p.nrm.skip;
@@ -1085,6 +1275,10 @@ static GemmParams norm_first(const GemmParams& p, hipStream_t s, bool packed = f
   q.clear = nullptr;
   q.nclear = 0;
   q.x_packed = packed;
+  if (defer) {
+    q.xinv = p.nrm.inv_tmp;
+    q.xinv_segs = p.nrm.segs;
+  }
   return q;
 }
 
@@ -1125,9 +1319,15 @@ static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
   const bool am = epi_rowred(p0.epi.kind);
   const bool lse = p0.epi.kind == EPI_LSE;
   const bool norm = p0.nrm.gain != nullptr;
+  // deferred 1 / rms: storage-type rows (the operand is then the input times
+  // its gains, exact for unit gains), one or three segments, bf16
+  const bool defer = sizeof(S) == 2 && norm && p0.nrm.defer && !p0.nrm.x_f32 &&
+                     (p0.nrm.segs == 1 || p0.nrm.segs == 3) && !epi_rowred(p0.epi.kind);
   if (p0.M <= 16) {
-    // activation rows + the zero chunk of the padding rows (+ the gains of a norm)
-    const size_t lds = (size_t)p0.M * (p0.K * sizeof(S) + 16) + 16 + (norm ? (size_t)p0.K * 4 : 0);
+    // activation rows + the zero chunk of the padding rows (+ the gains of a
+    // norm and its deferred scales)
+    const size_t lds = (size_t)p0.M * (p0.K * sizeof(S) + 16) + 16 +
+                       (norm ? (size_t)p0.K * 4 + (size_t)p0.M * p0.nrm.segs * 4 : 0);
     const int xsz = norm && p0.nrm.x_f32 ? 4 : (int)sizeof(S);
     const int seg_bytes = p0.nrm.seg_len * xsz;
     const bool xf32 = xsz == 4;
@@ -1144,24 +1344,37 @@ static int launch_gemm_t(const GemmParams& p0, hipStream_t s) {
     if (norm && xf32 && fsteps <= kFnormMaxSteps && (reinterpret_cast<uintptr_t>(p0.nrm.gain) & 15) == 0 &&
         p0.nrm.segs == 1 && (PE_FNORM_KINDS & (dual ? 2 : 1))) {
       // float rows (the residual stream): the norm folds into the weight stream
-      if (dual) launch_stream_fnorm<S, true>(p0, fks, s); else launch_stream_fnorm<S, false>(p0, fks, s);
+      const bool hl = sizeof(S) == 2 && p0.x_split;
+      if (dual) { if (hl) launch_stream_fnorm<S, true, true>(p0, fks, s); else launch_stream_fnorm<S, true, false>(p0, fks, s); }
+      else { if (hl) launch_stream_fnorm<S, false, true>(p0, fks, s); else launch_stream_fnorm<S, false, false>(p0, fks, s); }
       return 0;
     }
     if (norm && norm_fits && !xf32 && !dual && lds <= (size_t)kStreamXLds) {
       // storage-type rows (the captured streams, several segments): normalised
       // while they are staged in LDS
-      launch_stream_lds<S, S, false, true>(p0, lds, s);
+      GemmParams q = p0;
+      q.nrm.defer = defer;
+      launch_stream_lds<S, S, false, true>(q, lds, s);
       return 0;
     }
-    const GemmParams p = norm ? norm_first<S>(p0, s) : p0;
-    if (dual) launch_stream<S, true>(p, s); else launch_stream<S, false>(p, s);
+    const GemmParams p = norm ? norm_first<S>(p0, s, false, defer && p0.nrm.inv_tmp) : p0;
+    // a remainder operand: in columns 8..15 of the operand when M <= 8, else
+    // as a second matrix-core step per chunk
+    const int lom = (sizeof(S) == 2 && !norm && p.x_lo) ? (p.M <= 8 ? 2 : 1) : 0;
+    if (dual) launch_stream<S, true, 0>(p, s);
+    else if (lom == 2) launch_stream<S, false, 2>(p, s);
+    else if (lom == 1) launch_stream<S, false, 1>(p, s);
+    else launch_stream<S, false, 0>(p, s);
     return 0;
   }
   // rows normalised for the LDS-tiled kernel of gemm_big.hip go to its 1 KB
   // operand chunks (half the cache lines of 64-byte row pieces)
+  // a deferred norm needs the large-M kernel's K split along the segments
+  const bool defer_big = defer && p0.nrm.inv_tmp && gemm_big_splits(p0, p0.nrm.segs) > 0;
   const bool to_big = sizeof(S) == 2 && p0.M >= 128 && p0.K >= 64 && norm &&
-                      norm_packable(p0.nrm.seg_len, !p0.nrm.x_f32) && (am || gemm_big_splits(p0) > 0);
-  const GemmParams p = norm ? norm_first<S>(p0, s, to_big) : p0;
+                      norm_packable(p0.nrm.seg_len, !p0.nrm.x_f32) &&
+                      (am || gemm_big_splits(p0, defer_big ? p0.nrm.segs : 1) > 0);
+  const GemmParams p = norm ? norm_first<S>(p0, s, to_big, defer_big && to_big) : p0;
   // 128-wide tiles only when they still give every CU two workgroups (the
   // N = 2,880 projections get 64 x 64 tiles)
   const bool big = p.M >= 256 && (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) >= 512;

@@ -22,7 +22,10 @@
 //    which is what bounds the activation traffic of these tiles.
 // One barrier per k-step.  Workgroup ids map the M tiles of one N tile back
 // to back onto one XCD (workgroup i runs on XCD i % 8), so each weight chunk
-// is fetched from HBM once.  L2->LDS traffic per flop is (BM + BN) / (BM BN)
+// is fetched from HBM once.  A K split takes its shares' k-step ranges from
+// p.split_k when the host gives them (shares cut at the segments of an
+// operand with deferred scales, each share inside one segment), else equal
+// shares.  L2->LDS traffic per flop is (BM + BN) / (BM BN)
 // bytes: 3/256 for 256 x 128, against 1/64 for the 128 x 128 tiles.
 #include <math.h>
 #include "epilogue.h"
@@ -52,6 +55,7 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
                                                // last group repeats when NW does not divide BM / 16)
   constexpr int PT = WI * (DUAL ? 2 : 1) + XI;  // vector-memory operations per wave per k-step
   static_assert(BM % 32 == 0 && BN % 64 == 0 && WB % NW == 0, "tile shape");
+  static_assert(!ARGMAX || D * STAGE >= WN * BM * 16, "row-reduction lists fit in the ring");
   extern __shared__ __attribute__((aligned(16))) char lds[];  // D stages
 
   const int bid = blockIdx.x;
@@ -62,8 +66,9 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   const int M = p.M, N = p.N, K = p.K;
   // K split: workgroup (x, y) takes the y-th share of the 32-wide k-steps
   const int ksteps = K / 32;
-  const int kbeg = SPLIT ? (int)((int64_t)ksteps * blockIdx.y / gridDim.y) : 0;
-  const int nsteps = SPLIT ? (int)((int64_t)ksteps * (blockIdx.y + 1) / gridDim.y) - kbeg : ksteps;
+  const int y = blockIdx.y;
+  const int kbeg = !SPLIT ? 0 : p.nsplit_k ? p.split_beg[y] : (int)((int64_t)ksteps * y / gridDim.y);
+  const int nsteps = !SPLIT ? ksteps : (p.nsplit_k ? p.split_end[y] : (int)((int64_t)ksteps * (y + 1) / gridDim.y)) - kbeg;
   const int nfb = (N + 15) >> 4;
   const int n0 = ft * BN, m0 = mt * BM;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -176,11 +181,13 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
 #undef PE_BIG_ITER
 #undef PE_BIG_MMA
 #undef PE_BIG_FRAGS
-
   if constexpr (ARGMAX) {
     // argmax (EPI_ARGMAX) or log-sum-exp (EPI_LSE, LSE set) partials of this tile's rows
-    __shared__ float sbv[WN][BM], sbs[WN][BM];
-    __shared__ int sbi[WN][BM];
+    // per wave column and row: (v, s) or the top-2 list, in the copy ring's
+    // LDS once every wave is done with it (a static array would take the
+    // second workgroup's room on the CU)
+    __syncthreads();
+    u32x4* sb = reinterpret_cast<u32x4*>(lds);
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
       const int mloc = wm * (BM / 2) + q * 16 + r;
@@ -198,24 +205,31 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
             if (p.epi.logits) p.epi.logits[(int64_t)m * N + n] = v;
             if constexpr (LSE) {
               if (n == tgt) p.epi.tgt_logit[m] = v;
+              rr.add(true, v, n);
+            } else {
+              // the largest of the lane's 16 features per row; the merges
+              // below keep the two largest of the lanes' maxima
+              rr.add1(v, n);
             }
-            rr.add(LSE, v, n);
           }
         }
       rr.merge_groups(LSE);
-      if (g == 0) {
-        sbv[wn][mloc] = rr.v;
-        if constexpr (LSE) sbs[wn][mloc] = rr.s;
-        else sbi[wn][mloc] = rr.i;
-      }
+      if (g == 0) sb[wn * BM + mloc] = LSE ? u32x4{__float_as_uint(rr.v), 0u, __float_as_uint(rr.s), 0u} : rr.pack2();
     }
     __syncthreads();
     if (tid < BM && m0 + tid < M) {
-      RowRed rr{sbv[0][tid], LSE ? sbs[0][tid] : 0.f, LSE ? 0 : sbi[0][tid]};
-      for (int w = 1; w < WN; ++w) rr.merge(LSE, sbv[w][tid], LSE ? 0 : sbi[w][tid], LSE ? sbs[w][tid] : 0.f);
-      p.epi.part_val[(int64_t)ft * M + m0 + tid] = rr.v;
-      if constexpr (LSE) p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
-      else p.epi.part_idx[(int64_t)ft * M + m0 + tid] = rr.i;
+      RowRed rr = RowRed::init();
+      for (int w = 0; w < WN; ++w) {
+        const u32x4 o = sb[w * BM + tid];
+        if constexpr (LSE) rr.merge(true, __uint_as_float(o[0]), 0, __uint_as_float(o[2]));
+        else rr.merge_packed(o);
+      }
+      if constexpr (LSE) {
+        p.epi.part_val[(int64_t)ft * M + m0 + tid] = rr.v;
+        p.epi.part_sum[(int64_t)ft * M + m0 + tid] = rr.s;
+      } else {
+        p.epi.part_top2[(int64_t)ft * M + m0 + tid] = rr.pack2();
+      }
     }
   } else if constexpr (SPLIT) {
     // partial tile of split y: [y][m][n] (the second matrix's after all splits)
@@ -257,7 +271,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int sp
   const int m = (int)(i / (N / 4)), n = (int)(i % (N / 4)) * 4;
   f32x4 y = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < splits; ++s) {
-    y += *reinterpret_cast<const f32x4*>(p.split_ws + ((int64_t)s * M + m) * N + n);
+    // a share of a deferred-scale operand lies in one segment: scale it by the row's 1 / rms there
+    const float sc = p.xinv ? p.xinv[(int64_t)m * p.xinv_segs + (p.nsplit_k ? p.split_seg[s] : 0)] : 1.f;
+    y += *reinterpret_cast<const f32x4*>(p.split_ws + ((int64_t)s * M + m) * N + n) * sc;
     if constexpr (DUAL) y2 += *reinterpret_cast<const f32x4*>(p.split_ws + ((int64_t)(splits + s) * M + m) * N + n);
   }
 #pragma unroll
@@ -309,20 +325,73 @@ static bool rows224(int M) { return ((M + 223) / 224) * 224 < ((M + 255) / 256) 
 #define PE_SPLIT_STAGES 3
 #endif
 
-int gemm_big_splits(const GemmParams& p) {
+// Share ranges of a K split: `base` equal shares of the ksteps k-steps, also
+// cut at the segment boundaries of a deferred-scale operand (segs > 1) so that
+// every share lies in one segment (the fc fusion at 896 rows: 4 shares cut at
+// the three streams give 6 shares of 67, 23, 45, 45, 22 and 68 k-steps; the
+// longest is as long as with 4).  The shares are ordered longest first (the
+// dispatcher starts workgroups in share order, so the short ones fill in
+// behind the long ones).  Writes each share's range to bb / be and its
+// segment to bseg; returns the count (0 past kMaxSplitK).
+static int split_ranges(int ksteps, int base, int segs, int* bb, int* be, int* bseg) {
+  int bk[kMaxSplitK + 1];
+  int cut[kMaxSplitK * 2 + 2];
+  int n = 0;
+  for (int i = 0; i <= base; ++i) cut[n++] = (int)((int64_t)ksteps * i / base);
+  for (int j = 1; j < segs; ++j) cut[n++] = ksteps / segs * j;
+  for (int i = 1; i < n; ++i)  // insertion sort of at most a dozen cuts
+    for (int k = i; k > 0 && cut[k - 1] > cut[k]; --k) { const int t = cut[k]; cut[k] = cut[k - 1]; cut[k - 1] = t; }
+  int m = 0;
+  for (int i = 0; i < n; ++i)
+    if (m == 0 || cut[i] != bk[m - 1]) {
+      if (m > kMaxSplitK) return 0;
+      bk[m++] = cut[i];
+    }
+  const int n_sh = m - 1;
+  int ord[kMaxSplitK];
+  for (int i = 0; i < n_sh; ++i) ord[i] = i;
+  for (int i = 1; i < n_sh; ++i)  // stable: longer first, then in k order
+    for (int k = i; k > 0 && bk[ord[k] + 1] - bk[ord[k]] > bk[ord[k - 1] + 1] - bk[ord[k - 1]]; --k) {
+      const int t = ord[k]; ord[k] = ord[k - 1]; ord[k - 1] = t;
+    }
+  for (int i = 0; i < n_sh; ++i) {
+    bb[i] = bk[ord[i]];
+    be[i] = bk[ord[i] + 1];
+    bseg[i] = bk[ord[i]] / (ksteps / segs);
+  }
+  return n_sh;
+}
+
+// The K split of a non-argmax contraction: 0 when it should not split (and
+// cannot take a deferred-scale operand), else the share count, the ranges in
+// bb / be / bseg when given.
+static int big_split_plan(const GemmParams& p, int segs, int* bb, int* be, int* bseg) {
   // the gate/up pair measured faster on the 128 x 64 register-fed tiles
   // (67.6 us against 76 us split at 448 rows)
   if (p.epi.kind == EPI_SWIGLU || epi_rowred(p.epi.kind)) return 0;
   if (!p.split_ws || p.N % 4) return 0;
+  const int ksteps = p.K / 32;
+  if (segs > 1 && (ksteps % segs || segs > kMaxSplitK)) return 0;  // segments of whole k-steps
   const int bm = rows224(p.M) ? 224 : 256;
   const int tiles = ((p.N + 127) / 128) * ((p.M + bm - 1) / bm);
   const int64_t per = (int64_t)p.M * p.N * 4;
   int splits = (PE_SPLIT_SLOTS + tiles - 1) / tiles;
   splits = min(splits, PE_SPLIT_MAX);
-  splits = min(splits, (p.K / 32) / PE_SPLIT_MINSTEPS);
-  while (splits > 1 && (int64_t)splits * per > p.split_cap) --splits;
-  return splits >= 2 ? splits : 0;
+  splits = min(splits, ksteps / PE_SPLIT_MINSTEPS);
+  if (segs <= 1) {
+    while (splits > 1 && (int64_t)splits * per > p.split_cap) --splits;
+    return splits >= 2 ? splits : 0;
+  }
+  int tb[kMaxSplitK], te[kMaxSplitK], ts[kMaxSplitK];
+  if (!bb) { bb = tb; be = te; bseg = ts; }
+  for (int base = max(splits, 1); base >= 1; --base) {
+    const int n = split_ranges(ksteps, base, segs, bb, be, bseg);
+    if (n >= 2 && (int64_t)n * per <= p.split_cap) return n;
+  }
+  return 0;
 }
+
+int gemm_big_splits(const GemmParams& p, int segs) { return big_split_plan(p, segs, nullptr, nullptr, nullptr); }
 
 int launch_gemm_big(const GemmParams& p, hipStream_t s) {
   const bool r224 = rows224(p.M);
@@ -340,17 +409,19 @@ int launch_gemm_big(const GemmParams& p, hipStream_t s) {
     return r224 ? launch_big<224, 128, 2, 3, false, true, false>(p, 1, s)
                 : launch_big<256, 128, 2, 3, false, true, false>(p, 1, s);
   }
-  const int splits = gemm_big_splits(p);
+  GemmParams q = p;
+  const int splits = big_split_plan(p, p.xinv ? p.xinv_segs : 1, q.split_beg, q.split_end, q.split_seg);
   if (!splits) return -1;  // the caller's 128-tile kernel keeps the contraction
+  q.nsplit_k = (p.xinv && p.xinv_segs > 1) ? splits : 0;
   if (p.x_packed) {
-    if (r224) launch_big<224, 128, 2, PE_SPLIT_STAGES, false, false, true, true>(p, splits, s);
-    else launch_big<256, 128, 2, PE_SPLIT_STAGES, false, false, true, true>(p, splits, s);
+    if (r224) launch_big<224, 128, 2, PE_SPLIT_STAGES, false, false, true, true>(q, splits, s);
+    else launch_big<256, 128, 2, PE_SPLIT_STAGES, false, false, true, true>(q, splits, s);
   } else {
-    if (r224) launch_big<224, 128, 2, PE_SPLIT_STAGES, false, false, true>(p, splits, s);
-    else launch_big<256, 128, 2, PE_SPLIT_STAGES, false, false, true>(p, splits, s);
+    if (r224) launch_big<224, 128, 2, PE_SPLIT_STAGES, false, false, true>(q, splits, s);
+    else launch_big<256, 128, 2, PE_SPLIT_STAGES, false, false, true>(q, splits, s);
   }
   const int64_t n4 = (int64_t)p.M * (p.N / 4);
-  hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p, splits);
+  hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, q, splits);
   return 0;
 }
 

@@ -28,6 +28,11 @@ struct NormParams {
   int64_t ld_out;
   int* zero;             // counters cleared by the launch (block 0), or nullptr
   int nzero;
+  // Deferred scale: when set, out holds x * gain only (no 1 / rms) and
+  // inv_out[i * segs + seg] receives the row segment's 1 / rms (0 for skipped
+  // rows); the contraction applies it to its sum over that segment.  With
+  // unit gains and bf16 input the operand is then the input itself, exact.
+  float* inv_out;
   // bf16 output only: 0 = rows of ld_out elements; 1 = the matrix-core operand
   // layout of the large-M contractions (ld_out = K, a multiple of 32): the
   // 16-row x 32-column piece (G, S) is the 1 KB chunk G * (K / 32) + S, whose
@@ -50,7 +55,9 @@ enum EpiKind {
   EPI_QKV = 1,     // n < q_cols: q_out[m][n] = y; then k, v columns go to the
                    // caches at slots[m] (skipped when slots[m] < 0)
   EPI_RESID = 2,   // out_f32[m][n] = y + res[res_rows ? res_rows[m] : m][n]
-  EPI_SWIGLU = 3,  // out_s[m][n] = silu(y_gate) * y_up
+  EPI_SWIGLU = 3,  // out_s[m][n] = silu(y_gate) * y_up (and, with out_s_lo, the
+                   // storage-type remainder of that value: out_s + out_s_lo
+                   // carries it to about 16 mantissa bits)
   EPI_ARGMAX = 4,  // running (max, lowest index) per row; optional logits
   EPI_LSE = 5      // running (max m, sum exp(y - m)) per row and the target's logit
 };
@@ -72,9 +79,11 @@ struct Epi {
   const int32_t* slots;
   int q_cols, kv_cols, kv_rows;
   int embed_rows;
+  void* out_s_lo;        // swiglu: optional second output (the remainder), or nullptr
   float* logits;         // argmax: optional [M, N]
-  float* part_val;       // argmax: [P, M] partial maxima; lse: partial maxima m
-  int32_t* part_idx;     // argmax: [P, M] their indices
+  u32x4* part_top2;      // argmax: [P, M] partial (largest, index, second, index) as
+                         // (float bits, int, float bits, int), index 0x7fffffff when absent
+  float* part_val;       // lse: [P, M] partial maxima m
   float* part_sum;       // lse: [P, M] partial sums of exp(y - m)
   const int32_t* targets;  // lse: [M] target feature per row (< 0: none)
   float* tgt_logit;      // lse: [M] y of the target feature (written by the one tile that holds it)
@@ -91,9 +100,14 @@ struct NormIn {
   float eps;
   const uint8_t* skip;  // flags indexed by row, or nullptr
   int x_f32;            // X holds float32 (else the storage type)
+  int defer;            // scale by 1 / rms after the contraction (see GemmParams)
+  float* inv_tmp;       // [M, segs] room for the deferred scales when a separate
+                        // norm kernel runs first
   void* tmp;            // [M, K] storage type: normalised rows when the norm
                         // cannot be fused into the contraction's staging
 };
+
+constexpr int kMaxSplitK = 8;  // K-split shares of the large-M kernel at most
 
 struct GemmParams {
   const void* X;
@@ -109,6 +123,27 @@ struct GemmParams {
   float* split_ws;     // large M: room for K-split partial products, or nullptr (no split)
   int64_t split_cap;   // its size in bytes
   int x_packed;        // X in the operand layout of NormParams::packed (large-M argmax only)
+  // Operand precision (bf16 storage; no effect for f32):
+  //  * nrm.defer (with a norm of several segments, or one): the operand is
+  //    x * gain and each segment's sum is scaled by its 1 / rms after the
+  //    contraction (the weight-streaming kernels split K by segment, the
+  //    large-M kernel splits K into whole segments); where a path cannot, the
+  //    normalised operand is rounded as before.
+  //  * x_lo (M <= 16, no norm): the operand is X + x_lo (two bf16 parts), two
+  //    matrix-core steps per weight chunk.
+  //  * x_split (M <= 16, float rows with a folded norm): the rounded operand
+  //    and its remainder, two matrix-core steps per weight chunk.
+  const void* x_lo;
+  int x_split;
+  // Deferred segment scales of a normalised operand written by a separate
+  // norm kernel: xinv[m * xinv_segs + s] multiplies the sum over segment s.
+  const float* xinv;
+  int xinv_segs;
+  // Large-M K split into explicit k-step ranges (set by launch_gemm_big):
+  // share y covers k-steps [split_beg[y], split_end[y]) and lies in segment
+  // split_seg[y] of a deferred-scale operand; nsplit_k = 0: equal shares.
+  int nsplit_k;
+  int split_beg[kMaxSplitK], split_end[kMaxSplitK], split_seg[kMaxSplitK];
 };
 
 
@@ -120,7 +155,7 @@ void launch_pack(const void* src, void* dst, int N, int row_bytes, hipStream_t s
 // into the activation staging of the streaming kernels when the rows fit in
 // LDS; otherwise rmsnorm_rows_kernel writes p.nrm.tmp first.
 // EPI_ARGMAX (EPI_LSE) returns the number of partial rows P to reduce with
-// launch_argmax_reduce (launch_lse_reduce); every other kind returns 0.
+// launch_argmax_rescore (launch_lse_reduce); every other kind returns 0.
 int launch_gemm(const GemmParams& p, int bf16, hipStream_t s);
 // Upper bound of P for an argmax GEMM of this shape.
 int gemm_argmax_partials(int M, int N);
@@ -131,13 +166,23 @@ int gemm_argmax_partials(int M, int N);
 int launch_gemm_big(const GemmParams& p, hipStream_t s);
 // K-split count launch_gemm_big uses for a non-argmax contraction; 0 = it
 // launches nothing for this shape.
-int gemm_big_splits(const GemmParams& p);
+// segs > 1: for an operand whose segs segments of K are scaled after the
+// contraction (p.xinv), which needs segments of whole 32-wide k-steps.
+int gemm_big_splits(const GemmParams& p, int segs = 1);
 // Bytes of K-split workspace worth giving a large-M stage (T rows, widest
 // contraction output nmax).
 int64_t gemm_split_bytes(int T, int nmax);
 int gemm_big_partials(int N);
 
-void launch_argmax_reduce(const float* pv, const int32_t* pi, int P, int M, int32_t* tokens, hipStream_t s);
+// Greedy token of each row: the P partial top-2 lists merged into the row's
+// two largest logits (lowest index first among equal values), whose logits
+// are then computed again in fp32 from the unrounded normalised row,
+//   z = (sum_k W[c][k] x[m][k] g[k]) / sqrt(mean_k x[m][k]^2 + eps),
+// and the larger (lower index on a tie) is the token.  x: [M, K] float32
+// rows (stride ldx), W: packed [N, K] weights of storage type (bf16 when
+// w_bf16).
+void launch_argmax_rescore(const u32x4* part, int P, int M, const float* x, int64_t ldx, const float* gain,
+                           float eps, const void* W, int K, int w_bf16, int32_t* tokens, hipStream_t s);
 // lse[m] = log sum_v exp(y[m][v]) from the P partials of EPI_LSE, and
 // loss[m] = lse[m] - tgt[m] (0 where targets[m] is outside [0, N)); lse or
 // loss may be null.

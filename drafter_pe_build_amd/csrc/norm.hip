@@ -9,7 +9,9 @@
 // Rows flagged in `skip` are written as zeros.  bf16 output can also go to
 // the matrix-core operand layout of the large-M contractions (`packed`,
 // rmsnorm_packed_kernel below).  Block (0, 0) also clears the
-// split-K tile counters of the contraction that consumes this output.
+// split-K tile counters of the contraction that consumes this output.  With
+// inv_out the 1 / rms of each row segment goes there and the output is
+// x * g only (the consuming contraction scales its sums).
 #include "kernels.h"
 
 namespace pe {
@@ -47,7 +49,9 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(NormParams p) {
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-  const float inv = skip ? 0.f : 1.0f / sqrtf(tot / (float)p.d + p.eps);
+  const float inv0 = skip ? 0.f : 1.0f / sqrtf(tot / (float)p.d + p.eps);
+  if (p.inv_out && tid == 0) p.inv_out[(int64_t)i * p.segs + seg] = inv0;
+  const float inv = p.inv_out ? (skip ? 0.f : 1.f) : inv0;
 #pragma unroll
   for (int c = 0; c < kNormMaxChunks; ++c) {
     const int ch = tid + c * 256;
@@ -115,7 +119,9 @@ __global__ __launch_bounds__(1024) void rmsnorm_packed_kernel(NormParams p) {
 #pragma unroll
     for (int e = 0; e < CI; ++e) ss += elem(raw[c], e) * elem(raw[c], e);
   ss = wave_sum(ss);
-  const float inv = skip ? 0.f : 1.0f / sqrtf(ss / (float)p.d + p.eps);
+  const float inv0 = skip ? 0.f : 1.0f / sqrtf(ss / (float)p.d + p.eps);
+  if (p.inv_out && blockIdx.z == 0 && lane == 0 && i < p.n) p.inv_out[(int64_t)i * p.segs + seg] = inv0;
+  const float inv = p.inv_out ? (skip ? 0.f : 1.f) : inv0;
   const float* gain = p.gain + (int64_t)seg * p.d;
   const int rs = 64 * (k1 - k0) + 16;
   char* lrow = lds + rl * rs - k0 * 64;  // column k of the share at byte 2 k

@@ -13,15 +13,19 @@ from synth import inputs as si
 # ~1e-6).
 TOL = {"bf16": 2e-2, "f32": 1e-4}
 
+# Greedy tokens must equal the oracle's wherever its top-2 logit gap exceeds
+# GAP: the stated 1e-2 for bf16; for f32 storage (operands and accumulation
+# in fp32, logit errors ~1e-6) a tighter 1e-4.
+GAP = {"bf16": 1e-2, "f32": 1e-4}
 
-def token_gap(dtype, logit_rms):
-    """Per-row top-2 gap above which the greedy token is decided.
 
-    Each logit of a row is held to TOL times the row's rms; two logits that
-    each move by at most that much cannot swap order across a gap larger than
-    twice it.  Rows below the gap are near-ties that rounding in the storage
-    precision may legitimately break either way."""
-    return 2.0 * TOL[dtype] * np.asarray(logit_rms)
+def kernel_top2_ok(tokens, logits):
+    """Each token is one of the two largest of the kernel's own logits of its
+    row (the LM head scores those two again in fp32 and keeps the larger)."""
+    z = np.asarray(logits)
+    second = np.partition(z, -2, axis=1)[:, -2] if z.shape[1] > 1 else np.full(z.shape[0], -np.inf)
+    zt = z[np.arange(z.shape[0]), np.asarray(tokens)]
+    return bool(np.all(zt >= second))
 
 
 def say(*a):

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import TOL, bits, dev_to_f64, gptoss_weights, say, token_gap
+from helpers import GAP, TOL, bits, dev_to_f64, gptoss_weights, kernel_top2_ok, say
 from oracle import batch as ob
 from oracle import drafter as od
 from oracle import metrics as om
@@ -84,9 +84,11 @@ def check_case(name, dims, W, c, logits=True):
     st.lm_head(with_logits=logits)
     torch.cuda.synchronize()
     tok = st.tokens.cpu().numpy()
-    gap_min = token_gap(dims.dtype, ref["logit_rms"])
+    gap_min = GAP[dims.dtype]
     ok, n = om.tokens_agree(tok, ref["tokens"], ref["gap"], gap_min)
-    say("  tokens compared %d of %d, equal %s" % (n, len(tok), ok))
+    dec = ref["gap"] > gap_min
+    say("  tokens compared %d of %d (oracle top-2 gap > %g; smallest compared gap %.4g), equal %s"
+        % (n, len(tok), gap_min, ref["gap"][dec].min() if n else float("nan"), ok))
     if not ok and logits:
         lg = st.logits.cpu().numpy().astype(np.float64)
         for i in np.nonzero((tok != ref["tokens"]) & (ref["gap"] > gap_min))[0]:
@@ -100,8 +102,9 @@ def check_case(name, dims, W, c, logits=True):
         e = om.relerr(lg32, ref["logits"])
         say("  logits relerr %.3g" % e)
         assert e <= tol
-        # the kernel's token is the first maximum of its own fp32 logits
-        np.testing.assert_array_equal(tok, np.argmax(lg32, axis=1))
+        # the token is one of the two largest of the kernel's own logits (the
+        # LM head scores those two again in fp32 and keeps the larger)
+        assert kernel_top2_ok(tok, lg32)
 
     say("[%s] full step again (stage outputs must repeat bit for bit)" % name)
     t1 = st.tokens.clone()
