@@ -79,6 +79,8 @@ EXPORTS = {
     "pe_lm_head_argmax": (c_int, [POINTER(PeDims), POINTER(PeWeights), c_int32, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_size_t, c_void_p]),
     "pe_lm_head_argmax_workspace": (c_int, [POINTER(PeDims), c_int32, POINTER(c_size_t)]),
+    "pe_lm_head_argmax_noalloc": (c_int, [POINTER(PeDims), POINTER(PeWeights), c_int32, c_void_p, c_void_p,
+                                          c_void_p, c_void_p]),
     "pe_lm_head_loss": (c_int, [POINTER(PeDims), POINTER(PeWeights), c_int32, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "pe_lm_head_loss_workspace": (c_int, [POINTER(PeDims), c_int32, POINTER(c_size_t)]),
@@ -283,6 +285,14 @@ def pe_lm_head_loss(dims, weights, n, x, targets, lse=None, loss=None, workspace
     _check("pe_lm_head_loss", lib().pe_lm_head_loss(
         ctypes.byref(dims), ctypes.byref(w), n, ptr(x), ptr(targets), ptr(lse), ptr(loss), ptr(ws), ws.numel(),
         stream_handle(stream)))
+
+
+def pe_lm_head_argmax_noalloc(dims, weights, n, x, tokens, logits=None, stream=None):
+    """pe_lm_head_argmax with the library's fixed device array as workspace
+    (allocates nothing)."""
+    w = weights if isinstance(weights, PeWeights) else weights_struct(weights)
+    _check("pe_lm_head_argmax_noalloc", lib().pe_lm_head_argmax_noalloc(
+        ctypes.byref(dims), ctypes.byref(w), n, ptr(x), ptr(tokens), ptr(logits), stream_handle(stream)))
 
 
 def pe_lm_head_argmax(dims, weights, n, x, tokens, logits=None, workspace=None, stream=None):

@@ -4,10 +4,17 @@
 // and attention.hip on the caller's stream.
 #include <math.h>
 #include <string.h>
+#include <mutex>
 #include "pe.h"
 #include "kernels.h"
 
 using namespace pe;
+
+// Workspace of pe_lm_head_argmax_noalloc: a fixed array in the library's
+// device code.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` only names the symbol: its device
+// address comes from hipGetSymbolAddress, once per device (scratch_ptr).
+static __device__ __align__(256) char scratch[PE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -282,6 +289,23 @@ LmWs lm_ws(const pe_drafter_dims* d, int n, void* base, bool loss = false) {
 
 bool ws_ok(void* ws, size_t have, size_t need) {
   return ws && have >= need && (reinterpret_cast<uintptr_t>(ws) & 255) == 0;
+}
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current (thread-safe); nullptr on failure.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    const hipError_t st = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = st == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
 }
 
 pe_status check_attn_bwd(const pe_attn_bwd_args* a) {
@@ -628,16 +652,25 @@ pe_status pe_lm_head_argmax_workspace(const pe_drafter_dims* dims, int32_t n, si
   return PE_OK;
 }
 
-pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weights* w, int32_t n, const float* x,
-                            int32_t* tokens, float* logits, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of pe_lm_head_argmax (everything but the workspace).
+pe_status check_lm_argmax(const pe_drafter_dims* dims, const pe_drafter_weights* w, int32_t n, const float* x,
+                          const int32_t* tokens) {
   pe_status st = check_dims(dims);
   if (st != PE_OK) return st;
   if (!w || n < 0) return PE_ERR_INVALID_ARG;
   if (n == 0) return PE_OK;
   if (!x || !tokens || !w->final_gain || !w->w_lm || !al16(w->w_lm) || !al16(x) || !al16(w->final_gain))
     return PE_ERR_INVALID_ARG;
-  if (!ws_ok(workspace, workspace_bytes, lm_ws(dims, n, nullptr).total)) return PE_ERR_INVALID_ARG;
+  return PE_OK;
+}
+
+// The LM head's launches on a checked workspace (n > 0).
+pe_status run_lm_argmax(const pe_drafter_dims* dims, const pe_drafter_weights* w, int32_t n, const float* x,
+                        int32_t* tokens, float* logits, void* workspace, hipStream_t stream) {
   const LmWs lw = lm_ws(dims, n, workspace);
   const int d = dims->hidden;
   const int bf = dims->dtype == PE_BF16;
@@ -665,6 +698,29 @@ pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weight
   // the two leading tokens of each row, scored again in fp32 from x
   launch_argmax_rescore(lw.top2, used, n, x, d, w->final_gain, dims->eps, w->w_lm, d, bf, tokens, stream);
   return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weights* w, int32_t n, const float* x,
+                            int32_t* tokens, float* logits, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  const pe_status st = check_lm_argmax(dims, w, n, x, tokens);
+  if (st != PE_OK || n == 0) return st;
+  if (!ws_ok(workspace, workspace_bytes, lm_ws(dims, n, nullptr).total)) return PE_ERR_INVALID_ARG;
+  return run_lm_argmax(dims, w, n, x, tokens, logits, workspace, stream);
+}
+
+pe_status pe_lm_head_argmax_noalloc(const pe_drafter_dims* dims, const pe_drafter_weights* w, int32_t n,
+                                    const float* x, int32_t* tokens, float* logits, hipStream_t stream) {
+  const pe_status st = check_lm_argmax(dims, w, n, x, tokens);
+  if (st != PE_OK || n == 0) return st;
+  if (lm_ws(dims, n, nullptr).total > PE_NOALLOC_SCRATCH_BYTES) return PE_ERR_UNSUPPORTED;
+  void* ws = scratch_ptr();  // this device's array, never the symbol itself
+  if (!ws) return PE_ERR_DEVICE;
+  return run_lm_argmax(dims, w, n, x, tokens, logits, ws, stream);
 }
 
 pe_status pe_lm_head_loss_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes) {

@@ -405,6 +405,26 @@ pe_status pe_lm_head_argmax(const pe_drafter_dims* dims, const pe_drafter_weight
 pe_status pe_lm_head_argmax_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes);
 
 /*
+ * pe_lm_head_argmax_noalloc - pe_lm_head_argmax for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and results, with
+ * the workspace taken from a fixed array of PE_NOALLOC_SCRATCH_BYTES in the
+ * library's device code (one per GPU, held until the process ends; its
+ * address is looked up once per device on the first call there).  Returns
+ * PE_ERR_UNSUPPORTED when pe_lm_head_argmax_workspace(dims, n) exceeds that
+ * size (with a 201,088 x 2,880 bf16 head: more than 597 rows), checked
+ * before anything touches the device; PE_ERR_DEVICE when the array's address
+ * cannot be resolved.  Calls
+ * no allocator.  Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller; calls in one stream are ordered.
+ */
+#define PE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pe_status pe_lm_head_argmax_noalloc(const pe_drafter_dims* dims, const pe_drafter_weights* w,
+                                    int32_t n, const float* x, int32_t* tokens, float* logits,
+                                    hipStream_t stream);
+
+/*
  * pe_lm_head_loss - the LM head's log-sum-exp and cross-entropy without the
  * logits.
  *

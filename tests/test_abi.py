@@ -150,3 +150,23 @@ def test_attention_validation_and_workspace():
     a4 = L.attn_args(**{**base, "window_sink": 256, "window_len": 2048})
     assert lib.pe_draft_attention_workspace(ctypes.byref(a4), ctypes.byref(n)) == 0
     assert n.value == 16
+
+
+def test_noalloc_lm_head_refuses_oversized_batches_before_any_device_call():
+    # 598 rows of a 201,088 x 2,880 bf16 head need more workspace than the
+    # fixed array holds: PE_ERR_UNSUPPORTED, decided on the host; 597 fit
+    lib = L.lib()
+    d = L.dims_struct(2880, 64, 8, 64, 8192, 201088, 201087, 1e-6, "bf16")
+    n = ctypes.c_size_t()
+    assert lib.pe_lm_head_argmax_workspace(ctypes.byref(d), 597, ctypes.byref(n)) == 0
+    assert n.value <= (32 << 20)
+    assert lib.pe_lm_head_argmax_workspace(ctypes.byref(d), 598, ctypes.byref(n)) == 0
+    assert n.value > (32 << 20)
+    w = L.PeWeights()
+    w.w_lm = FAKE
+    w.final_gain = FAKE
+    assert lib.pe_lm_head_argmax_noalloc(ctypes.byref(d), ctypes.byref(w), 598, FAKE, FAKE, None, None) == 2
+    # the usual argument checks come first
+    assert lib.pe_lm_head_argmax_noalloc(ctypes.byref(d), ctypes.byref(w), 7, None, FAKE, None, None) == 1
+    assert lib.pe_lm_head_argmax_noalloc(ctypes.byref(d), ctypes.byref(w), -1, FAKE, FAKE, None, None) == 1
+    assert lib.pe_lm_head_argmax_noalloc(ctypes.byref(d), ctypes.byref(w), 0, None, None, None, None) == 0
