@@ -26,14 +26,19 @@ BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch of the LM-head stage measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE, scaled by a 1 GiB copy (profiles/decode_c1_lm_head_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
-LM_STAGE_TRAFFIC = {"fingerprint": "9f0dc7ce5bc13bd2", "bytes": 1164103022}
+LM_STAGE_TRAFFIC = {"fingerprint": "4d19772a7dfe6f22", "bytes": 1165415520}
 LM_SOURCES = ("gemm.hip", "norm.hip", "common.h", "kernels.h", "epilogue.h")
+# The same for one whole c=64 decode step (every kernel of the step), from
+# profiles/decode_c64_step_counters.md.
+DECODE64_TRAFFIC = {"fingerprint": "84d505b532d29ab6", "bytes": 2810140745}
+ALL_SOURCES = ("api.hip", "attention.hip", "batch.hip", "common.h", "epilogue.h", "gemm.hip", "gemm_big.hip",
+               "kernels.h", "norm.hip")
 
 
-def source_fingerprint():
+def source_fingerprint(files=LM_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for f in LM_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "drafter_pe_build_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -44,7 +49,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
+    ap.add_argument("--cpu-configs", default="0,1,2,3,4",
+                    help="configs whose oracle CPU baseline is timed (comma-separated, of 0-4)")
     ap.add_argument("--no-extra", action="store_true", help="skip the c=64 decode and attention measurements")
     ap.add_argument("--attention-only", type=int, choices=(3, 4, 5, 6), default=0,
                     help="time only the COD (3), parallel-group (4), random-anchor (5) or windowed "
@@ -64,26 +71,62 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class CacheFlush:
+    """Evicts the 256 MB Infinity Cache (and the L2s) between timed passes by
+    reading a 512 MB buffer: a read-only pass leaves no dirty lines whose
+    write-back would land in the next timed pass."""
+
+    def __init__(self, nbytes=512 << 20):
+        import torch
+        self.buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        return self.buf.sum()
+
+
+_FLUSH = None
+
+
+def flush_cache():
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = CacheFlush()
+    _FLUSH()
+
+
 def time_loop(fn, steps, warmup, stream):
+    """W untimed passes, then exactly `steps` timed passes, each preceded by a
+    cache flush outside its timed region and bracketed by HIP events on the
+    stream the library launches on (torch's current stream); the whole timed
+    loop sits between two device synchronisations.  Returns the median pass
+    time in ms (the mean, min and max go to time_loop.last)."""
+    import numpy as np
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        flush_cache()
+        e0.record(stream)
         fn()
-    e1.record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps  # ms
+    d = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    time_loop.last = {"median_ms": float(np.median(d)), "mean_ms": float(d.mean()), "min_ms": float(d.min()),
+                      "max_ms": float(d.max()), "passes": int(steps), "cache": "flushed before every pass"}
+    return float(np.median(d))
+
+
+time_loop.last = {}
 
 
 def time_sustained(fn, min_steps, stream, warm_s=0.03, timed_s=0.05):
     """Time fn once its clocks have settled: one pass sizes the loops, then
     at least warm_s seconds of untimed passes and at least timed_s seconds
-    (and min_steps passes) of timed ones.  Short compute-bound kernels run
-    well below their sustained clock during the first tens of milliseconds."""
+    (and min_steps passes) of timed ones, each timed pass after a cache
+    flush; the median pass.  Short compute-bound kernels run well below their
+    sustained clock during the first tens of milliseconds."""
     import math
     import torch
     fn()
@@ -305,18 +348,141 @@ def measure_decode64(dims, W, steps, stream):
     RK2 = st2.R * st2.K
     gs2 = GraphStep(st2)
     ms2 = time_sustained(gs2.replay, steps, stream)
+    st_stats = dict(time_loop.last)
+    # the dominant kernel's stage alone: final RMSNorm, LM head with the fused
+    # top-2, the fp32 re-score of the two leading tokens
+    ms_lm = time_sustained(lambda: st2.lm_head(False), steps, stream)
+    lm_stats = dict(time_loop.last)
     b2, _ = decode_bytes(dims, case2, st2.T, RK2)
-    live2 = int(np.sum(np.diff(case2["cu_window"]) - case2["n_rej"])) + RK2
+    W_ = np.diff(case2["cu_window"])
+    n_acc = W_ - case2["n_rej"]
+    live2 = int(np.sum(n_acc)) + RK2
+    # attention: a query at position P sees P + 1 rows; positions kv_len + n_acc + j, j < K
+    keys = int(np.sum((case2["kv_len"].astype(np.int64) + n_acc)[:, None] + 1 + np.arange(case2["K"])[None, :]))
+    fl_attn = 4.0 * dims.n_q_heads * dims.head_dim * keys
     fl2 = 2.0 * (live2 * (3 * dims.hidden * dims.hidden + dims.qkv_rows * dims.hidden)
                  + RK2 * (dims.hidden * dims.n_q_heads * dims.head_dim + 3 * dims.ffn * dims.hidden
-                          + dims.vocab * dims.hidden))
-    log("  %.1f us" % (ms2 * 1e3))
+                          + dims.vocab * dims.hidden)) + fl_attn
+    fl_lm = 2.0 * RK2 * dims.vocab * dims.hidden
+    log("  step %.1f us, LM stage %.1f us" % (ms2 * 1e3, ms_lm * 1e3))
     del gs2, st2
     torch.cuda.empty_cache()
+    tf_lm = fl_lm / (ms_lm * 1e-3) / 1e12
+    traffic = (DECODE64_TRAFFIC["bytes"] if source_fingerprint(ALL_SOURCES) == DECODE64_TRAFFIC["fingerprint"]
+               else None)
     return {"ms_per_step": ms2, "draft_positions_per_s": RK2 / (ms2 * 1e-3),
+            "timing": st_stats,
+            "algorithmic_bytes": b2, "algorithmic_flops": fl2,
             "hbm_gbs": b2 / (ms2 * 1e-3) / 1e9, "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "gemm_tflops": fl2 / (ms2 * 1e-3) / 1e12,
-            "mfma_frac": fl2 / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+            "mfma_frac": fl2 / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "binding": "mfma (%.0f flop per algorithmic byte, above the %.0f ridge)"
+                       % (fl2 / b2, BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)),
+            "step_traffic_bytes": traffic,
+            "roofline": {"bound": "mfma",
+                         "kernel": "LM-head stage (448 x 201,088 x 2,880 on the matrix cores with the final "
+                                   "RMSNorm, the fused top-2 and the fp32 re-score of the two leading tokens)",
+                         "achieved": tf_lm, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf_lm / BF16_PEAK_TFLOPS, "traffic": None, "launch_us": ms_lm * 1e3,
+                         "algorithmic_flops": fl_lm, "timing": lm_stats}}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_threads():
+    """Threads the fp64 oracle's BLAS calls use (the host cores it may run on)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            n = max(blas)
+    except Exception:
+        pass
+    return n
+
+
+def cpu_oracle_decode(dims, W, case):
+    """One full decode step of the fp64 oracle (batch build, fuse, layer, LM
+    head + argmax); seconds."""
+    from oracle import batch as ob
+    from oracle import drafter as od
+    t0 = time.time()
+    b = ob.build_draft_batch(case["K"], dims.mask_token_id, case["cu_window"], case["n_rej"], case["kv_len"],
+                             case["kv_base"], case["window_ids"], case["window_pos"], case["window_hrow"],
+                             case["new_token"], case["ctx_hrow"], case["target_hidden"], W["h_shared"])
+    od.drafter_forward(dims, W, b, case["kv_base"], case["k_cache"], case["v_cache"], keep_logits=False)
+    return time.time() - t0
+
+
+def cpu_oracle_attention(cfg):
+    """The fp64 oracle's COD attention on a seeded, bounded query sample of the
+    N=4096 (cfg 3) or N=8192 x 8 (cfg 4) layout; the time is extrapolated per
+    query to the whole layout (input generation and the bf16 -> fp64
+    conversion excluded)."""
+    import numpy as np
+    from oracle import cod as oc
+    from oracle import drafter as od
+    from synth import inputs as si
+    Lay = si.cod_config(cfg)
+    q, k, v = (od.to_f64(Lay[n], "bf16") for n in ("q", "k", "v"))
+    T = Lay["T"]
+    if cfg == 3:
+        qs = np.arange(0, T, 32)
+        desc = "every 32nd of the %d query rows (%d queries, all depths)" % (T, len(qs))
+    else:
+        qs = np.concatenate([np.r_[8192 * c:8192 * c + 16, 8192 * (c + 1) - 16:8192 * (c + 1)] for c in range(8)])
+        desc = ("the first and last 16 rows of each of the 8 query chunks (one chunk per depth: %d queries, "
+                "starts 0-15 and 8176-8191)" % len(qs))
+    t0 = time.time()
+    oc.attention(q, k, v, Lay["start"], Lay["depth"], qs)
+    t = time.time() - t0
+    pairs_s = int(np.sum(Lay["start"][qs].astype(np.int64) + 1 + Lay["depth"][qs]))
+    pairs = int(np.sum(Lay["start"].astype(np.int64) + 1 + Lay["depth"]))
+    return {"sample_seconds": t, "sample_queries": int(len(qs)), "sample_pairs": pairs_s, "T": T,
+            "visible_pairs": pairs, "seconds": t * T / len(qs), "sample": desc}
+
+
+def cpu_baselines(dims, W, case1, which):
+    """The fp64 oracle timed on the host cores, one entry per config."""
+    from synth import inputs as si
+    out = {"cpu_model": cpu_model(), "cores": oracle_threads(), "kind": "oracle",
+           "note": "the plain fp64 numpy oracle as written (not tuned); a reported baseline, not a target"}
+    for cfg in which:
+        log("oracle CPU baseline, config %d" % cfg)
+        if cfg == 0:
+            d0, W0, c0 = si.decode_config(0)
+            t = cpu_oracle_decode(d0, W0, c0)
+            n = c0["R"] * c0["K"]
+            out["tiny_fp32_n128_k4"] = {"seconds": t, "value": n / t, "unit": "draft positions/s",
+                                        "sample": "one full step (%d draft positions)" % n}
+        elif cfg == 1:
+            t = cpu_oracle_decode(dims, W, case1)
+            n = case1["R"] * case1["K"]
+            out["decode_c1"] = {"seconds": t, "value": n / t, "unit": "draft positions/s",
+                                "sample": "one full step (%d draft positions)" % n}
+        elif cfg == 2:
+            _, _, c2 = si.decode_config(2, with_weights=False)
+            t = cpu_oracle_decode(dims, W, c2)
+            n = c2["R"] * c2["K"]
+            out["decode_c64"] = {"seconds": t, "value": n / t, "unit": "draft positions/s",
+                                 "sample": "one full step (%d draft positions)" % n}
+        else:
+            r = cpu_oracle_attention(cfg)
+            name = "cod_attention_n4096" if cfg == 3 else "group_attention_n8192"
+            out[name] = {**r, "value": r["T"] / r["seconds"], "unit": "positions/s (extrapolated per query)"}
+        log("  done")
+    return out
 
 
 def main():
@@ -335,6 +501,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.copy_probe:  # three 1 GiB device copies: the scale of the HBM byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     if args.attention_only:
         if args.attention_only == 5:
             r = measure_anchor(args.steps, stream)
@@ -369,21 +543,26 @@ def main():
     st = DraftStep(dims, W, case1)
     RK = st.R * st.K
     ms_eager = time_loop(st.run, args.steps, args.warmup, stream)
-    log("c=1 step, eager launches: %.1f us" % (ms_eager * 1e3))
+    stats_eager = dict(time_loop.last)
+    log("c=1 step, eager launches: %.1f us (median)" % (ms_eager * 1e3))
     gs = GraphStep(st)
     ms = time_loop(gs.replay, args.steps, args.warmup, stream)
+    stats_graph = dict(time_loop.last)
     step_bytes, weight_bytes = decode_bytes(dims, case1, st.T, RK)
     ms_graph = ms
     log("c=1 step, one graph replay: %.1f us" % (ms_graph * 1e3))
     launch_mode = "one HIP graph replay of the four stage calls"
+    stats = stats_graph
     if ms_eager < ms_graph:
         ms = ms_eager
+        stats = stats_eager
         launch_mode = "the four stage calls launched eagerly on one stream"
 
     # dominant kernel: the LM-head stage (the W_lm stream with the final
     # RMSNorm in its staging and the fused argmax, then the reduce of the
     # per-workgroup partials)
     lm_ms = time_loop(lambda: st.lm_head(False), args.steps, args.warmup, stream)
+    lm_stats = dict(time_loop.last)
     # algorithmic bytes: W_lm once, the x rows (f32), the tokens
     lm_bytes = dims.vocab * dims.hidden * 2 + RK * dims.hidden * 4 + RK * 4
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
@@ -400,6 +579,8 @@ def main():
         "eager_ms_per_step": ms_eager,
         "graph_ms_per_step": ms_graph,
         "launch": launch_mode + " (the faster of eager launches and graph replay)",
+        "timing": {**stats, "statistic": "median of the timed steps, each after a 512 MB cache flush, "
+                                         "by HIP events on the library's stream"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -416,18 +597,10 @@ def main():
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lm_gbs / HBM_PEAK_GBS,
                      "traffic": (LM_STAGE_TRAFFIC["bytes"]
                                  if source_fingerprint() == LM_STAGE_TRAFFIC["fingerprint"] else None),
-                     "launch_us": lm_ms * 1e3, "algorithmic_bytes": lm_bytes},
+                     "launch_us": lm_ms * 1e3, "algorithmic_bytes": lm_bytes, "timing": lm_stats},
     }
     del gs, st
     torch.cuda.empty_cache()
-    if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        torch.cuda.empty_cache()
 
     if not args.no_extra:
         extra = {}
@@ -441,27 +614,14 @@ def main():
         result["secondary"] = extra
 
     if not args.no_cpu:
-        log("oracle CPU baseline (one full c=1 step in fp64)")
-        ncores = len(os.sched_getaffinity(0))
-        try:
-            from threadpoolctl import threadpool_info
-            blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
-            if blas:
-                ncores = max(blas)
-        except Exception:
-            pass
-        from oracle import batch as ob
-        from oracle import drafter as od
-        t0 = time.time()
-        b = ob.build_draft_batch(case1["K"], dims.mask_token_id, case1["cu_window"], case1["n_rej"],
-                                 case1["kv_len"], case1["kv_base"], case1["window_ids"], case1["window_pos"],
-                                 case1["window_hrow"], case1["new_token"], case1["ctx_hrow"],
-                                 case1["target_hidden"], W["h_shared"])
-        od.drafter_forward(dims, W, b, case1["kv_base"], case1["k_cache"], case1["v_cache"], keep_logits=False)
-        tc = time.time() - t0
-        result["cpu_baseline"] = {"value": RK / tc, "unit": "draft positions/s", "cores": ncores, "kind": "oracle",
-                                  "sample": "one full c=1 decode step (7 draft positions), fp64 numpy, %.1f s" % tc}
-        log("  %.1f s" % tc)
+        which = sorted({int(c) for c in args.cpu_configs.split(",") if c.strip()} | {1})
+        cb = cpu_baselines(dims, W, case1, which)
+        c1 = cb["decode_c1"]
+        result["cpu_baseline"] = {"value": c1["value"], "unit": "draft positions/s", "cores": cb["cores"],
+                                  "kind": "oracle", "cpu_model": cb["cpu_model"],
+                                  "sample": "one full c=1 decode step (7 draft positions), fp64 numpy, %.2f s"
+                                            % c1["seconds"]}
+        result["cpu_baseline_by_config"] = cb
     print(json.dumps(result), flush=True)
 
 

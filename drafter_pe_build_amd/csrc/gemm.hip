@@ -912,7 +912,10 @@ __global__ __launch_bounds__(256) void argmax_rescore_kernel(const u32x4* part, 
   constexpr int CH = Storage<S>::CH;  // elements per 16-byte chunk
   constexpr int STEP = 4 * CH;        // elements per packed 1 KB step of a 16-row block
   constexpr int NPRE = 2;             // chunks per thread held from before the merge (K <= 512 CH)
-  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rpx = (M + 7) / 8;  // rows per XCD (see launch_argmax_rescore)
+  const int m = (int)(blockIdx.x % 8) * rpx + (int)(blockIdx.x / 8);
+  if (m >= M) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = K / CH;
   const float* xr = x + (int64_t)m * ldx;
   // the row and its gains first, so that their loads overlap the partials'
@@ -1011,12 +1014,16 @@ __global__ __launch_bounds__(256) void argmax_rescore_kernel(const u32x4* part, 
 void launch_argmax_rescore(const u32x4* part, int P, int M, const float* x, int64_t ldx, const float* gain,
                            float eps, const void* W, int K, int w_bf16, int32_t* tokens, hipStream_t s) {
   const char* w = reinterpret_cast<const char*>(W);
+  // workgroup b runs on XCD b % 8 and takes row (b % 8) * rpx + b / 8, so the
+  // rows of one XCD are consecutive and share the lines of the tile-major
+  // lists in that XCD's L2 (eight rows' lists of one partial per 128 bytes)
+  const int rpx = (M + 7) / 8;
   if (w_bf16)
-    hipLaunchKernelGGL(argmax_rescore_kernel<uint16_t>, dim3(M), dim3(256), 0, s, part, P, M, x, ldx, gain, eps, w, K,
-                       tokens);
+    hipLaunchKernelGGL(argmax_rescore_kernel<uint16_t>, dim3(8 * rpx), dim3(256), 0, s, part, P, M, x, ldx, gain, eps,
+                       w, K, tokens);
   else
-    hipLaunchKernelGGL(argmax_rescore_kernel<float>, dim3(M), dim3(256), 0, s, part, P, M, x, ldx, gain, eps, w, K,
-                       tokens);
+    hipLaunchKernelGGL(argmax_rescore_kernel<float>, dim3(8 * rpx), dim3(256), 0, s, part, P, M, x, ldx, gain, eps,
+                       w, K, tokens);
 }
 
 // Log-sum-exp of each row from its P partial (maximum, sum of exp) pairs, merged
