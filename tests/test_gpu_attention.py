@@ -134,11 +134,14 @@ def test_cod_training_shape_n4096():
     out, lse, cnt, hsh = run_cod(Dv, Lay)
     torch.cuda.synchronize()
     go = Lay["group_off"]
+    # values: every query of the last 256 rows of each depth group (the
+    # largest starts, so every prefix tile), the first 8 of each group, and
+    # 2 % of all rows at random
     sample = set()
     for e in range(len(go) - 1):
         sample.update(range(go[e], min(go[e] + 8, go[e + 1])))
-        sample.update(range(max(go[e], go[e + 1] - 8), go[e + 1]))
-    sample.update(np.random.default_rng(0).choice(Lay["T"], 64, replace=False).tolist())
+        sample.update(range(max(go[e], go[e + 1] - 256), go[e + 1]))
+    sample.update(np.random.default_rng(0).choice(Lay["T"], int(0.02 * Lay["T"]) + 1, replace=False).tolist())
     check_against_oracle(Lay, out, lse, None, None, np.array(sorted(sample)), "N=4096 values")
     # index stats of every query
     rc, rh = oc.index_stats(Lay["start"], Lay["depth"])
@@ -313,10 +316,14 @@ def test_long_sequence_chunked_n8192():
     # visible-pair closed form through the kernel's own counters
     assert int(cnt[:, 0].sum().item()) == 268697600
     g = np.random.default_rng(1)
+    # values: every query of the first and last 64 rows of each chunk (two
+    # 32-query workgroup tiles at both chunk edges; one chunk per depth) and
+    # 0.5 % of all rows at random
     sample = set()
     for c in range(8):
-        sample.update([8192 * c, 8192 * c + 1, 8192 * c + 8190, 8192 * c + 8191])
-    sample.update(g.choice(T, 24, replace=False).tolist())
+        sample.update(range(8192 * c, 8192 * c + 64))
+        sample.update(range(8192 * (c + 1) - 64, 8192 * (c + 1)))
+    sample.update(g.choice(T, int(0.005 * T) + 1, replace=False).tolist())
     check_against_oracle(Lay, out, lse, cnt, hsh, np.array(sorted(sample)), "N=8192 sampled")
 
 

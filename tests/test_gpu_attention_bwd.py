@@ -112,27 +112,49 @@ def test_backward_training_shape_n4096():
     out, lse = _forward(Dv, Lay)
     dq, dk, dv = _backward(Dv, Lay, out, lse, [(0, T)])
     tol = TOL["bf16"]
-    # dq of sampled queries: each query's dq needs only its own keys
     go = Lay["group_off"]
-    sample = set(np.random.default_rng(5).choice(T, 20, replace=False).tolist())
-    for e in range(len(go) - 1):
-        sample.update([int(go[e]), int(go[e + 1]) - 1])
-    qs = np.array(sorted(sample))
-    rq, _, _ = _oracle(Lay, dout, qs)
-    e = om.relerr(dev_to_f64(dq)[qs], rq)
-    say("  dq relerr %.3g (%d queries)" % (e, len(qs)))
+    start, depth = Lay["start"], Lay["depth"]
+    D = len(go) - 1
+    # key rows checked in full: every chain row of the deepest group (each is
+    # seen by itself only) and the last 64 original positions (seen by the
+    # queries starting there); their viewers plus a dq sample (32 queries of
+    # each depth group and 64 at random) go through the oracle in one call
+    deep = np.arange(go[D - 1], go[D])
+    late = np.arange(N - 64, N)
+    viewers = np.nonzero(start >= N - 64)[0]
+    dq_rows = set(np.random.default_rng(5).choice(T, 64, replace=False).tolist())
+    for e in range(D):
+        dq_rows.update(np.linspace(go[e], go[e + 1] - 1, 32).astype(int).tolist())
+    qs = np.array(sorted(set(deep.tolist()) | set(viewers.tolist()) | dq_rows))
+    say("  oracle backward over %d queries" % len(qs))
+    rq, rk, rv = _oracle(Lay, dout, qs)
+    pos = {int(t): n for n, t in enumerate(qs)}
+    dqr = np.array(sorted(dq_rows))
+    e = om.relerr(dev_to_f64(dq)[dqr], rq[[pos[int(t)] for t in dqr]])
+    say("  dq relerr %.3g (%d queries)" % (e, len(dqr)))
     assert e <= tol
-    # dk, dv of key rows seen by few queries: late original positions and chain rows
-    keys = [N - 1, N - 3, N - 20, int(go[1]), int(go[2]) + 5, T - 1]
-    for j in keys:
-        viewers = np.nonzero([oc.visible(Lay["start"][t], Lay["depth"][t], np.array([Lay["start"][j]]),
-                                         np.array([Lay["depth"][j]]))[0] for t in range(T)])[0]
-        _, rk, rv = _oracle(Lay, dout, viewers)
-        ek = om.relerr(dev_to_f64(dk)[j], rk[j])
-        ev = om.relerr(dev_to_f64(dv)[j], rv[j])
-        say("  key row %d (start %d depth %d, %d viewers): dk relerr %.3g dv relerr %.3g"
-            % (j, Lay["start"][j], Lay["depth"][j], len(viewers), ek, ev))
+    gk, gv = dev_to_f64(dk), dev_to_f64(dv)
+    for name, rows in (("depth-%d chain rows" % (D - 1), deep), ("last 64 positions", late)):
+        # every viewer of these rows is among the oracle's queries
+        for j in rows[:: max(1, len(rows) // 8)]:
+            vis = oc.visible(start, depth, np.array([start[j]]), np.array([depth[j]]))
+            assert set(np.nonzero(vis)[0].tolist()) <= set(qs.tolist())
+        ek = om.relerr(gk[rows], rk[rows])
+        ev = om.relerr(gv[rows], rv[rows])
+        say("  %s (%d rows): dk relerr %.3g dv relerr %.3g" % (name, len(rows), ek, ev))
         assert ek <= tol and ev <= tol
+    # identities over every row: the probabilities of a query sum to one, so
+    # sum_j dV[j] is the sum of dout over the queries of each kv head's group,
+    # and dS sums to zero over a query's keys, so sum_j dK[j] = 0
+    Hq, Hkv, Dh = Lay["heads"]
+    G = Hq // Hkv
+    dsum = dev_to_f64(Dv["dout"]).reshape(T, Hkv, G, Dh).sum(axis=(0, 2))
+    e = om.relerr(gv.sum(axis=0), dsum)
+    say("  sum of dV over all rows vs sum of dout: relerr %.3g" % e)
+    assert e <= tol
+    ek0 = np.abs(gk.sum(axis=0)).max() / np.abs(gk).sum(axis=0).max()
+    say("  |sum of dK over all rows| / sum |dK|: %.3g" % ek0)
+    assert ek0 <= tol
 
 
 def test_backward_empty_chunk_is_noop():
