@@ -177,6 +177,38 @@ def lm_head_loss(x, final_gain, w_lm, eps, targets, dtype="f64", chunk=16384):
     return lse, loss
 
 
+def lm_head_kl_topk(x, final_gain, w_lm, eps, target_ids, target_probs, dtype="f64", chunk=16384):
+    """KL divergence from a target distribution given by its top-k entries to
+    the drafter's LM-head distribution, row by row.
+
+    [RFC] "Experiment Setup": the drafter is trained with a KL loss against
+    the verifier's output distribution.  The target arrives as k (token id,
+    probability) pairs per row (the verifier's top-k, zero mass elsewhere):
+        q = softmax(z),  z = W_lm RMSNorm(x),
+        KL(p || q) = sum_j p_j (log p_j - log q_j)
+                   = sum_j p_j (log p_j - z[id_j] + lse).
+    A pair whose id lies outside [0, V) or whose probability is not positive
+    adds nothing (p log p -> 0 as p -> 0; no logit exists outside the
+    vocabulary).  The probabilities are used as given (no renormalisation).
+    Returns (lse, kl) [n] float64; lse as in lm_head_loss.
+    """
+    ids = np.asarray(target_ids, dtype=np.int64)
+    p = np.asarray(target_probs, dtype=np.float64)
+    n = ids.shape[0]
+    V = w_lm.shape[0]
+    lse, _ = lm_head_loss(x, final_gain, w_lm, eps, np.full(n, -1), dtype=dtype, chunk=chunk)
+    f = rmsnorm(np.asarray(x, dtype=np.float64), final_gain, eps)
+    kl = np.zeros(n)
+    for i in range(n):
+        use = (ids[i] >= 0) & (ids[i] < V) & (p[i] > 0)
+        t = ids[i][use]
+        w = w_lm[t]
+        w = bf16_to_f64(w) if dtype == "bf16" else np.asarray(w, dtype=np.float64)
+        z = w @ f[i]
+        kl[i] = np.sum(p[i][use] * (np.log(p[i][use]) - z + lse[i]))
+    return lse, kl
+
+
 def drafter_forward(dims, weights, batch, kv_base, k_cache, v_cache, keep_logits=True):
     """Stages 2-4 of the drafter on a built batch (stage 1 is oracle.batch).
 

@@ -6,7 +6,11 @@ of torch fp64 CPU ops (rms_norm, linear, scaled_dot_product_attention with a
 boolean mask and GQA, silu).  Argmax: numpy's first maximum, including ties
 across the oracle's vocabulary slices.  LM-head loss: torch's logsumexp and
 cross_entropy (ignore_index) in fp64 over slices that do not divide V, log V
-for equal logits, and direct summation on a two-token vocabulary.
+for equal logits, and direct summation on a two-token vocabulary.  Top-k KL
+loss: torch's kl_div of the log-softmax (a full target in shuffled order and
+a sparse top-k target scattered into the vocabulary), the cross-entropy for a
+one-hot target, zero for the drafter's own distribution, sum p log p + log V
+for equal logits, and ignored pairs (p = 0, ids outside the vocabulary).
 """
 import numpy as np
 import pytest
@@ -182,3 +186,79 @@ def test_lm_head_loss_closed_forms():
     z = np.array([f[0, 0], 2 * f[0, 1]])
     assert abs(lse[0] - np.log(np.exp(z[0]) + np.exp(z[1]))) < 1e-14
     assert abs(loss[0] - (lse[0] - z[1])) < 1e-14
+
+
+def _kl_case(seed, n=6, d=16, V=500):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((n, d))
+    gain = g.uniform(0.5, 1.5, d)
+    w = g.standard_normal((V, d)) * 0.5
+    return x, gain, w
+
+
+def test_lm_head_kl_against_torch_kl_div():
+    # a full target distribution over the whole vocabulary (k = V, in shuffled
+    # order): torch's kl_div of the log-softmax in fp64
+    x, gain, w = _kl_case(41)
+    n, V = x.shape[0], w.shape[0]
+    g = np.random.default_rng(42)
+    logits_t = g.standard_normal((n, V)) * 2.0
+    p = np.exp(logits_t - logits_t.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    perm = np.stack([g.permutation(V) for _ in range(n)])
+    ids = perm
+    probs = np.take_along_axis(p, perm, axis=1)
+    lse, kl = od.lm_head_kl_topk(x, gain, w, 1e-6, ids, probs, chunk=128)
+    z = torch.from_numpy(od.rmsnorm(x, gain, 1e-6) @ w.T)
+    ref = F.kl_div(F.log_softmax(z, dim=1), torch.from_numpy(p), reduction="none").sum(1).numpy()
+    np.testing.assert_allclose(kl, ref, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(z, 1).numpy(), rtol=1e-13)
+
+
+def test_lm_head_kl_topk_against_torch_kl_div_sparse():
+    # a top-k target (zero mass elsewhere): torch's kl_div over the dense
+    # vocabulary with the k probabilities scattered in, zeros contributing 0
+    x, gain, w = _kl_case(43)
+    n, V, k = x.shape[0], w.shape[0], 7
+    g = np.random.default_rng(44)
+    ids = np.stack([g.choice(V, k, replace=False) for _ in range(n)])
+    probs = g.dirichlet(np.ones(k), n)
+    _, kl = od.lm_head_kl_topk(x, gain, w, 1e-6, ids, probs, chunk=77)
+    dense = np.zeros((n, V))
+    np.put_along_axis(dense, ids, probs, axis=1)
+    z = torch.from_numpy(od.rmsnorm(x, gain, 1e-6) @ w.T)
+    ref = F.kl_div(F.log_softmax(z, dim=1), torch.from_numpy(dense), reduction="none").sum(1).numpy()
+    np.testing.assert_allclose(kl, ref, rtol=1e-11, atol=1e-13)
+    assert np.all(kl > 0)                               # Gibbs: p differs from q
+
+
+def test_lm_head_kl_special_cases():
+    x, gain, w = _kl_case(45)
+    n, V = x.shape[0], w.shape[0]
+    # one-hot target: the cross-entropy of that token
+    t = np.random.default_rng(46).integers(0, V, n)
+    _, kl = od.lm_head_kl_topk(x, gain, w, 1e-6, t[:, None], np.ones((n, 1)), chunk=64)
+    _, ce = od.lm_head_loss(x, gain, w, 1e-6, t, chunk=64)
+    np.testing.assert_allclose(kl, ce, rtol=1e-13)
+    # the drafter's own distribution as the target: KL = 0
+    z = od.rmsnorm(x, gain, 1e-6) @ w.T
+    q = np.exp(z - z.max(1, keepdims=True))
+    q /= q.sum(1, keepdims=True)
+    ids = np.tile(np.arange(V), (n, 1))
+    _, kl0 = od.lm_head_kl_topk(x, gain, w, 1e-6, ids, q, chunk=64)
+    assert np.max(np.abs(kl0)) < 1e-12
+    # equal logits: KL = sum p log p + log V
+    p = np.array([[0.5, 0.25, 0.25], [1.0, 0.0, 0.0]])
+    _, klu = od.lm_head_kl_topk(x[:2], gain, np.zeros((V, x.shape[1])), 1e-6, [[3, 9, 400], [7, 8, 9]], p)
+    np.testing.assert_allclose(klu, [np.log(V) - 1.5 * np.log(2.0), np.log(V)], rtol=1e-14)
+    # zero-probability and out-of-vocabulary pairs add nothing; order is free
+    ids = np.array([[5, 17, 200, -1, V, 31]])
+    pr = np.array([[0.2, 0.3, 0.5, 0.7, 0.9, 0.0]])
+    _, a = od.lm_head_kl_topk(x[:1], gain, w, 1e-6, ids, pr)
+    _, b = od.lm_head_kl_topk(x[:1], gain, w, 1e-6, ids[:, [2, 0, 1]], pr[:, [2, 0, 1]])
+    np.testing.assert_allclose(a, b, rtol=1e-14)
+    # bf16 storage: the same as fp64 weights holding the decoded values
+    wb = si.f32_to_bf16_bits(w.astype(np.float32))
+    _, kb = od.lm_head_kl_topk(x[:1], gain, wb, 1e-6, ids, pr, dtype="bf16")
+    _, kf = od.lm_head_kl_topk(x[:1], gain, od.bf16_to_f64(wb), 1e-6, ids, pr)
+    np.testing.assert_array_equal(kb, kf)
