@@ -328,11 +328,23 @@ def measure_loss(dims, steps, stream, W=None):
     ms = time_sustained(lambda: L.pe_lm_head_loss(cd, cw, n, x, t, lse, loss, workspace=ws), steps, stream)
     fl = 2.0 * n * dims.vocab * dims.hidden
     log("  %.1f us, %.0f TFLOP/s" % (ms * 1e3, fl / (ms * 1e-3) / 1e12))
-    del cw, x, t, lse, loss, ws
+    # the top-k KL variant on the same rows: k = 32 target pairs per row
+    k = 32
+    ids, pr = si.kl_targets(n, dims.vocab, k, 7)
+    ids, pr = torch.from_numpy(ids).cuda(), torch.from_numpy(pr).cuda()
+    kl = torch.empty(n, dtype=torch.float32, device="cuda")
+    wsk = torch.empty(L.pe_lm_head_kl_workspace(cd, n), dtype=torch.uint8, device="cuda")
+    kms = time_sustained(lambda: L.pe_lm_head_kl(cd, cw, n, x, k, ids, pr, kl, lse, workspace=wsk), steps, stream)
+    log("  top-%d KL: %.1f us" % (k, kms * 1e3))
+    del cw, x, t, lse, loss, ws, ids, pr, kl, wsk
     torch.cuda.empty_cache()
     return {"rows": n, "ms": ms, "rows_per_s": n / (ms * 1e-3), "tflops": fl / (ms * 1e-3) / 1e12,
             "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "logits_bytes_avoided": n * dims.vocab * 4}
+            "logits_bytes_avoided": n * dims.vocab * 4,
+            "kl_topk": {"k": k, "ms": kms, "rows_per_s": n / (kms * 1e-3),
+                        "tflops": fl / (kms * 1e-3) / 1e12, "mfma_frac": fl / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                        "note": "log-sum-exp pass plus one fp32 dot product per target pair (n * k rows of W_lm "
+                                "gathered)"}}
 
 
 def measure_decode64(dims, W, steps, stream):

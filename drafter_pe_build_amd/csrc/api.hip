@@ -264,12 +264,13 @@ struct LmWs {
   u32x4* top2;
   float* ps;
   float* tgt;
+  float* lse;  // KL loss: the rows' log-sum-exp when the caller keeps none
   int* zero;
   int nzero;
   size_t total;
 };
 
-LmWs lm_ws(const pe_drafter_dims* d, int n, void* base, bool loss = false) {
+LmWs lm_ws(const pe_drafter_dims* d, int n, void* base, bool loss = false, bool kl = false) {
   LmWs w{};
   Carver c(base);
   const size_t P = (size_t)gemm_argmax_partials(n, d->vocab);
@@ -278,6 +279,7 @@ LmWs lm_ws(const pe_drafter_dims* d, int n, void* base, bool loss = false) {
     w.pv = static_cast<float*>(c.take(P * n * 4));
     w.ps = static_cast<float*>(c.take(P * n * 4));
     w.tgt = static_cast<float*>(c.take((size_t)n * 4));
+    if (kl) w.lse = static_cast<float*>(c.take((size_t)n * 4));
   } else {
     w.top2 = static_cast<u32x4*>(c.take(P * n * 16));
   }
@@ -769,6 +771,58 @@ pe_status pe_lm_head_loss(const pe_drafter_dims* dims, const pe_drafter_weights*
   gp.epi.tgt_logit = lw.tgt;
   const int used = launch_gemm(gp, bf, stream);
   launch_lse_reduce(lw.pv, lw.ps, used, n, dims->vocab, targets, lw.tgt, lse, loss, stream);
+  return launched();
+}
+
+pe_status pe_lm_head_kl_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes) {
+  pe_status st = check_dims(dims);
+  if (st != PE_OK) return st;
+  if (!bytes || n < 0) return PE_ERR_INVALID_ARG;
+  *bytes = lm_ws(dims, n, nullptr, true, true).total;
+  return PE_OK;
+}
+
+pe_status pe_lm_head_kl(const pe_drafter_dims* dims, const pe_drafter_weights* w, int32_t n, const float* x,
+                        int32_t k, const int32_t* target_ids, const float* target_probs, float* lse, float* kl,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pe_status st = check_dims(dims);
+  if (st != PE_OK) return st;
+  if (!w || n < 0 || k < 1) return PE_ERR_INVALID_ARG;
+  if ((int64_t)n * k > INT32_MAX) return PE_ERR_INVALID_ARG;
+  if (n == 0) return PE_OK;
+  if (!x || !w->final_gain || !w->w_lm || !al16(w->w_lm) || !al16(x) || !al16(w->final_gain)) return PE_ERR_INVALID_ARG;
+  if (!target_ids || !target_probs || !kl) return PE_ERR_INVALID_ARG;
+  const int bf = dims->dtype == PE_BF16;
+  if (kl_topk_lds_bytes(dims->hidden, bf) > 65536) return PE_ERR_UNSUPPORTED;
+  if (!ws_ok(workspace, workspace_bytes, lm_ws(dims, n, nullptr, true, true).total)) return PE_ERR_INVALID_ARG;
+  const LmWs lw = lm_ws(dims, n, workspace, true, true);
+  const int d = dims->hidden;
+  // the log-sum-exp of z = w_lm RMSNorm(x), streamed tile by tile as in pe_lm_head_loss
+  GemmParams gp{};
+  gp.X = x;
+  gp.ldx = d;
+  gp.W = w->w_lm;
+  gp.M = n;
+  gp.N = dims->vocab;
+  gp.K = d;
+  gp.xzero = lw.zero;
+  gp.nrm.gain = w->final_gain;
+  gp.nrm.segs = 1;
+  gp.nrm.seg_len = d;
+  gp.nrm.eps = dims->eps;
+  gp.nrm.x_f32 = 1;
+  gp.nrm.tmp = lw.f;
+  gp.clear = lw.zero;
+  gp.nclear = lw.nzero;
+  gp.epi.kind = EPI_LSE;
+  gp.epi.part_val = lw.pv;
+  gp.epi.part_sum = lw.ps;
+  const int used = launch_gemm(gp, bf, stream);
+  float* l = lse ? lse : lw.lse;
+  launch_lse_reduce(lw.pv, lw.ps, used, n, dims->vocab, nullptr, nullptr, l, nullptr, stream);
+  // the target logits in fp32 and the KL sum of each row
+  launch_kl_topk(x, d, w->final_gain, dims->eps, w->w_lm, d, dims->vocab, bf, k, target_ids, target_probs, l, kl, n,
+                 stream);
   return launched();
 }
 

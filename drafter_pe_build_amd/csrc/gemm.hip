@@ -1093,6 +1093,101 @@ void launch_lse_reduce(const float* pv, const float* ps, int P, int M, int N, co
     hipLaunchKernelGGL(lse_reduce_kernel, dim3(M), dim3(256), 0, s, pv, ps, P, M, N, targets, tgt, lse, loss);
 }
 
+// KL divergence of row m from its k target pairs (one workgroup per row):
+//   kl[m] = sum_j p_j (log p_j - z_j + lse[m]),  z_j = inv * sum_k W[id_j][k] x[m][k] g[k],
+// over the pairs with id_j in [0, N) and p_j > 0.  The row's x * g is staged
+// in LDS (zero-padded to whole rounds of chunks, so that the weight loads of
+// a round need no predicate: their chunk index is clamped instead and meets a
+// zero); wave w takes pairs w, w + 4, ..., each as one wave-wide dot product
+// with U chunk loads in flight per lane; the four waves' sums are added in a
+// fixed order.  The target logits are fp32 from the unrounded row, as in the
+// argmax re-score.
+template <typename S>
+__global__ __launch_bounds__(256) void kl_topk_kernel(const float* x, int64_t ldx, const float* gain, float eps,
+                                                      const char* W, int K, int N, int k, const int32_t* ids,
+                                                      const float* probs, const float* lse, float* kl, int M) {
+  constexpr int CH = Storage<S>::CH;  // elements per 16-byte chunk
+  constexpr int STEP = 4 * CH;        // elements per packed 1 KB step of a 16-row block
+  constexpr int U = 4;                // chunk loads in flight per lane
+  extern __shared__ float sf[];
+  const int rpx = (M + 7) / 8;  // rows per XCD, consecutive rows on one XCD (as in the re-score)
+  const int m = (int)(blockIdx.x % 8) * rpx + (int)(blockIdx.x / 8);
+  if (m >= M) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = K / CH;
+  const int npad = (nch + 64 * U - 1) / (64 * U) * (64 * U);
+  const float* xr = x + (int64_t)m * ldx;
+  float ss = 0.f;
+  for (int e = 4 * tid; e < npad * CH; e += 1024) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (e < K) {
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(xr + e);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gain + e);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ss += xv[q] * xv[q];
+        v[q] = xv[q] * gv[q];
+      }
+    }
+    *reinterpret_cast<f32x4*>(sf + e) = v;
+  }
+  ss = wave_sum(ss);
+  __shared__ float sred[4];
+  if (lane == 0) sred[wave] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf(((sred[0] + sred[1]) + (sred[2] + sred[3])) / (float)K + eps);
+  const float L = lse[m];
+  const int steps = K / STEP;
+  float acc = 0.f;
+  for (int j = wave; j < k; j += 4) {
+    const int t = ids[(int64_t)m * k + j];
+    const float p = probs[(int64_t)m * k + j];
+    if (t < 0 || t >= N || !(p > 0.f)) continue;  // the same pair for the whole wave
+    const char* wr = W + (int64_t)(t >> 4) * steps * 1024 + (t & 15) * 16;
+    float d = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 64 * U) {
+      u32x4 a[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ch = min(c0 + 64 * u + lane, nch - 1);
+        const int k0 = ch * CH;
+        a[u] = ld16(wr + (int64_t)(k0 / STEP) * 1024 + ((k0 % STEP) / CH) * 256);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float* f = sf + (c0 + 64 * u + lane) * CH;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) d += chunk_elem<S>(a[u], e) * f[e];
+      }
+    }
+    d = wave_sum(d);  // the same value in every lane
+    acc += p * (logf(p) - d * inv + L);
+  }
+  __shared__ float sacc[4];
+  if (lane == 0) sacc[wave] = acc;
+  __syncthreads();
+  if (tid == 0) kl[m] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
+}
+
+int kl_topk_lds_bytes(int K, int w_bf16) {
+  const int CH = w_bf16 ? 8 : 4, U = 4;
+  const int nch = K / CH;
+  return (nch + 64 * U - 1) / (64 * U) * (64 * U) * CH * 4;
+}
+
+void launch_kl_topk(const float* x, int64_t ldx, const float* gain, float eps, const void* W, int K, int N, int w_bf16,
+                    int k, const int32_t* ids, const float* probs, const float* lse, float* kl, int M, hipStream_t s) {
+  const char* w = reinterpret_cast<const char*>(W);
+  const int rpx = (M + 7) / 8;
+  const size_t lds = (size_t)kl_topk_lds_bytes(K, w_bf16);
+  if (w_bf16)
+    hipLaunchKernelGGL(kl_topk_kernel<uint16_t>, dim3(8 * rpx), dim3(256), lds, s, x, ldx, gain, eps, w, K, N, k, ids,
+                       probs, lse, kl, M);
+  else
+    hipLaunchKernelGGL(kl_topk_kernel<float>, dim3(8 * rpx), dim3(256), lds, s, x, ldx, gain, eps, w, K, N, k, ids,
+                       probs, lse, kl, M);
+}
+
 // ---------------------------------------------------------------------------
 // Dispatch
 static constexpr int kStreamU = 8;     // 1 KB steps in flight per wave

@@ -188,6 +188,13 @@ void launch_argmax_rescore(const u32x4* part, int P, int M, const float* x, int6
 // loss may be null.
 void launch_lse_reduce(const float* pv, const float* ps, int P, int M, int N, const int32_t* targets,
                        const float* tgt, float* lse, float* loss, hipStream_t s);
+// kl[m] = sum_j p[m][j] (log p[m][j] - z[m][id[m][j]] + lse[m]) over the k
+// pairs of row m with an id in [0, N) and p > 0; z from the unrounded
+// normalised row in fp32 (as in launch_argmax_rescore).  ids, probs: [M, k].
+// Dynamic LDS: kl_topk_lds_bytes(K, w_bf16) (the row's x * g, padded).
+int kl_topk_lds_bytes(int K, int w_bf16);
+void launch_kl_topk(const float* x, int64_t ldx, const float* gain, float eps, const void* W, int K, int N, int w_bf16,
+                    int k, const int32_t* ids, const float* probs, const float* lse, float* kl, int M, hipStream_t s);
 
 struct AttnParams {
   const void* q;

@@ -446,6 +446,33 @@ pe_status pe_lm_head_loss(const pe_drafter_dims* dims, const pe_drafter_weights*
                           hipStream_t stream);
 pe_status pe_lm_head_loss_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes);
 
+/*
+ * pe_lm_head_kl - the LM head's KL loss against a top-k target distribution,
+ * without the logits.
+ *
+ * "[RFC]: Add random anchor for p-eagle first position", section "Experiment
+ * Setup": the drafter is trained with a KL loss against the verifier's
+ * distribution.  Here the target of row i arrives as k (token id,
+ * probability) pairs, row-major in target_ids [n, k] int32 and target_probs
+ * [n, k] f32 (device; the verifier's top-k, zero mass elsewhere).  With
+ * z = w_lm RMSNorm(x[i], final_gain) and lse[i] = log sum_v exp(z_v):
+ *   kl[i] = sum_j p_ij (log p_ij - z[id_ij] + lse[i])   ( = KL(p_i || softmax(z)) )
+ * A pair whose id lies outside [0, vocab) or whose probability is not
+ * positive (NaN included) adds nothing; the probabilities are used as given
+ * (no renormalisation).  lse is streamed tile by tile as in pe_lm_head_loss;
+ * the k target logits are computed in fp32 from the unrounded normalised
+ * row.  x [n, hidden] f32 and final_gain 16-byte aligned; k >= 1 and
+ * n * k < 2^31; kl [n] f32 required, lse [n] f32 may be NULL; otherwise
+ * PE_ERR_INVALID_ARG.
+ * Results do not depend on timing (fixed-order sums).  Workspace:
+ * pe_lm_head_kl_workspace (256-byte aligned).
+ */
+pe_status pe_lm_head_kl(const pe_drafter_dims* dims, const pe_drafter_weights* weights,
+                        int32_t n, const float* x, int32_t k, const int32_t* target_ids,
+                        const float* target_probs, float* lse, float* kl, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+pe_status pe_lm_head_kl_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

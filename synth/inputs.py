@@ -354,3 +354,18 @@ def cod_config(cfg: int, draw_qkv: bool = True) -> dict:
         # keep 1.0 and an all-ones loss mask: U[0,1) < 1.0 always holds.
         return cod_case(8192, 8, 1.0, 1.0, 4, draw_qkv=draw_qkv)
     raise ValueError(cfg)
+
+
+def kl_targets(n: int, vocab: int, k: int, seed: int, tag: int = 51) -> tuple:
+    """A stand-in for a verifier's top-k distribution per row: k distinct
+    token ids drawn uniformly from the vocabulary and probabilities
+    proportional to exp(2 N(0,1)), summing to 1 (float32).  Returns
+    (ids [n, k] int32, probs [n, k] float32)."""
+    g = rng(seed, tag)
+    ids = np.empty((n, k), np.int32)
+    for i in range(n):
+        ids[i] = g.choice(vocab, k, replace=False)
+    a = g.standard_normal((n, k)) * 2.0
+    p = np.exp(a - a.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return ids, p.astype(np.float32)
