@@ -117,30 +117,81 @@ pe_status check_attn(const pe_attn_args* a) {
   return PE_OK;
 }
 
-size_t attn_ws_bytes(int num_q, int Hq, int Hkv, int Dh, int n_splits) {
-  if (n_splits <= 1) return 16;
-  const size_t nqh = (size_t)num_q * Hq;
-  return up256(nqh * n_splits * Dh * 4) + up256(nqh * n_splits * 8) + up256((size_t)num_q * Hkv * n_splits * 16);
+// Launches of one to four rounds of workgroups (PE_ATTN_NOSPLIT_GROUPS up to
+// PE_ATTN_PLAN_GROUPS) run from a device-built work plan: the query tiles in
+// decreasing order of work, so that the longest start first and the tail is
+// short (a launch of one round otherwise ends with its longest tile).  Below
+// PE_ATTN_PLAN_SPLIT_GROUPS the plan also cuts the longer tiles into up to
+// three equal pieces of at most 3/8 of the longest possible prefix, merged
+// by the combine pass.  Explicit split lengths and windowed launches keep the
+// fixed grid.
+#ifndef PE_ATTN_PLAN_GROUPS
+#define PE_ATTN_PLAN_GROUPS 1024
+#endif
+#ifndef PE_ATTN_PLAN_SPLIT_GROUPS
+#define PE_ATTN_PLAN_SPLIT_GROUPS 1024
+#endif
+#ifndef PE_ATTN_PLAN_NMAX
+#define PE_ATTN_PLAN_NMAX 3
+#endif
+#ifndef PE_ATTN_PLAN_NUM  // piece length: at most NUM/DEN of the longest possible prefix
+#define PE_ATTN_PLAN_NUM 3
+#endif
+#ifndef PE_ATTN_PLAN_DEN
+#define PE_ATTN_PLAN_DEN 8
+#endif
+struct AttnSplit {
+  int n_splits = 1, split_len = 64;  // fixed grid
+  int plan = 0, plan_nmax = 1, plan_tiles = 1, ntiles = 0;
+};
+
+AttnSplit attn_split(int ntiles, int Hkv, int max_prefix, int split_req, bool window) {
+  AttnSplit a;
+  a.ntiles = ntiles;
+  const int mp = max_prefix > 1 ? max_prefix : 1;
+  const int base = ntiles * Hkv > 1 ? ntiles * Hkv : 1;
+  if (window) {  // the window kernel walks two tile ranges of one unsplit prefix
+    a.split_len = up64(mp);
+    return a;
+  }
+  choose_split(base, max_prefix, split_req, &a.n_splits, &a.split_len);
+  if (split_req > 0 || base < PE_ATTN_NOSPLIT_GROUPS || base >= PE_ATTN_PLAN_GROUPS || ntiles > kPlanMaxTiles)
+    return a;
+  a.plan = 1;
+  if (base < PE_ATTN_PLAN_SPLIT_GROUPS) {
+    const int max_tiles = (mp + 63) / 64;
+    a.plan_nmax = PE_ATTN_PLAN_NMAX;
+    a.plan_tiles = (PE_ATTN_PLAN_NUM * max_tiles + PE_ATTN_PLAN_DEN - 1) / PE_ATTN_PLAN_DEN;
+    if (a.plan_tiles < 1) a.plan_tiles = 1;
+  }
+  return a;
 }
 
-void attn_split_for(const pe_attn_args* a, int* n_splits, int* split_len) {
+size_t attn_ws_bytes(int num_q, int Hq, int Hkv, int Dh, const AttnSplit& sp) {
+  size_t b = 0;
+  const int ns = sp.plan ? sp.plan_nmax : sp.n_splits;
+  if (ns > 1) {
+    const size_t nqh = (size_t)num_q * Hq;
+    b += up256(nqh * ns * Dh * 4) + up256(nqh * ns * 8) + up256((size_t)num_q * Hkv * ns * 16);
+  }
+  if (sp.plan) b += up256((size_t)sp.ntiles * sp.plan_nmax * 8) + up256((size_t)sp.ntiles * 4) + 256;
+  return b > 16 ? b : 16;
+}
+
+AttnSplit attn_split_for(const pe_attn_args* a) {
   const int G = a->n_q_heads / a->n_kv_heads;
   const int QPW = attn_queries_per_workgroup(G, a->head_dim);
   const int tps = (a->q_per_seg + QPW - 1) / QPW;
-  int base = a->num_seg * tps * a->n_kv_heads;
-  if (base < 1) base = 1;
-  choose_split(base, a->max_prefix, a->split_len, n_splits, split_len);
-  if (a->window_len > 0) {  // the window kernel walks two tile ranges of one unsplit prefix
-    *n_splits = 1;
-    *split_len = up64(a->max_prefix > 1 ? a->max_prefix : 1);
-  }
+  return attn_split(a->num_seg * tps, a->n_kv_heads, a->max_prefix, a->split_len, a->window_len > 0);
 }
 
 pe_status run_attention(const pe_attn_args* a, void* ws, size_t ws_bytes, int meta_by_row, hipStream_t s) {
-  int n_splits, split_len;
-  attn_split_for(a, &n_splits, &split_len);
-  const size_t need = attn_ws_bytes(a->num_q, a->n_q_heads, a->n_kv_heads, a->head_dim, n_splits);
-  if (n_splits > 1 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255))) return PE_ERR_INVALID_ARG;
+  const AttnSplit sp = attn_split_for(a);
+  const int n_splits = sp.n_splits, split_len = sp.split_len;
+  const int ns = sp.plan ? sp.plan_nmax : n_splits;
+  const size_t need = attn_ws_bytes(a->num_q, a->n_q_heads, a->n_kv_heads, a->head_dim, sp);
+  if ((ns > 1 || sp.plan) && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255)))
+    return PE_ERR_INVALID_ARG;
   AttnParams p{};
   p.q = a->q;
   p.q_stride = a->q_row_stride;
@@ -170,12 +221,19 @@ pe_status run_attention(const pe_attn_args* a, void* ws, size_t ws_bytes, int me
   p.lse = a->lse;
   p.dbg_count = a->dbg_count;
   p.dbg_hash = a->dbg_hash;
-  if (n_splits > 1) {
-    Carver c(ws);
+  Carver c(ws);
+  if (ns > 1) {
     const size_t nqh = (size_t)a->num_q * a->n_q_heads;
-    p.part_o = static_cast<float*>(c.take(nqh * n_splits * a->head_dim * 4));
-    p.part_ml = static_cast<float*>(c.take(nqh * n_splits * 8));
-    p.part_dbg = static_cast<uint64_t*>(c.take((size_t)a->num_q * a->n_kv_heads * n_splits * 16));
+    p.part_o = static_cast<float*>(c.take(nqh * ns * a->head_dim * 4));
+    p.part_ml = static_cast<float*>(c.take(nqh * ns * 8));
+    p.part_dbg = static_cast<uint64_t*>(c.take((size_t)a->num_q * a->n_kv_heads * ns * 16));
+  }
+  if (sp.plan) {
+    p.plan_items = static_cast<int2*>(c.take((size_t)sp.ntiles * sp.plan_nmax * 8));
+    p.plan_pieces = static_cast<int*>(c.take((size_t)sp.ntiles * 4));
+    p.plan_count = static_cast<int*>(c.take(256));
+    p.plan_nmax = sp.plan_nmax;
+    p.plan_tiles = sp.plan_tiles;
   }
   if (a->num_q == 0) return PE_OK;
   launch_attention(p, a->dtype == PE_BF16, a->head_dim, s);
@@ -219,9 +277,8 @@ LayerWs layer_ws(const pe_drafter_dims* d, int T, int R, int K, int max_pos, voi
   w.zero = static_cast<int*>(c.take((size_t)w.nzero * 4));
   const int G = d->n_q_heads / d->n_kv_heads;
   const int QPW = attn_queries_per_workgroup(G, d->head_dim);
-  int n_splits, split_len;
-  choose_split(R * ((K + QPW - 1) / QPW) * d->n_kv_heads, max_pos, 0, &n_splits, &split_len);
-  w.attn_bytes = attn_ws_bytes(RK, d->n_q_heads, d->n_kv_heads, d->head_dim, n_splits);
+  const AttnSplit sp = attn_split(R * ((K + QPW - 1) / QPW), d->n_kv_heads, max_pos, 0, false);
+  w.attn_bytes = attn_ws_bytes(RK, d->n_q_heads, d->n_kv_heads, d->head_dim, sp);
   w.attn = c.take(w.attn_bytes);
   int nmax = d->hidden > (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim ? d->hidden
                                                                          : (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
@@ -479,9 +536,7 @@ pe_status pe_draft_attention_workspace(const pe_attn_args* args, size_t* bytes) 
   pe_status st = check_attn(args);
   if (st != PE_OK) return st;
   if (!bytes) return PE_ERR_INVALID_ARG;
-  int n_splits, split_len;
-  attn_split_for(args, &n_splits, &split_len);
-  *bytes = attn_ws_bytes(args->num_q, args->n_q_heads, args->n_kv_heads, args->head_dim, n_splits);
+  *bytes = attn_ws_bytes(args->num_q, args->n_q_heads, args->n_kv_heads, args->head_dim, attn_split_for(args));
   return PE_OK;
 }
 

@@ -123,9 +123,19 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   int bid = blockIdx.x;
   const int kvh = bid % Hkv;
   bid /= Hkv;
-  const int sp = bid % p.n_splits;
-  bid /= p.n_splits;
-  const int lin = p.num_seg * tps - 1 - bid;  // later (longer) tiles first
+  int sp, lin, ncut;
+  if (p.plan_items) {  // the planned item: (tile, piece) in decreasing order of work
+    if (bid >= *p.plan_count) return;
+    const int2 it = p.plan_items[bid];
+    lin = it.x;
+    sp = it.y;
+    ncut = p.plan_pieces[lin];
+  } else {
+    sp = bid % p.n_splits;
+    bid /= p.n_splits;
+    lin = p.num_seg * tps - 1 - bid;  // later (longer) tiles first
+    ncut = p.n_splits;
+  }
   const int seg = lin / tps, tile = lin % tps;
   const int qbase = seg * p.q_per_seg + tile * QPW;
   const int nq = min(QPW, p.q_per_seg - tile * QPW);
@@ -190,9 +200,17 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   const int n_anc = (sp == 0) ? n_anc_all : 0;
   const int seg_base = p.seg_kv_base[seg];
 
-  // ---- this split's prefix range [kbeg, kend]
-  const int kbeg = sp * p.split_len;
-  const int kend = (sp == p.n_splits - 1) ? max_start : min(max_start, kbeg + p.split_len - 1);
+  // ---- this split's prefix range [kbeg, kend]: piece sp of ncut equal
+  // pieces of the tile's own range (plan), or of split_len keys
+  int kbeg, kend;
+  if (p.plan_items) {
+    const int np_all = max_start >= 0 ? (max_start + KT) / KT : 0;
+    kbeg = (int)((int64_t)sp * np_all / ncut) * KT;
+    kend = (sp == ncut - 1) ? max_start : (int)((int64_t)(sp + 1) * np_all / ncut) * KT - 1;
+  } else {
+    kbeg = sp * p.split_len;
+    kend = (sp == ncut - 1) ? max_start : min(max_start, kbeg + p.split_len - 1);
+  }
   int n_pref = (kend >= kbeg) ? (kend - kbeg + KT) / KT : 0;
   // StreamingLLM window (never split): the sink tiles, then the tiles from the
   // earliest window start of this workgroup's queries to its last prefix key
@@ -635,7 +653,7 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
     if (!cact[cb]) continue;
     const int qo = qbase + cq[cb];
     const int h = hh[cb];
-    if (p.n_splits == 1) {
+    if (ncut == 1) {
       const float inv = l_col > 0.f ? 1.0f / l_col : 0.f;
       S* o = reinterpret_cast<S*>(p.out) + ((int64_t)qo * Hq + h) * DH;
 #pragma unroll
@@ -664,7 +682,7 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
     }
     if constexpr (DBG) {
       if (h % G == 0 && g == 0) {
-        if (p.n_splits == 1) {
+        if (ncut == 1) {
           p.dbg_count[(int64_t)qo * Hkv + kvh] = dcnt[cb];
           p.dbg_hash[(int64_t)qo * Hkv + kvh] = dhsh[cb];
         } else {
@@ -679,14 +697,21 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
 
 // Merge of split partials, one wave per (query, head), lane s = split s:
 // O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^((m_s - M) * scale * log2 e), M = max_s m_s.
+// With a plan, query q merges the plan_pieces of its tile (one piece: the
+// attention kernel wrote q's output itself, nothing to do).
 template <typename S, int DH>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, int QPW, int tps) {
   const int lane = threadIdx.x & 63;
   const int64_t qh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nqh = (int64_t)p.num_q * p.Hq;
-  const int ns = p.n_splits;  // <= 64
   const float sl2 = p.scale_log2;
-  if (qh < nqh) {
+  auto pieces_of = [&](int64_t q) -> int {  // <= 64
+    if (!p.plan_items) return p.n_splits;
+    const int seg = (int)(q / p.q_per_seg), tile = (int)(q % p.q_per_seg) / QPW;
+    return p.plan_pieces[seg * tps + tile];
+  };
+  const int ns = qh < nqh ? pieces_of(qh / p.Hq) : 1;
+  if (qh < nqh && ns > 1) {
     float m = -INFINITY, l = 0.f;
     if (lane < ns) {
       m = p.part_ml[((int64_t)lane * nqh + qh) * 2];
@@ -714,9 +739,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   if (p.dbg_count) {
     const int64_t nqk = (int64_t)p.num_q * p.Hkv;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx < nqk) {
+    const int nsd = idx < nqk ? pieces_of(idx / p.Hkv) : 1;
+    if (idx < nqk && nsd > 1) {
       uint64_t c = 0, h = 0;
-      for (int s = 0; s < ns; ++s) {
+      for (int s = 0; s < nsd; ++s) {
         c += p.part_dbg[((int64_t)s * nqk + idx) * 2];
         h += p.part_dbg[((int64_t)s * nqk + idx) * 2 + 1];
       }
@@ -726,12 +752,96 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   }
 }
 
+// Work plan of one launch (one workgroup of 1,024 threads; at most
+// kPlanMaxTiles query tiles).  A query tile's work is estimated as its prefix
+// tiles (up to its largest start) plus its chain tiles; the per-query reads
+// are spread over all threads (a thread per tile would wait on each of its
+// queries in turn).  The tile is cut into pieces (see AttnParams) and the
+// items are bucket-sorted by decreasing work (largest first: the longest
+// items start in the first round and the short ones fill the tail).  The
+// order within a bucket may vary from run to run; results do not depend on
+// it (every piece and every merge is computed in a fixed order).
+__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnParams p, int QPW, int tps) {
+  constexpr int NB = 2048;  // work buckets (in key tiles; larger items share the last)
+  __shared__ int hist[NB];
+  __shared__ int tmax[kPlanMaxTiles], tchain[kPlanMaxTiles];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntiles = p.num_seg * tps;
+  for (int b = tid; b < NB; b += 1024) hist[b] = 0;
+  for (int t = tid; t < ntiles; t += 1024) {
+    tmax[t] = -1;
+    tchain[t] = 0;
+  }
+  __syncthreads();
+  constexpr int UQ = 4;  // queries whose metadata loads are in flight together
+  for (int q0 = tid; q0 < p.num_q; q0 += 1024 * UQ) {
+    int st[UQ], dp[UQ];
+#pragma unroll
+    for (int u = 0; u < UQ; ++u) {
+      const int q = q0 + 1024 * u;
+      const int mi = q < p.num_q ? ((p.meta_by_row && p.q_rows) ? p.q_rows[q] : q) : -1;
+      st[u] = mi >= 0 ? p.q_start[mi] : -1;
+      dp[u] = (mi >= 0 && p.q_depth) ? min(max(p.q_depth[mi], 0), p.max_depth) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < UQ; ++u) {
+      const int q = q0 + 1024 * u;
+      if (q < p.num_q) {
+        const int lin = (q / p.q_per_seg) * tps + (q % p.q_per_seg) / QPW;
+        atomicMax(&tmax[lin], st[u]);
+        if (dp[u]) atomicAdd(&tchain[lin], dp[u]);
+      }
+    }
+  }
+  __syncthreads();
+  auto pieces = [&](int npref) {
+    return p.plan_nmax > 1 ? min(p.plan_nmax, max(1, (npref + p.plan_tiles - 1) / p.plan_tiles)) : 1;
+  };
+  auto bucket = [&](int npref, int nanc, int c, int sp) {
+    const int w = (int)((int64_t)(sp + 1) * npref / c - (int64_t)sp * npref / c) + (sp == 0 ? nanc : 0);
+    return min(w, NB - 1);
+  };
+  for (int lin = tid; lin < ntiles; lin += 1024) {
+    const int np = tmax[lin] >= 0 ? (tmax[lin] + KT) / KT : 0, na = (tchain[lin] + KT - 1) / KT;
+    const int c = pieces(np);
+    p.plan_pieces[lin] = c;
+    for (int sp = 0; sp < c; ++sp) atomicAdd(&hist[bucket(np, na, c, sp)], 1);
+  }
+  __syncthreads();
+  // exclusive scan over the buckets in decreasing order of work: thread t
+  // takes positions 2t, 2t + 1 (buckets NB-1-2t, NB-2-2t)
+  const int b0 = NB - 1 - 2 * tid, b1 = b0 - 1;
+  const int h0 = hist[b0], h1 = hist[b1];
+  const int v = h0 + h1;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int wofs = 0;
+  for (int w = 0; w < wave; ++w) wofs += wsum[w];
+  hist[b0] = wofs + incl - v;
+  hist[b1] = wofs + incl - v + h0;
+  if (tid == 1023) *p.plan_count = wofs + incl;
+  __syncthreads();
+  for (int lin = tid; lin < ntiles; lin += 1024) {
+    const int np = tmax[lin] >= 0 ? (tmax[lin] + KT) / KT : 0, na = (tchain[lin] + KT - 1) / KT;
+    const int c = pieces(np);
+    for (int sp = 0; sp < c; ++sp) p.plan_items[atomicAdd(&hist[bucket(np, na, c, sp)], 1)] = make_int2(lin, sp);
+  }
+}
+
 template <typename S, int DH>
 static void launch_attn_t(const AttnParams& p, hipStream_t s) {
   const int G = p.Hq / p.Hkv;
   const int QPW = attn_queries_per_workgroup(G, DH);
   const int tps = (p.q_per_seg + QPW - 1) / QPW;
-  const int grid = p.num_seg * tps * p.n_splits * p.Hkv;
+  const int ncut = p.plan_items ? p.plan_nmax : p.n_splits;
+  const int grid = p.num_seg * tps * ncut * p.Hkv;
+  if (p.plan_items) hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, p, QPW, tps);
   if (p.win_len > 0) {
     if (p.dbg_count) hipLaunchKernelGGL((attn_kernel<S, DH, true, true>), dim3(grid), dim3(256), 0, s, p, G, tps);
     else hipLaunchKernelGGL((attn_kernel<S, DH, false, true>), dim3(grid), dim3(256), 0, s, p, G, tps);
@@ -739,12 +849,12 @@ static void launch_attn_t(const AttnParams& p, hipStream_t s) {
     if (p.dbg_count) hipLaunchKernelGGL((attn_kernel<S, DH, true, false>), dim3(grid), dim3(256), 0, s, p, G, tps);
     else hipLaunchKernelGGL((attn_kernel<S, DH, false, false>), dim3(grid), dim3(256), 0, s, p, G, tps);
   }
-  if (p.n_splits > 1) {
+  if (ncut > 1) {
     const int64_t nqh = (int64_t)p.num_q * p.Hq;
     const int64_t nqk = (int64_t)p.num_q * p.Hkv;
     int64_t blocks = (nqh + 3) / 4;
     if (p.dbg_count && (nqk + 255) / 256 > blocks) blocks = (nqk + 255) / 256;
-    hipLaunchKernelGGL((attn_combine_kernel<S, DH>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_combine_kernel<S, DH>), dim3((unsigned)blocks), dim3(256), 0, s, p, QPW, tps);
   }
 }
 

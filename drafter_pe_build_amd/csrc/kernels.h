@@ -215,8 +215,20 @@ struct AttnParams {
   float* part_ml;      // [n_splits, num_q*Hq, 2]
   uint64_t* part_dbg;  // [n_splits, num_q*Hkv, 2]
   int win_sink, win_len;  // StreamingLLM window over the prefix keys (win_len 0: none; never split)
+  // Work plan (null plan_items: every query tile is cut into n_splits pieces
+  // of split_len keys, in the fixed grid order).  With a plan, attn_plan_kernel
+  // cuts each tile's prefix into plan_pieces[tile] <= plan_nmax equal pieces
+  // (one when plan_nmax is 1, else as many as pieces of at most plan_tiles key
+  // tiles need) and lists the (tile, piece) items by decreasing work; workgroup
+  // b takes item b / Hkv.  Partials use slot = piece.
+  int2* plan_items;   // [tiles * plan_nmax]
+  int* plan_count;    // number of items
+  int* plan_pieces;   // [tiles]
+  int plan_nmax, plan_tiles;
 };
 void launch_attention(const AttnParams& p, int bf16, int head_dim, hipStream_t s);
+// Query tiles of one planned launch at most.
+constexpr int kPlanMaxTiles = 2048;
 
 // Backward of the COD attention over the depth-major training layout (bf16
 // operands, f32 gradients): dq of the queries [q_begin, q_end), their dk and

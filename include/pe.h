@@ -256,7 +256,13 @@ typedef struct {
     const int32_t* kv_parent;    /* [num_kv_rows] or NULL when q_depth is NULL */
     int32_t max_prefix;     /* host bound on 1 + max q_start (work split only;
                                a smaller true bound only costs balance)        */
-    int32_t split_len;      /* keys per split (multiple of 64) or 0 = auto     */
+    int32_t split_len;      /* keys per split (multiple of 64) or 0 = auto:
+                               launches below 512 workgroups cut every
+                               query tile's prefix into pieces; from 512 to
+                               2,047 a work plan built on the device runs the
+                               tiles longest first and, below 1,024, cuts
+                               the longer ones into up to three equal pieces
+                               (workspace needed in both cases)              */
     void* out;              /* [num_q, Hq, Dh]                                 */
     float* lse;             /* [num_q, Hq] natural-log sum-exp of scaled
                                scores, or NULL                                 */
