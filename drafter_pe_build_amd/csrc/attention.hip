@@ -752,6 +752,85 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, int QPW
   }
 }
 
+// The same merge for launches of a few pieces per query (a plan's at most
+// three): DH / 4 threads per (query, head), four dimensions (one 16-byte
+// partial load per piece) each,
+// O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^((m_s - M) * scale * log2 e), M = max_s m_s,
+// summed over the pieces in order.  With a plan, query q merges the
+// plan_pieces of its tile (one piece: the attention kernel wrote q's output
+// itself, nothing to do).
+template <typename S, int DH>
+__global__ __launch_bounds__(256) void attn_combine_few_kernel(AttnParams p, int QPW, int tps) {
+  constexpr int TPQ = DH / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t qh = gid / TPQ;
+  const int d4 = (int)(gid % TPQ) * 4;
+  const int64_t nqh = (int64_t)p.num_q * p.Hq;
+  const float sl2 = p.scale_log2;
+  auto pieces_of = [&](int64_t q) -> int {
+    if (!p.plan_items) return p.n_splits;
+    const int seg = (int)(q / p.q_per_seg), tile = (int)(q % p.q_per_seg) / QPW;
+    return p.plan_pieces[seg * tps + tile];
+  };
+  const int ns = qh < nqh ? pieces_of(qh / p.Hq) : 1;
+  if (qh < nqh && ns > 1) {
+    // loads in batches of U pieces (independent, in flight together); the
+    // sums still run over the pieces in order
+    constexpr int U = 8;
+    const float* ml = p.part_ml + qh * 2;
+    const int64_t sml = nqh * 2, spo = nqh * DH;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += U) {
+      float t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) t[u] = s0 + u < ns ? ml[(int64_t)(s0 + u) * sml] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) M = fmaxf(M, t[u]);
+    }
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    const float* po = p.part_o + qh * DH + d4;
+    for (int s0 = 0; s0 < ns; s0 += U) {
+      float2 t[U];
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sc = min(s0 + u, ns - 1);  // clamped; pieces past ns get weight 0
+        t[u] = *reinterpret_cast<const float2*>(ml + (int64_t)sc * sml);
+        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)sc * spo);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = (s0 + u >= ns || t[u].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((t[u].x - M) * sl2);
+        L += w * t[u].y;
+        o += w * v[u];
+      }
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    S* out = reinterpret_cast<S*>(p.out) + qh * DH + d4;
+    if constexpr (sizeof(S) == 2) {
+      *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+    } else {
+      *reinterpret_cast<f32x4*>(out) = o * inv;
+    }
+    if (d4 == 0 && p.lse) p.lse[qh] = L > 0.f ? M * p.scale + logf(L) : -INFINITY;
+  }
+  if (p.dbg_count) {
+    const int64_t nqk = (int64_t)p.num_q * p.Hkv;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nsd = idx < nqk ? pieces_of(idx / p.Hkv) : 1;
+    if (idx < nqk && nsd > 1) {
+      uint64_t c = 0, h = 0;
+      for (int s = 0; s < nsd; ++s) {
+        c += p.part_dbg[((int64_t)s * nqk + idx) * 2];
+        h += p.part_dbg[((int64_t)s * nqk + idx) * 2 + 1];
+      }
+      p.dbg_count[idx] = (int64_t)c;
+      p.dbg_hash[idx] = h;
+    }
+  }
+}
+
 // Work plan of one launch (one workgroup of 1,024 threads; at most
 // kPlanMaxTiles query tiles).  A query tile's work is estimated as its prefix
 // tiles (up to its largest start) plus its chain tiles; the per-query reads
@@ -852,9 +931,15 @@ static void launch_attn_t(const AttnParams& p, hipStream_t s) {
   if (ncut > 1) {
     const int64_t nqh = (int64_t)p.num_q * p.Hq;
     const int64_t nqk = (int64_t)p.num_q * p.Hkv;
-    int64_t blocks = (nqh + 3) / 4;
-    if (p.dbg_count && (nqk + 255) / 256 > blocks) blocks = (nqk + 255) / 256;
-    hipLaunchKernelGGL((attn_combine_kernel<S, DH>), dim3((unsigned)blocks), dim3(256), 0, s, p, QPW, tps);
+    if (ncut <= 8) {
+      int64_t blocks = (nqh * (DH / 4) + 255) / 256;
+      if (p.dbg_count && (nqk + 255) / 256 > blocks) blocks = (nqk + 255) / 256;
+      hipLaunchKernelGGL((attn_combine_few_kernel<S, DH>), dim3((unsigned)blocks), dim3(256), 0, s, p, QPW, tps);
+    } else {
+      int64_t blocks = (nqh + 3) / 4;
+      if (p.dbg_count && (nqk + 255) / 256 > blocks) blocks = (nqk + 255) / 256;
+      hipLaunchKernelGGL((attn_combine_kernel<S, DH>), dim3((unsigned)blocks), dim3(256), 0, s, p, QPW, tps);
+    }
   }
 }
 
