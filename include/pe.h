@@ -15,6 +15,19 @@
  *                         training-shaped COD layout)
  *   pe_lm_head_argmax     final RMSNorm, LM head and greedy argmax
  *
+ * Interface choices
+ * -----------------
+ * Beyond one call per stage with plain tensors: every linear weight is
+ * passed pre-packed (pe_pack_weight, once per weight), because the packed
+ * 1 KB chunks make each weight load one contiguous matrix-core operand;
+ * pe_lm_head_argmax takes the weights struct (final_gain, w_lm) so that all
+ * stages share one weights handle; h_shared is an argument of
+ * pe_build_draft_batch, the only stage that reads it, not a weights member;
+ * pe_attn_args carries host bounds (max_prefix, max_depth) that the work
+ * split and the chain-depth check need before launch.  The two LM-head
+ * losses, the attention backward and the allocation-free LM head are
+ * additional entry points.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers.  Every tensor pointer is a DEVICE pointer; structs passed by
