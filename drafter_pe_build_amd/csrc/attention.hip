@@ -275,9 +275,16 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   // m_run: running maximum (raw score units); thr = m_run + thr_gap; mb =
   // m_run * scale * log2 e (0 while no score has been seen, m_run = -inf)
   // l_run: this lane's share of the row sum (its keys); the column's l is
-  // the sum over the column's four lanes
-  float m_run[CBLK], thr[CBLK], mb[CBLK], l_run[CBLK];
+  // the sum over the column's four lanes.  bf16 at head_dim 128 (LMMA): the
+  // row sum is one more matrix product per column block, a row of ones times
+  // P^T (acc_l, row 0 of a 16-row block: element 0 on the lanes with g = 0,
+  // zero elsewhere), so it is rescaled with O and costs no vector adds (the
+  // training shapes are bound by the softmax's vector work: 316 against 324
+  // us at N=4096; the decode shapes at head_dim 64 keep the adds).
+  constexpr bool LMMA = BF && DH == 128;
+  float m_run[CBLK], thr[CBLK], mb[CBLK], l_run[LMMA ? 1 : CBLK];
   f32x4 acc[CBLK][NMB];
+  f32x4 acc_l[LMMA ? CBLK : 1];
   int64_t dcnt[CBLK];
   uint64_t dhsh[CBLK];
 #pragma unroll
@@ -285,7 +292,8 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
     m_run[cb] = -INFINITY;
     thr[cb] = -INFINITY;
     mb[cb] = 0.f;
-    l_run[cb] = 0.f;
+    if constexpr (LMMA) acc_l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    else l_run[cb] = 0.f;
     dcnt[cb] = 0;
     dhsh[cb] = 0;
 #pragma unroll
@@ -520,7 +528,8 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   auto rescale = [&]() {
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) {
-      l_run[cb] *= alpha[cb];
+      if constexpr (LMMA) acc_l[cb] *= alpha[cb];
+      else l_run[cb] *= alpha[cb];
 #pragma unroll
       for (int i = 0; i < NMB; ++i) acc[cb][i] *= alpha[cb];
     }
@@ -534,7 +543,7 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[cb][i >> 2][i & 3], sl2, -mb[cb]));
-      lp[cb] = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+      if constexpr (!LMMA) lp[cb] = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
       if constexpr (BF) {
         bop[cb][0] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                            pack_bf16x2(pv[6], pv[7])};
@@ -549,8 +558,16 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   // O^T += V^T P^T and l += sum P; each V^T operand read once, used for
   // every column block
   auto pv_half = [&](const char* Vb, int h, const HalfP& bop, const float (&lp)[CBLK]) {
+    if constexpr (LMMA) {
+      // l += (row of ones) P^T: the ones sit in operand row 0 (lanes 0, 16, 32, 48)
+      const uint32_t one2 = (r == 0) ? 0x3F803F80u : 0u;  // two bf16 1.0
+      const u32x4 ones = {one2, one2, one2, one2};
 #pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb) l_run[cb] += lp[cb];
+      for (int cb = 0; cb < CBLK; ++cb) mma16(acc_l[cb], ones, bop[cb][0], S());
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) l_run[cb] += lp[cb];
+    }
 #pragma unroll
     for (int mbk = 0; mbk < NMB; ++mbk) {
       if constexpr (BF) {
@@ -643,7 +660,9 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   // ---- epilogue
 #pragma unroll
   for (int cb = 0; cb < CBLK; ++cb) {
-    const float l_col = colgroup_sum(l_run[cb]);
+    float l_col;
+    if constexpr (LMMA) l_col = colgroup_sum(acc_l[cb][0]);  // rows 4g: l on g = 0, zeros elsewhere
+    else l_col = colgroup_sum(l_run[cb]);
     if constexpr (DBG) {
       for (int o = 16; o < 64; o <<= 1) {
         dcnt[cb] += __shfl_xor(dcnt[cb], o, 64);
