@@ -41,6 +41,7 @@
 // same grouping of chain tiles, i.e. chunks that start at multiples of the
 // workgroup's query count).
 #include <math.h>
+#include <type_traits>
 #include "kernels.h"
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       doff[q] = (uint32_t)key * (uint32_t)rstride + (uint32_t)(ch * CH);
     }
   }
-  auto dma_tile = [&](int it, int buf) {
+  auto dma_tile = [&](int it, int buf) __attribute__((always_inline)) {
     if constexpr (BF) {
       if (it < n_pref) {
         const int p0 = pkey(it);
@@ -455,8 +456,9 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   // is over.  Returns whether any m moved; alpha then holds the factors
   // (1 on columns that keep m) for O and l, applied by rescale().
   float alpha[CBLK];
-  auto check_half = [&](int h, bool anc, bool full, int k0, HalfS& sacc) -> bool {
-    if (anc) {
+  auto check_half = [&](int h, auto anc_c, bool full, int k0, HalfS& sacc) -> bool {
+    constexpr bool anc = decltype(anc_c)::value;
+    if constexpr (anc) {
       int own[8];
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
@@ -619,7 +621,11 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       store_tile(0);
     }
   }
-  for (int it = 0; it < n_iter; ++it) {
+  // One tile; the prefix tiles and the chain tiles run in loops of their
+  // own, so that each body has one masking path besides the unmasked one
+  // (with both in one body the compiler copied every score at the join).
+  auto tile_step = [&](int it, auto anc_c) {
+    constexpr bool anc = decltype(anc_c)::value;
     const int buf = it & 1;
     if constexpr (BF) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of tile it
     __syncthreads();
@@ -629,7 +635,6 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       load_tile(min(it + 1, n_iter - 1));
     }
 
-    const bool anc = it >= n_pref;
     const int k0 = anc ? (it - n_pref) * KT : pkey(it);
     // window: a tile no column sees is past the sink and before every window
     const bool skip = anc ? (k0 + KT <= wa0 || k0 >= wa1)
@@ -643,11 +648,11 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       HalfP p0, p1;
       float l0[CBLK], l1[CBLK];
       s_half(Kb, 0, s0);
-      if (check_half(0, anc, full, k0, s0)) rescale();
+      if (check_half(0, anc_c, full, k0, s0)) rescale();
       s_half(Kb, 1, s1);
       exp_half(s0, p0, l0);
       pin(p0);  // keeps exp0 beside S1 (the compiler would sink it to PV0)
-      const bool moved1 = check_half(1, anc, full, k0, s1);
+      const bool moved1 = check_half(1, anc_c, full, k0, s1);
       pv_half(Vb, 0, p0, l0);
       exp_half(s1, p1, l1);
       pin(p1);  // keeps exp1 beside PV0
@@ -655,7 +660,10 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       pv_half(Vb, 1, p1, l1);
     }
     if constexpr (!BF) store_tile(buf ^ 1);
-  }
+  };
+  const int n_pit = min(n_pref, n_iter);
+  for (int it = 0; it < n_pit; ++it) tile_step(it, std::false_type{});
+  for (int it = n_pit; it < n_iter; ++it) tile_step(it, std::true_type{});
 
   // ---- epilogue
 #pragma unroll
