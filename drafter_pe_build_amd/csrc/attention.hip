@@ -99,11 +99,18 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   constexpr int NST = DH / STEP;
   constexpr int NMB = DH / 16;
   constexpr int DC = DH / CH;                    // 16-byte chunks per head row
-  constexpr int KPB = DH * (int)sizeof(S) + 16;  // K row pitch, bytes
+  // bf16 at head_dim 128 (SWZ): K and V rows of 256 bytes, unpadded, whose
+  // 16-byte chunk c sits at position c ^ swz(row) (swz(row) = 2 (row & 7)):
+  // the 16 rows of a K operand read and the 4 rows x 2 chunks of a
+  // transposed V read fall on distinct chunk positions, and a tile is 32
+  // whole 1 KB copies (8 per wave).  Otherwise padded rows:
+  constexpr bool SWZ = BF && DH == 128;
+  constexpr int KPB = SWZ ? DH * 2 : DH * (int)sizeof(S) + 16;  // K row pitch, bytes
   // bf16: V row-major (pitch DH*2 + 32), read transposed by ds_read_b64_tr_b16;
   // f32: V^T[dh][key] (pitch KT*4 + 16), written transposed
-  constexpr int VPB = BF ? DH * 2 + 32 : KT * 4 + 16;
+  constexpr int VPB = SWZ ? DH * 2 : BF ? DH * 2 + 32 : KT * 4 + 16;
   constexpr int VBYTES = BF ? KT * VPB : DH * VPB;
+  auto swz = [](int row) { return SWZ ? (row & 7) << 1 : 0; };
   constexpr int NCH = (KT * DC + 255) / 256;     // 16-byte chunks of K (and of V) per thread per tile
   constexpr int NB = BF ? 1 : 2;                 // 16-key blocks per P^T operand of one half tile
   static_assert(2 * NCH <= 32, "valid-row bits");
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
     const int ps = isv ? VPS : KPS;
     const int slot = (isv ? j - KPS : j) * 64 + lane;
     key = slot / ps;
-    ch = (slot % ps < DC) ? slot % ps : 0;
+    ch = SWZ ? (slot % ps) ^ swz(key) : (slot % ps < DC) ? slot % ps : 0;
   };
   uint32_t doff[BF ? NDW : 1];  // element offset of copy q within a full prefix tile
   if constexpr (BF) {
@@ -441,7 +448,8 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int t = 0; t < NST; ++t) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(Kb + (16 * (2 * h + bb) + r) * KPB + (4 * t + g) * 16);
+        const int kr = 16 * (2 * h + bb) + r;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(Kb + kr * KPB + (((4 * t + g) ^ swz(kr)) * 16));
 #pragma unroll
         for (int cb = 0; cb < CBLK; ++cb) mma16(sacc[cb][bb], a, qreg[cb][t], S());
       }
@@ -577,7 +585,10 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
         // key 32h + 16s + 4g + c; lane r then receives dim 16 mbk + r of the
         // four keys c = 0..3 (slots 4s + c of the operand).
         typedef __attribute__((address_space(3))) short4_t lds_s4;
-        const char* vp = Vb + (32 * h + 4 * g + (r >> 2)) * VPB + (16 * mbk + 4 * (r & 3)) * 2;
+        // (the row 16 further down has the same swizzle)
+        const int vr = 32 * h + 4 * g + (r >> 2);
+        const int vb = (16 * mbk + 4 * (r & 3)) * 2;  // byte of the row
+        const char* vp = Vb + vr * VPB + ((((vb >> 4) ^ swz(vr)) << 4) | (vb & 15));
         const auto lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp));
         const auto hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vp + 16 * VPB));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
