@@ -162,6 +162,24 @@ def test_attention_validation_and_workspace():
     a4 = L.attn_args(**{**base, "window_sink": 256, "window_len": 2048})
     assert lib.pe_draft_attention_workspace(ctypes.byref(a4), ctypes.byref(n)) == 0
     assert n.value == 16
+    # launch sizes and their work split: 2,048 queries of G = 4 at head_dim 128 are
+    # 64 tiles x 8 kv heads = 512 workgroups (a planned launch with cut tiles: plan
+    # arrays and partials), 4,096 queries 1,024 (the fixed grid, no workspace), and
+    # an explicit split length keeps the fixed split
+    train = dict(num_seg=1, num_kv_rows=8192, n_q_heads=32, n_kv_heads=8, head_dim=128, scale=0.088,
+                 dtype=L.PE_BF16, q=FAKE, q_row_stride=4096, k=FAKE, v=FAKE, seg_kv_base=FAKE, q_start=FAKE,
+                 out=FAKE, max_prefix=8192)
+    sizes = {}
+    for nq, extra in ((2048, {}), (4096, {}), (2048, {"split_len": 4096})):
+        a6 = L.attn_args(**{**train, "num_q": nq, "q_per_seg": nq, **extra})
+        assert lib.pe_draft_attention_workspace(ctypes.byref(a6), ctypes.byref(n)) == 0
+        sizes[(nq, bool(extra))] = n.value
+        if n.value > 16:  # a launch that needs workspace refuses to run without it
+            assert lib.pe_draft_attention(ctypes.byref(a6), None, 0, None) == 1
+    nqh = 2048 * 32
+    assert sizes[(2048, False)] >= 3 * nqh * (128 + 2) * 4 + 64 * 3 * 8  # three pieces' partials + the plan
+    assert sizes[(4096, False)] == 16
+    assert sizes[(2048, True)] >= 2 * nqh * (128 + 2) * 4             # two fixed 4,096-key splits
 
 
 def test_noalloc_lm_head_refuses_oversized_batches_before_any_device_call():
