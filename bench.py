@@ -50,8 +50,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
-    ap.add_argument("--cpu-configs", default="0,1,2,3,4",
-                    help="configs whose oracle CPU baseline is timed (comma-separated, of 0-4)")
+    ap.add_argument("--cpu-workloads", default="0,1,2,3,4",
+                    help="workloads whose oracle CPU baseline is timed, comma-separated: 0 tiny fp32 decode "
+                         "(N=128, K=4), 1 decode c=1, 2 decode c=64, 3 COD attention N=4096, 4 parallel-group "
+                         "attention N=8192")
     ap.add_argument("--no-extra", action="store_true", help="skip the c=64 decode and attention measurements")
     ap.add_argument("--attention-only", type=int, choices=(3, 4, 5, 6), default=0,
                     help="time only the COD (3), parallel-group (4), random-anchor (5) or windowed "
@@ -170,14 +172,14 @@ WINDOW_SINK, WINDOW_LEN = 256, 2048
 
 def measure_attention(cfg, steps, stream):
     """COD attention N=4096 (one launch) or parallel-group attention N=8192
-    (8 query chunks of 8192; cfg 6: with the StreamingLLM window): time per
-    pass over all queries and rate."""
+    (8 query chunks of 8192; workload 6: with the StreamingLLM window): time
+    per pass over all queries and rate."""
     import numpy as np
     import torch
     from drafter_pe_build_amd import _lib as L
     from drafter_pe_build_amd.step import to_device
     from synth import inputs as si
-    log("attention config %d" % cfg)
+    log(ATTN_NAMES[cfg])
     Lay = si.cod_config(4 if cfg == 6 else cfg)
     sink, window = (WINDOW_SINK, WINDOW_LEN) if cfg == 6 else (0, 0)
     T = Lay["T"]
@@ -439,7 +441,7 @@ def cpu_oracle_decode(dims, W, case):
 
 def cpu_oracle_attention(cfg):
     """The fp64 oracle's COD attention on a seeded, bounded query sample of the
-    N=4096 (cfg 3) or N=8192 x 8 (cfg 4) layout; the time is extrapolated per
+    N=4096 (workload 3) or N=8192 x 8 (workload 4) layout; the time is extrapolated per
     query to the whole layout (input generation and the bf16 -> fp64
     conversion excluded)."""
     import numpy as np
@@ -471,7 +473,7 @@ def cpu_baselines(dims, W, case1, which):
     out = {"cpu_model": cpu_model(), "cores": oracle_threads(), "kind": "oracle",
            "note": "the plain fp64 numpy oracle as written (not tuned); a reported baseline, not a target"}
     for cfg in which:
-        log("oracle CPU baseline, config %d" % cfg)
+        log("oracle CPU baseline, workload %d" % cfg)
         if cfg == 0:
             d0, W0, c0 = si.decode_config(0)
             t = cpu_oracle_decode(d0, W0, c0)
@@ -626,7 +628,7 @@ def main():
         result["secondary"] = extra
 
     if not args.no_cpu:
-        which = sorted({int(c) for c in args.cpu_configs.split(",") if c.strip()} | {1})
+        which = sorted({int(c) for c in args.cpu_workloads.split(",") if c.strip()} | {1})
         cb = cpu_baselines(dims, W, case1, which)
         c1 = cb["decode_c1"]
         result["cpu_baseline"] = {"value": c1["value"], "unit": "draft positions/s", "cores": cb["cores"],

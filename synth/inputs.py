@@ -233,7 +233,10 @@ def decode_case(dims: DrafterDims, seed: int, R: int, K: int, W: Sequence[int],
 
 
 def decode_config(cfg: int, with_weights: bool = True) -> tuple:
-    """(dims, weights, case) for decode configs 0, 1 and 2."""
+    """(dims, weights, case) of the decode workloads: 0 the tiny fp32 step
+    (N=128 window rows, K=4), 1 the single-request step (c=1, K=7, 2,048
+    cached positions), 2 the 64-request step (c=64, K=7, ragged caches of
+    512-4,096 positions)."""
     if cfg == 0:
         dims = TINY_DIMS
         case = decode_case(dims, 0, R=1, K=4, W=[128], kv_len=[0], n_rej=[0],
@@ -348,6 +351,9 @@ def anchor_config(draw_qkv: bool = True) -> dict:
 
 
 def cod_config(cfg: int, draw_qkv: bool = True) -> dict:
+    """Training-shaped attention layouts: 3 the COD layout at N=4096 (5
+    depths, keep 0.7, loss mask rate 0.5), 4 the parallel groups at N=8192
+    (8 depths, keep 1.0, every position a chain start)."""
     if cfg == 3:
         return cod_case(4096, 5, 0.7, 0.5, 3, draw_qkv=draw_qkv)
     if cfg == 4:
