@@ -338,15 +338,22 @@ def measure_loss(dims, steps, stream, W=None):
     wsk = torch.empty(L.pe_lm_head_kl_workspace(cd, n), dtype=torch.uint8, device="cuda")
     kms = time_sustained(lambda: L.pe_lm_head_kl(cd, cw, n, x, k, ids, pr, kl, lse, workspace=wsk), steps, stream)
     log("  top-%d KL: %.1f us" % (k, kms * 1e3))
-    del cw, x, t, lse, loss, ws, ids, pr, kl, wsk
+    # the same with the target rows read from the row-major LM head
+    w_rows = to_device(W["w_lm"], "cuda")
+    rms = time_sustained(lambda: L.pe_lm_head_kl(cd, cw, n, x, k, ids, pr, kl, lse, w_lm_rows=w_rows, workspace=wsk),
+                         steps, stream)
+    log("  top-%d KL, row-major target rows: %.1f us" % (k, rms * 1e3))
+    del cw, x, t, lse, loss, ws, ids, pr, kl, wsk, w_rows
     torch.cuda.empty_cache()
     return {"rows": n, "ms": ms, "rows_per_s": n / (ms * 1e-3), "tflops": fl / (ms * 1e-3) / 1e12,
             "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "logits_bytes_avoided": n * dims.vocab * 4,
             "kl_topk": {"k": k, "ms": kms, "rows_per_s": n / (kms * 1e-3),
                         "tflops": fl / (kms * 1e-3) / 1e12, "mfma_frac": fl / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                        "ms_row_major_targets": rms,
                         "note": "log-sum-exp pass plus one fp32 dot product per target pair (n * k rows of W_lm "
-                                "gathered)"}}
+                                "gathered from the packed weight; ms_row_major_targets reads them from a row-major "
+                                "copy)"}}
 
 
 def measure_decode64(dims, W, steps, stream):

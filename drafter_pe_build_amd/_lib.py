@@ -85,7 +85,7 @@ EXPORTS = {
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "pe_lm_head_loss_workspace": (c_int, [POINTER(PeDims), c_int32, POINTER(c_size_t)]),
     "pe_lm_head_kl": (c_int, [POINTER(PeDims), POINTER(PeWeights), c_int32, c_void_p, c_int32, c_void_p, c_void_p,
-                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "pe_lm_head_kl_workspace": (c_int, [POINTER(PeDims), c_int32, POINTER(c_size_t)]),
     "pe_draft_attention_backward": (c_int, [POINTER(PeAttnBwdArgs), c_void_p, c_size_t, c_void_p]),
     "pe_draft_attention_backward_workspace": (c_int, [POINTER(PeAttnBwdArgs), POINTER(c_size_t)]),
@@ -296,12 +296,13 @@ def pe_lm_head_kl_workspace(dims, n):
     return m.value
 
 
-def pe_lm_head_kl(dims, weights, n, x, k, target_ids, target_probs, kl, lse=None, workspace=None, stream=None):
+def pe_lm_head_kl(dims, weights, n, x, k, target_ids, target_probs, kl, lse=None, w_lm_rows=None, workspace=None,
+                  stream=None):
     ws = _workspace(pe_lm_head_kl_workspace(dims, n), x.device, workspace)
     w = weights if isinstance(weights, PeWeights) else weights_struct(weights)
     _check("pe_lm_head_kl", lib().pe_lm_head_kl(
-        ctypes.byref(dims), ctypes.byref(w), n, ptr(x), k, ptr(target_ids), ptr(target_probs), ptr(lse), ptr(kl),
-        ptr(ws), ws.numel(), stream_handle(stream)))
+        ctypes.byref(dims), ctypes.byref(w), n, ptr(x), k, ptr(target_ids), ptr(target_probs), ptr(w_lm_rows),
+        ptr(lse), ptr(kl), ptr(ws), ws.numel(), stream_handle(stream)))
 
 
 def pe_lm_head_argmax_noalloc(dims, weights, n, x, tokens, logits=None, stream=None):

@@ -838,8 +838,8 @@ pe_status pe_lm_head_kl_workspace(const pe_drafter_dims* dims, int32_t n, size_t
 }
 
 pe_status pe_lm_head_kl(const pe_drafter_dims* dims, const pe_drafter_weights* w, int32_t n, const float* x,
-                        int32_t k, const int32_t* target_ids, const float* target_probs, float* lse, float* kl,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        int32_t k, const int32_t* target_ids, const float* target_probs, const void* w_lm_rows,
+                        float* lse, float* kl, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   pe_status st = check_dims(dims);
   if (st != PE_OK) return st;
   if (!w || n < 0 || k < 1) return PE_ERR_INVALID_ARG;
@@ -847,6 +847,7 @@ pe_status pe_lm_head_kl(const pe_drafter_dims* dims, const pe_drafter_weights* w
   if (n == 0) return PE_OK;
   if (!x || !w->final_gain || !w->w_lm || !al16(w->w_lm) || !al16(x) || !al16(w->final_gain)) return PE_ERR_INVALID_ARG;
   if (!target_ids || !target_probs || !kl) return PE_ERR_INVALID_ARG;
+  if (w_lm_rows && !al16(w_lm_rows)) return PE_ERR_INVALID_ARG;
   const int bf = dims->dtype == PE_BF16;
   if (kl_topk_lds_bytes(dims->hidden, bf) > 65536) return PE_ERR_UNSUPPORTED;
   if (!ws_ok(workspace, workspace_bytes, lm_ws(dims, n, nullptr, true, true).total)) return PE_ERR_INVALID_ARG;
@@ -876,8 +877,8 @@ pe_status pe_lm_head_kl(const pe_drafter_dims* dims, const pe_drafter_weights* w
   float* l = lse ? lse : lw.lse;
   launch_lse_reduce(lw.pv, lw.ps, used, n, dims->vocab, nullptr, nullptr, l, nullptr, stream);
   // the target logits in fp32 and the KL sum of each row
-  launch_kl_topk(x, d, w->final_gain, dims->eps, w->w_lm, d, dims->vocab, bf, k, target_ids, target_probs, l, kl, n,
-                 stream);
+  launch_kl_topk(x, d, w->final_gain, dims->eps, w->w_lm, w_lm_rows, d, dims->vocab, bf, k, target_ids, target_probs, l,
+                 kl, n, stream);
   return launched();
 }
 

@@ -1101,11 +1101,14 @@ void launch_lse_reduce(const float* pv, const float* ps, int P, int M, int N, co
 // zero); wave w takes pairs w, w + 4, ..., each as one wave-wide dot product
 // with U chunk loads in flight per lane; the four waves' sums are added in a
 // fixed order.  The target logits are fp32 from the unrounded row, as in the
-// argmax re-score.
+// argmax re-score.  A row of the packed weight holds 16 of every 64 bytes of
+// its 16-row block, so a wave's loads of it touch 64 cache lines each; with
+// the row-major weight (Wrows) a wave reads 1 KB of one row per load.
 template <typename S>
 __global__ __launch_bounds__(256) void kl_topk_kernel(const float* x, int64_t ldx, const float* gain, float eps,
-                                                      const char* W, int K, int N, int k, const int32_t* ids,
-                                                      const float* probs, const float* lse, float* kl, int M) {
+                                                      const char* W, const char* Wrows, int K, int N, int k,
+                                                      const int32_t* ids, const float* probs, const float* lse,
+                                                      float* kl, int M) {
   constexpr int CH = Storage<S>::CH;  // elements per 16-byte chunk
   constexpr int STEP = 4 * CH;        // elements per packed 1 KB step of a 16-row block
   constexpr int U = 4;                // chunk loads in flight per lane
@@ -1143,7 +1146,8 @@ __global__ __launch_bounds__(256) void kl_topk_kernel(const float* x, int64_t ld
     const int t = ids[(int64_t)m * k + j];
     const float p = probs[(int64_t)m * k + j];
     if (t < 0 || t >= N || !(p > 0.f)) continue;  // the same pair for the whole wave
-    const char* wr = W + (int64_t)(t >> 4) * steps * 1024 + (t & 15) * 16;
+    const char* wr = Wrows ? Wrows + (int64_t)t * K * (int)sizeof(S)
+                           : W + (int64_t)(t >> 4) * steps * 1024 + (t & 15) * 16;
     float d = 0.f;
     for (int c0 = 0; c0 < nch; c0 += 64 * U) {
       u32x4 a[U];
@@ -1151,7 +1155,7 @@ __global__ __launch_bounds__(256) void kl_topk_kernel(const float* x, int64_t ld
       for (int u = 0; u < U; ++u) {
         const int ch = min(c0 + 64 * u + lane, nch - 1);
         const int k0 = ch * CH;
-        a[u] = ld16(wr + (int64_t)(k0 / STEP) * 1024 + ((k0 % STEP) / CH) * 256);
+        a[u] = ld16(wr + (Wrows ? (int64_t)ch * 16 : (int64_t)(k0 / STEP) * 1024 + ((k0 % STEP) / CH) * 256));
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -1175,17 +1179,19 @@ int kl_topk_lds_bytes(int K, int w_bf16) {
   return (nch + 64 * U - 1) / (64 * U) * (64 * U) * CH * 4;
 }
 
-void launch_kl_topk(const float* x, int64_t ldx, const float* gain, float eps, const void* W, int K, int N, int w_bf16,
-                    int k, const int32_t* ids, const float* probs, const float* lse, float* kl, int M, hipStream_t s) {
+void launch_kl_topk(const float* x, int64_t ldx, const float* gain, float eps, const void* W, const void* Wrows, int K,
+                    int N, int w_bf16, int k, const int32_t* ids, const float* probs, const float* lse, float* kl,
+                    int M, hipStream_t s) {
   const char* w = reinterpret_cast<const char*>(W);
+  const char* wrows = reinterpret_cast<const char*>(Wrows);
   const int rpx = (M + 7) / 8;
   const size_t lds = (size_t)kl_topk_lds_bytes(K, w_bf16);
   if (w_bf16)
-    hipLaunchKernelGGL(kl_topk_kernel<uint16_t>, dim3(8 * rpx), dim3(256), lds, s, x, ldx, gain, eps, w, K, N, k, ids,
-                       probs, lse, kl, M);
+    hipLaunchKernelGGL(kl_topk_kernel<uint16_t>, dim3(8 * rpx), dim3(256), lds, s, x, ldx, gain, eps, w, wrows, K, N,
+                       k, ids, probs, lse, kl, M);
   else
-    hipLaunchKernelGGL(kl_topk_kernel<float>, dim3(8 * rpx), dim3(256), lds, s, x, ldx, gain, eps, w, K, N, k, ids,
-                       probs, lse, kl, M);
+    hipLaunchKernelGGL(kl_topk_kernel<float>, dim3(8 * rpx), dim3(256), lds, s, x, ldx, gain, eps, w, wrows, K, N, k,
+                       ids, probs, lse, kl, M);
 }
 
 // ---------------------------------------------------------------------------

@@ -193,8 +193,11 @@ void launch_lse_reduce(const float* pv, const float* ps, int P, int M, int N, co
 // normalised row in fp32 (as in launch_argmax_rescore).  ids, probs: [M, k].
 // Dynamic LDS: kl_topk_lds_bytes(K, w_bf16) (the row's x * g, padded).
 int kl_topk_lds_bytes(int K, int w_bf16);
-void launch_kl_topk(const float* x, int64_t ldx, const float* gain, float eps, const void* W, int K, int N, int w_bf16,
-                    int k, const int32_t* ids, const float* probs, const float* lse, float* kl, int M, hipStream_t s);
+// Wrows: the same weight row-major [N, K] (storage type), or nullptr (the
+// rows are gathered from the packed W).
+void launch_kl_topk(const float* x, int64_t ldx, const float* gain, float eps, const void* W, const void* Wrows, int K,
+                    int N, int w_bf16, int k, const int32_t* ids, const float* probs, const float* lse, float* kl,
+                    int M, hipStream_t s);
 
 struct AttnParams {
   const void* q;

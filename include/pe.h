@@ -480,7 +480,12 @@ pe_status pe_lm_head_loss_workspace(const pe_drafter_dims* dims, int32_t n, size
  * positive (NaN included) adds nothing; the probabilities are used as given
  * (no renormalisation).  lse is streamed tile by tile as in pe_lm_head_loss;
  * the k target logits are computed in fp32 from the unrounded normalised
- * row.  x [n, hidden] f32 and final_gain 16-byte aligned; k >= 1 and
+ * row, reading the k target rows of the LM head.  w_lm_rows (optional,
+ * device, 16-byte aligned): the same LM head in its row-major [vocab,
+ * hidden] storage-type layout (the matrix pe_pack_weight packed); when given
+ * the target rows are read from it as whole rows, which costs about a
+ * quarter of the memory requests of gathering them from the packed weight;
+ * NULL gathers them from weights->w_lm.  x [n, hidden] f32 and final_gain 16-byte aligned; k >= 1 and
  * n * k < 2^31; kl [n] f32 required, lse [n] f32 may be NULL; otherwise
  * PE_ERR_INVALID_ARG.
  * Results do not depend on timing (fixed-order sums).  Workspace:
@@ -488,8 +493,8 @@ pe_status pe_lm_head_loss_workspace(const pe_drafter_dims* dims, int32_t n, size
  */
 pe_status pe_lm_head_kl(const pe_drafter_dims* dims, const pe_drafter_weights* weights,
                         int32_t n, const float* x, int32_t k, const int32_t* target_ids,
-                        const float* target_probs, float* lse, float* kl, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream);
+                        const float* target_probs, const void* w_lm_rows, float* lse, float* kl,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 pe_status pe_lm_head_kl_workspace(const pe_drafter_dims* dims, int32_t n, size_t* bytes);
 
 #ifdef __cplusplus

@@ -97,16 +97,18 @@ def test_entry_points_reject_before_launch():
     assert lib.pe_lm_head_loss(ctypes.byref(d), ctypes.byref(w), 0, None, None, None, None, None, 0, None) == 0
     n = ctypes.c_size_t()
     assert lib.pe_lm_head_loss_workspace(ctypes.byref(d), 7, ctypes.byref(n)) == 0 and n.value > 0
-    # top-k KL loss: k < 1, missing ids / probabilities / output, n * k past int32, workspace too small;
+    # top-k KL loss: k < 1, missing ids / probabilities / output, n * k past int32, workspace too small,
+    # a misaligned row-major weight;
     # empty is a no-op; its workspace holds the loss's plus the rows' log-sum-exp
     kl = lib.pe_lm_head_kl
-    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 0, FAKE, FAKE, None, FAKE, FAKE, big, None) == 1
-    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, None, FAKE, None, FAKE, FAKE, big, None) == 1
-    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, FAKE, None, None, FAKE, FAKE, big, None) == 1
-    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, FAKE, FAKE, FAKE, None, FAKE, big, None) == 1
-    assert kl(ctypes.byref(d), ctypes.byref(w2), 1 << 16, FAKE, 1 << 15, FAKE, FAKE, None, FAKE, FAKE, big, None) == 1
-    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, FAKE, FAKE, None, FAKE, FAKE, 16, None) == 1
-    assert kl(ctypes.byref(d), ctypes.byref(w), 0, None, 3, None, None, None, None, None, 0, None) == 0
+    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 0, FAKE, FAKE, None, None, FAKE, FAKE, big, None) == 1
+    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, None, FAKE, None, None, FAKE, FAKE, big, None) == 1
+    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, FAKE, None, None, None, FAKE, FAKE, big, None) == 1
+    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, FAKE, FAKE, None, FAKE, None, FAKE, big, None) == 1
+    assert kl(ctypes.byref(d), ctypes.byref(w2), 1 << 16, FAKE, 1 << 15, FAKE, FAKE, None, None, FAKE, FAKE, big, None) == 1
+    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, FAKE, FAKE, None, None, FAKE, FAKE, 16, None) == 1
+    assert kl(ctypes.byref(d), ctypes.byref(w2), 4, FAKE, 3, FAKE, FAKE, ctypes.c_void_p(0x1002), None, FAKE, FAKE, big, None) == 1
+    assert kl(ctypes.byref(d), ctypes.byref(w), 0, None, 3, None, None, None, None, None, None, 0, None) == 0
     m = ctypes.c_size_t()
     assert lib.pe_lm_head_kl_workspace(ctypes.byref(d), 7, ctypes.byref(m)) == 0 and m.value >= n.value + 7 * 4
 

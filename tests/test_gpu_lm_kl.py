@@ -7,7 +7,10 @@ stream for M <= 16 rows, the tiled kernel, the large-M bf16 kernel) in bf16
 and f32, k from 1 to 64, and pairs that add nothing (ids -1 and >= vocab, a
 zero and a NaN probability, a row with no valid pair).  Full-size: the c=1
 shape (7 rows, vocab 201,088) in full and the 7,794-row training batch at
-k = 32 on a sample of rows.  Results repeat bit for bit.
+k = 32 on a sample of rows.  Results repeat bit for bit, and reading the
+target rows from the row-major LM head (w_lm_rows) gives the same bits as
+gathering them from the packed one: each lane sums the same chunks in the
+same order either way.
 """
 import numpy as np
 import pytest
@@ -38,19 +41,24 @@ def _case(dims, n, k, seed):
     return W, x, ids, p
 
 
-def _run(dims, W, x, ids, p, dev=None):
+def _run(dims, W, x, ids, p, dev=None, rows=False):
     n, k = ids.shape
     cd = L.dims_struct(dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn, dims.vocab,
                        dims.mask_token_id, dims.eps, dims.dtype)
     if dev is None:
         dev = dict(w_lm=L.pe_pack_weight(to_device(W["w_lm"], "cuda")), final_gain=to_device(W["final_gain"], "cuda"))
     cw = L.weights_struct(dev)
+    w_rows = None
+    if rows:
+        w_rows = dev.get("w_lm_rows")
+        if w_rows is None:
+            w_rows = dev["w_lm_rows"] = to_device(W["w_lm"], "cuda")
     xd = torch.from_numpy(x).cuda()
     idd = torch.from_numpy(ids).cuda()
     pd = torch.from_numpy(p).cuda()
     lse = torch.empty(n, dtype=torch.float32, device="cuda")
     kl = torch.empty(n, dtype=torch.float32, device="cuda")
-    L.pe_lm_head_kl(cd, cw, n, xd, k, idd, pd, kl, lse)
+    L.pe_lm_head_kl(cd, cw, n, xd, k, idd, pd, kl, lse, w_lm_rows=w_rows)
     torch.cuda.synchronize()
     return lse, kl, dev
 
@@ -82,6 +90,8 @@ def test_small_vocab_paths(dtype, n, k):
     _check("%s n=%d k=%d" % (dtype, n, k), dims, W, x, ids, p, lse, kl)
     lse2, kl2, _ = _run(dims, W, x, ids, p, dev)
     assert torch.equal(lse, lse2) and torch.equal(kl, kl2)
+    lse3, kl3, _ = _run(dims, W, x, ids, p, dev, rows=True)
+    assert torch.equal(lse, lse3) and torch.equal(kl, kl3)
 
 
 def test_ragged_hidden_rounds():
@@ -91,8 +101,10 @@ def test_ragged_hidden_rounds():
         dims = si.DrafterDims(hidden=hidden, n_q_heads=2, n_kv_heads=1, head_dim=64, ffn=128, vocab=1000, dtype=dtype)
         W, x, ids, p = _case(dims, 24, 17, 70)
         say("kl %s hidden=%d" % (dtype, hidden))
-        lse, kl, _ = _run(dims, W, x, ids, p)
+        lse, kl, dev = _run(dims, W, x, ids, p)
         _check("%s hidden=%d" % (dtype, hidden), dims, W, x, ids, p, lse, kl)
+        lse2, kl2, _ = _run(dims, W, x, ids, p, dev, rows=True)
+        assert torch.equal(lse, lse2) and torch.equal(kl, kl2)
 
 
 def test_full_vocab_decode_shape():
@@ -108,7 +120,10 @@ def test_training_sized_batch_sampled():
     n, k = 7794, 32
     W, x, ids, p = _case(dims, n, k, 72)
     say("kl full vocab n=%d k=%d" % (n, k))
-    lse, kl, _ = _run(dims, W, x, ids, p)
+    lse, kl, dev = _run(dims, W, x, ids, p)
+    lse2, kl2, _ = _run(dims, W, x, ids, p, dev, rows=True)
+    assert torch.equal(lse, lse2) and torch.equal(kl, kl2)
+    del dev
     rows = np.unique(np.concatenate([[0, 1, 2, n // 2, n - 2, n - 1],
                                      np.random.default_rng(5).choice(n, 26, replace=False)]))
     _check("vocab 201088 n=%d k=%d sampled" % (n, k), dims, W, x, ids, p, lse, kl, rows)
