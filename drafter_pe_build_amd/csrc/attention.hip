@@ -114,8 +114,13 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   constexpr int NCH = (KT * DC + 255) / 256;     // 16-byte chunks of K (and of V) per thread per tile
   constexpr int NB = BF ? 1 : 2;                 // 16-key blocks per P^T operand of one half tile
   static_assert(2 * NCH <= 32, "valid-row bits");
-  __shared__ __attribute__((aligned(16))) char Ks[2][KT * KPB];
-  __shared__ __attribute__((aligned(16))) char Vs[2][VBYTES];
+  // K/V ring: bf16 at head_dim 64 (the decode shapes, whose tiles carry
+  // little work per byte) keeps two tiles in flight while one is used, in
+  // 57 KB of the two workgroups' 160 KB; otherwise one (head_dim 128 fills
+  // its 80 KB with two 32 KB stages).
+  constexpr int NBUF = (BF && DH == 64) ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) char Ks[NBUF][KT * KPB];
+  __shared__ __attribute__((aligned(16))) char Vs[NBUF][VBYTES];
   __shared__ int s_start[QMAX], s_off[QMAX + 1];
   __shared__ int s_anc_row[ANC_MAX];                               // chain rows, then
   __shared__ __attribute__((aligned(16))) int s_anc_own[ANC_MAX];  // -1 to the end of the tile
@@ -615,11 +620,12 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       for (int bb = 0; bb < NB; ++bb) asm volatile("" : : "v"(bop[cb][bb]));
   };
 
-  // ---- tile loop.  The next tile's global loads are issued after the
-  // barrier and written to the other LDS buffer after this tile's work (every
-  // wave has passed the barrier that follows its last read of that buffer).
-  // The last iteration reloads its own tile into the unused buffer, which
-  // keeps the loop free of branches around the staging.  Within a tile the
+  // ---- tile loop.  Tile it + NBUF - 1's copies are issued after the
+  // barrier, into the buffer of tile it - 1 (every wave has passed the
+  // barrier that follows its last read of it); f32 tiles are staged through
+  // registers and written to the other buffer after this tile's work, the
+  // last iteration reloading its own tile, which keeps the loop free of
+  // branches around the staging.  Within a tile the
   // steps are ordered so that the exponentials of one half run beside the
   // matrix products of the other:
   //   S0 | check0 (+rescale) | S1 + exp0 | check1 | PV0 + exp1 | (rescale) | PV1
@@ -627,6 +633,7 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   if (n_iter > 0) {
     if constexpr (BF) {
       dma_tile(0, 0);
+      if (NBUF > 2 && n_iter > 1) dma_tile(1, 1);
     } else {
       load_tile(0);
       store_tile(0);
@@ -637,11 +644,17 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   // (with both in one body the compiler copied every score at the join).
   auto tile_step = [&](int it, auto anc_c) {
     constexpr bool anc = decltype(anc_c)::value;
-    const int buf = it & 1;
-    if constexpr (BF) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of tile it
+    const int buf = NBUF == 2 ? it & 1 : it % NBUF;
+    if constexpr (BF) {
+      // this wave's copies of tile it (those of tile it + 1, issued later,
+      // may stay in flight: the memory counter retires them in order)
+      if (NBUF == 2 || it + 1 >= n_iter) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if (wave < NDMA - NWAVE * (NDW - 1)) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NDW) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NDW - 1) : "memory");
+    }
     __syncthreads();
     if constexpr (BF) {
-      if (it + 1 < n_iter) dma_tile(it + 1, buf ^ 1);  // into the buffer of tile it - 1, read by now
+      if (it + NBUF - 1 < n_iter) dma_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
     } else {
       load_tile(min(it + 1, n_iter - 1));
     }
