@@ -588,7 +588,8 @@ void gemm_stream_lds_kernel(GemmParams p) {
   }
 }
 
-// LM head for M <= 16: grid-stride over groups of NFB weight blocks; KS waves
+// LM head for M <= 16 whose rows do not fit in LDS (XL false; staged rows go to
+// lm_head_sweep_kernel): grid-stride over groups of NFB weight blocks; KS waves
 // per block split K and sum through LDS in ks order.  With XL the M
 // activation rows are staged once per workgroup in LDS, RMS-normalised on the
 // way when NORM (row pitch K*elem + 16 bytes, so the 16 lanes of one k-chunk
@@ -716,6 +717,125 @@ void lm_argmax_stream_kernel(GemmParams p) {
   if ((int)threadIdx.x < M) {
     RowRed t = RowRed::init();
     for (int w = 0; w < NW; ++w) {
+      const u32x4 o = sb[w][threadIdx.x];
+      if (LSE) t.merge(true, __uint_as_float(o[0]), 0, __uint_as_float(o[2]));
+      else t.merge_packed(o);
+    }
+    if (LSE) {
+      p.epi.part_val[(int64_t)blockIdx.x * M + threadIdx.x] = t.v;
+      p.epi.part_sum[(int64_t)blockIdx.x * M + threadIdx.x] = t.s;
+    } else {
+      p.epi.part_top2[(int64_t)blockIdx.x * M + threadIdx.x] = t.pack2();
+    }
+  }
+}
+
+// LM head for M <= 16 with the rows staged in LDS, block-sweep form.
+// Workgroup w of G (one per CU) takes the weight blocks w, w + G, w + 2G, ...,
+// so at any moment the G workgroups read G neighbouring blocks: one contiguous
+// region of the packed weight, which HBM streams faster than G separate runs
+// (a plain read of the 1.16 GB LM head: 6.38 TB/s this way against 6.08 TB/s
+// for contiguous shares per wave).  Within a block the NWV waves take
+// interleaved 1 KB steps (wave v: steps v, v + NWV, ...), UB per batch; the
+// next batch (of this block or the next) is in flight while one is
+// multiplied.  A block's NWV partial tiles are summed in wave order through
+// LDS by one wave (a different one each block), which keeps the running
+// top-2 (or log-sum-exp) of its rows; the waves' lists are merged at the end
+// into partial slot [blockIdx][row], reduced by argmax_rescore_kernel.  The
+// first weight batch is requested right after the rows' reads, so the
+// staging hides under its round trip.  Two waves per SIMD (256 registers per
+// lane), one workgroup per CU.
+template <typename S, int NWV, int UB, bool NORM, bool LSE>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2)))
+void lm_head_sweep_kernel(GemmParams p) {
+  constexpr int CH = Storage<S>::CH;
+  constexpr int STEP = 4 * CH;
+  extern __shared__ __attribute__((aligned(16))) char xs[];
+  __shared__ f32x4 red[2][NWV][64];
+  __shared__ u32x4 sb[NWV][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nsteps = K / STEP;
+  const int nfb = (N + 15) >> 4;
+  const int G = gridDim.x;
+  const int nbat = (nsteps + NWV * UB - 1) / (NWV * UB);  // batches per block and wave
+  const int nblk = (int)blockIdx.x < nfb ? (nfb - 1 - (int)blockIdx.x) / G + 1 : 0;
+  const int nitems = nblk * nbat;
+  const bool xr = r < M;
+  // this wave's last step (step 0 for a wave without steps): slots past the
+  // end re-read it, so every load stays inside the block
+  const int vlast = wave < nsteps ? wave + NWV * ((nsteps - 1 - wave) / NWV) : 0;
+  const char* W = reinterpret_cast<const char*>(p.W) + lane * 16;
+  auto step_of = [&](int i, int u) { return wave + NWV * ((i % nbat) * UB + u); };
+  auto load = [&](u32x4 (&dst)[UB], int i) {
+    const char* src = W + (int64_t)((int)blockIdx.x + G * (i / nbat)) * nsteps * 1024;
+#pragma unroll
+    for (int u = 0; u < UB; ++u) dst[u] = ld16(src + (int64_t)min(step_of(i, u), vlast) * 1024);
+  };
+  u32x4 wa[UB], wb[UB];
+  const int xp = K * (int)sizeof(S) + 16;  // LDS row pitch, bytes
+  {
+    std::conditional_t<NORM, NormStage<S, float, norm_chunks<float>()>, CopyStage<S, 8>> stage;
+    if constexpr (NORM) stage.load(p, wave); else stage.load(p);
+    if (nitems > 0) load(wa, 0);
+    // LDS: M rows at pitch xp, the zero chunk, then the gains of a norm
+    if constexpr (NORM) stage.finish(p, xs, xp, xs + M * xp + 16, wave, NWV); else stage.finish(p, xs, xp);
+  }
+  clear_ints(p);
+  const char* xzero = xs + M * xp;
+  if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(xs + M * xp) = zero4();
+  __syncthreads();
+  const char* xrow = xr ? xs + r * xp + g * 16 : xzero;
+  const int xstep = xr ? STEP * (int)sizeof(S) : 0;
+
+  RowRed rr = RowRed::init();  // argmax or (LSE) log-sum-exp state of row r over this lane's features
+  const int tgt = (LSE && p.epi.targets && xr) ? p.epi.targets[r] : -1;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4 (&src)[UB], int i) {
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int st = step_of(i, u);
+      // slots past the wave's steps multiply the zero chunk
+      mma16(acc, src[u], ld16(st < nsteps ? xrow + (int64_t)st * xstep : xzero), S());
+    }
+    if (i % nbat == nbat - 1) {  // the block is complete: its partial tiles summed in wave order
+      const int bi = i / nbat;
+      red[bi & 1][wave][lane] = acc;
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      if (wave == bi % NWV) {
+        f32x4 t = red[bi & 1][0][lane];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) t += red[bi & 1][w][lane];
+        if (xr) {
+          const int b = (int)blockIdx.x + G * bi;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = b * 16 + 4 * g + j;
+            if (n >= N) continue;
+            if (p.epi.logits) p.epi.logits[(int64_t)r * N + n] = t[j];
+            if (LSE && n == tgt) p.epi.tgt_logit[r] = t[j];
+            rr.add(LSE, t[j], n);
+          }
+        }
+      }
+    }
+  };
+  for (int i = 0; i < nitems; i += 2) {
+    if (i + 1 < nitems) load(wb, i + 1);
+    compute(wa, i);
+    if (i + 1 >= nitems) break;
+    if (i + 2 < nitems) load(wa, i + 2);
+    compute(wb, i + 1);
+  }
+  rr.merge_groups(LSE);
+  if (g == 0) sb[wave][r] = LSE ? u32x4{__float_as_uint(rr.v), 0u, __float_as_uint(rr.s), 0u} : rr.pack2();
+  __syncthreads();
+  if ((int)threadIdx.x < M) {
+    RowRed t = RowRed::init();
+    for (int w = 0; w < NWV; ++w) {
       const u32x4 o = sb[w][threadIdx.x];
       if (LSE) t.merge(true, __uint_as_float(o[0]), 0, __uint_as_float(o[2]));
       else t.merge_packed(o);
@@ -1197,23 +1317,31 @@ void launch_kl_topk(const float* x, int64_t ldx, const float* gain, float eps, c
 // ---------------------------------------------------------------------------
 // Dispatch
 static constexpr int kStreamU = 8;     // 1 KB steps in flight per wave
-// LM-head launch shape: NFB blocks x KS waves per workgroup, grid capped at kLmGrid.
+// Launch shape of lm_argmax_stream_kernel (rows too wide for LDS): NFB blocks x
+// KS waves per workgroup.
 #ifndef PE_LM_NFB
 #define PE_LM_NFB 4
 #endif
 #ifndef PE_LM_KS
 #define PE_LM_KS 3
 #endif
-#ifndef PE_LM_GRID
-#define PE_LM_GRID 1024
-#endif
 #ifndef PE_LM_U
 #define PE_LM_U 5
 #endif
-static constexpr int kLmNFB = PE_LM_NFB, kLmKS = PE_LM_KS, kLmGrid = PE_LM_GRID, kLmU = PE_LM_U;
-// Largest activation block the LM-head kernel stages in LDS (its own arrays
-// take a few KB of the 160 KB); wider rows are read from global memory.
-static constexpr int kLmXLds = 144 * 1024;
+static constexpr int kLmNFB = PE_LM_NFB, kLmKS = PE_LM_KS, kLmU = PE_LM_U;
+// The block-sweep LM-head kernel: waves per workgroup and steps per wave and
+// batch (8 x 12: one batch per block of the 90-step d = 2880 rows; measured
+// against 4 x 23, 12 x 8 and 16 x 6), workgroups (the CU count of MI355X),
+// and the largest row block it stages beside its static LDS (the two rings
+// of partial tiles and the lists).
+#ifndef PE_LM_SWEEP_W
+#define PE_LM_SWEEP_W 8
+#endif
+#ifndef PE_LM_SWEEP_U
+#define PE_LM_SWEEP_U 12
+#endif
+static constexpr int kLmSweepW = PE_LM_SWEEP_W, kLmSweepU = PE_LM_SWEEP_U, kLmSweepGrid = 256;
+static constexpr int kLmSweepXLds = 158 * 1024 - 3 * kLmSweepW * 1024;
 
 // Waves per 16-row block: the most (up to 16) that still leave every wave at
 // least one full batch of kStreamU steps.
@@ -1232,9 +1360,9 @@ static int stream_ks_segs(int nsteps, int segs) {
 }
 
 int gemm_argmax_partials(int M, int N) {
-  if (M <= 16) {
-    const int ntiles = ((N + 15) / 16 + kLmNFB - 1) / kLmNFB;
-    return ntiles < kLmGrid ? ntiles : kLmGrid;
+  if (M <= 16) {  // one workgroup per CU, each with at least one weight block
+    const int nfb = (N + 15) / 16;
+    return nfb < kLmSweepGrid ? nfb : kLmSweepGrid;
   }
   return (N + 63) / 64;  // largest count over the tiled configurations (BN >= 64)
 }
@@ -1396,25 +1524,25 @@ static GemmParams norm_first(const GemmParams& p, hipStream_t s, bool packed = f
 template <typename S, bool LSE>
 static int launch_lm_stream(const GemmParams& p0, bool norm, bool norm_fits, bool xf32, size_t lds, hipStream_t s) {
   const int grid = gemm_argmax_partials(p0.M, p0.N);
-  const dim3 block(64 * kLmNFB * kLmKS);
-  if (lds <= (size_t)kLmXLds && norm_fits && (!norm || xf32)) {
+  if (lds <= (size_t)kLmSweepXLds && norm_fits && (!norm || xf32)) {
     if (norm) {
-      allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, true, LSE>>(kLmXLds);
-      hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, true, LSE>), dim3(grid), block, lds, s,
-                         p0);
+      allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, true, LSE>>(kLmSweepXLds);
+      hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, true, LSE>), dim3(grid), dim3(64 * kLmSweepW),
+                         lds, s, p0);
     } else {
-      allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false, LSE>>(kLmXLds);
-      hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false, LSE>), dim3(grid), block, lds,
-                         s, p0);
+      allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE>>(kLmSweepXLds);
+      hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE>), dim3(grid), dim3(64 * kLmSweepW),
+                         lds, s, p0);
     }
     return grid;
   }
   const GemmParams p = norm ? norm_first<S>(p0, s, false) : p0;
-  if (lds <= (size_t)kLmXLds) {
-    allow_lds<&lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false, LSE>>(kLmXLds);
-    hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, true, false, LSE>), dim3(grid), block, lds, s,
-                       p);
+  if (lds <= (size_t)kLmSweepXLds) {
+    allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE>>(kLmSweepXLds);
+    hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE>), dim3(grid), dim3(64 * kLmSweepW),
+                       lds, s, p);
   } else {
+    const dim3 block(64 * kLmNFB * kLmKS);
     hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, false, false, LSE>), dim3(grid), block, 0, s,
                        p);
   }
