@@ -1330,15 +1330,16 @@ static constexpr int kStreamU = 8;     // 1 KB steps in flight per wave
 #endif
 static constexpr int kLmNFB = PE_LM_NFB, kLmKS = PE_LM_KS, kLmU = PE_LM_U;
 // The block-sweep LM-head kernel: waves per workgroup and steps per wave and
-// batch (8 x 12: one batch per block of the 90-step d = 2880 rows; measured
-// against 4 x 23, 12 x 8 and 16 x 6), workgroups (the CU count of MI355X),
+// batch (8 x 6: two batches per block of the 90-step d = 2880 rows; 8 x 3,
+// 8 x 4, 8 x 12, 4 x 12, 4 x 23 and 12 x 8 measured slower, as was a third
+// batch in flight), workgroups (the CU count of MI355X),
 // and the largest row block it stages beside its static LDS (the two rings
 // of partial tiles and the lists).
 #ifndef PE_LM_SWEEP_W
 #define PE_LM_SWEEP_W 8
 #endif
 #ifndef PE_LM_SWEEP_U
-#define PE_LM_SWEEP_U 12
+#define PE_LM_SWEEP_U 6
 #endif
 static constexpr int kLmSweepW = PE_LM_SWEEP_W, kLmSweepU = PE_LM_SWEEP_U, kLmSweepGrid = 256;
 static constexpr int kLmSweepXLds = 158 * 1024 - 3 * kLmSweepW * 1024;
