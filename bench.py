@@ -26,7 +26,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch of the LM-head stage measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE, scaled by a 1 GiB copy (profiles/decode_c1_lm_head_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
-LM_STAGE_TRAFFIC = {"fingerprint": "e83fac8ccbb4cfa8", "bytes": 1165387571}
+LM_STAGE_TRAFFIC = {"fingerprint": "11374d725bea609e", "bytes": 1160387994}
 LM_SOURCES = ("gemm.hip", "norm.hip", "common.h", "kernels.h", "epilogue.h")
 # The same for one whole c=64 decode step (every kernel of the step), from
 # profiles/decode_c64_step_counters.md.
