@@ -243,78 +243,9 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   };
   const int n_tiles = n_pref + (n_anc + KT - 1) / KT;
 
-  // ---- this lane's columns, one per column block
   const S* Q = reinterpret_cast<const S*>(p.q);
   const S* Kg = reinterpret_cast<const S*>(p.k);
   const S* Vg = reinterpret_cast<const S*>(p.v);
-  int cq[CBLK], climit[CBLK], hh[CBLK];
-  bool cact[CBLK];
-  u32x4 qreg[CBLK][NST];
-  int lo = 0x7fffffff, hi = -1;
-#pragma unroll
-  for (int cb = 0; cb < CBLK; ++cb) {
-    const int col = wave * (CBLK * 16) + cb * 16 + r;
-    cq[cb] = col / G;
-    hh[cb] = kvh * G + col % G;
-    cact[cb] = cq[cb] < nq;
-    climit[cb] = cact[cb] ? min(s_start[cq[cb]], kend) : -1;
-    if (cact[cb]) {
-      lo = min(lo, climit[cb]);
-      hi = max(hi, climit[cb]);
-    }
-    const int qrow = cact[cb] ? (p.q_rows ? p.q_rows[qbase + cq[cb]] : qbase + cq[cb]) : -1;
-#pragma unroll
-    for (int t = 0; t < NST; ++t)
-      qreg[cb][t] = (qrow >= 0) ? ld16(Q + (int64_t)qrow * p.q_stride + (int64_t)hh[cb] * DH + t * STEP + g * CH)
-                                : u32x4{0u, 0u, 0u, 0u};
-  }
-  // the Q operands are complete before the tile loop, whose global loads
-  // are then only the next tile's
-#pragma unroll
-  for (int cb = 0; cb < CBLK; ++cb)
-#pragma unroll
-    for (int t = 0; t < NST; ++t) asm volatile("" : : "v"(qreg[cb][t]));
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, __shfl_xor(lo, o, 64));
-    hi = max(hi, __shfl_xor(hi, o, 64));
-  }
-  const int wmin = __builtin_amdgcn_readfirstlane(lo);   // every active column sees keys <= wmin
-  const int wmax = __builtin_amdgcn_readfirstlane(hi);   // no column sees keys > wmax
-  // chain entries owned by this wave's queries (a query's G columns may
-  // straddle two waves when G exceeds a wave's 16 * CBLK columns)
-  const int wq0 = min(wave * CBLK * 16 / G, nq), wq1 = min(((wave + 1) * CBLK * 16 + G - 1) / G, nq);
-  const int wa0 = s_off[wq0], wa1 = s_off[wq1];
-
-  // m_run: running maximum (raw score units); thr = m_run + thr_gap; mb =
-  // m_run * scale * log2 e (0 while no score has been seen, m_run = -inf)
-  // l_run: this lane's share of the row sum (its keys); the column's l is
-  // the sum over the column's four lanes.  bf16 at head_dim 128 (LMMA): the
-  // row sum is one more matrix product per column block, a row of ones times
-  // P^T (acc_l, row 0 of a 16-row block: element 0 on the lanes with g = 0,
-  // zero elsewhere), so it is rescaled with O and costs no vector adds (the
-  // training shapes are bound by the softmax's vector work: 316 against 324
-  // us at N=4096; the decode shapes at head_dim 64 keep the adds).
-  constexpr bool LMMA = BF && DH == 128;
-  float m_run[CBLK], thr[CBLK], mb[CBLK], l_run[LMMA ? 1 : CBLK];
-  f32x4 acc[CBLK][NMB];
-  f32x4 acc_l[LMMA ? CBLK : 1];
-  int64_t dcnt[CBLK];
-  uint64_t dhsh[CBLK];
-#pragma unroll
-  for (int cb = 0; cb < CBLK; ++cb) {
-    m_run[cb] = -INFINITY;
-    thr[cb] = -INFINITY;
-    mb[cb] = 0.f;
-    if constexpr (LMMA) acc_l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    else l_run[cb] = 0.f;
-    dcnt[cb] = 0;
-    dhsh[cb] = 0;
-#pragma unroll
-    for (int i = 0; i < NMB; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const float sl2 = p.scale_log2;
-  const float thr_gap = 8.0f / sl2;
-
   // ---- tile staging.  Thread chunk i covers key (tid + 256 i) / DC, 16-byte
   // chunk (tid + 256 i) % DC of both K and V.  Keys a tile does not hold for
   // anyone (past the prefix end, padding of the last chain tile) load a row
@@ -442,6 +373,81 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       }
     }
   };
+
+  // ---- this lane's columns, one per column block
+  int cq[CBLK], climit[CBLK], hh[CBLK];
+  bool cact[CBLK];
+  u32x4 qreg[CBLK][NST];
+  int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+  for (int cb = 0; cb < CBLK; ++cb) {
+    const int col = wave * (CBLK * 16) + cb * 16 + r;
+    cq[cb] = col / G;
+    hh[cb] = kvh * G + col % G;
+    cact[cb] = cq[cb] < nq;
+    climit[cb] = cact[cb] ? min(s_start[cq[cb]], kend) : -1;
+    if (cact[cb]) {
+      lo = min(lo, climit[cb]);
+      hi = max(hi, climit[cb]);
+    }
+    const int qrow = cact[cb] ? (p.q_rows ? p.q_rows[qbase + cq[cb]] : qbase + cq[cb]) : -1;
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+      qreg[cb][t] = (qrow >= 0) ? ld16(Q + (int64_t)qrow * p.q_stride + (int64_t)hh[cb] * DH + t * STEP + g * CH)
+                                : u32x4{0u, 0u, 0u, 0u};
+  }
+  // the first tiles' copies go out beside the Q reads (one round trip for
+  // both); the Q operands are complete before the tile loop, whose global
+  // loads are then only the copies of later tiles
+  const int n_iter = have_rows ? n_tiles : 0;
+  if constexpr (BF) {
+    if (n_iter > 0) dma_tile(0, 0);
+    if (NBUF > 2 && n_iter > 1) dma_tile(1, 1);
+  }
+#pragma unroll
+  for (int cb = 0; cb < CBLK; ++cb)
+#pragma unroll
+    for (int t = 0; t < NST; ++t) asm volatile("" : : "v"(qreg[cb][t]));
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o, 64));
+    hi = max(hi, __shfl_xor(hi, o, 64));
+  }
+  const int wmin = __builtin_amdgcn_readfirstlane(lo);   // every active column sees keys <= wmin
+  const int wmax = __builtin_amdgcn_readfirstlane(hi);   // no column sees keys > wmax
+  // chain entries owned by this wave's queries (a query's G columns may
+  // straddle two waves when G exceeds a wave's 16 * CBLK columns)
+  const int wq0 = min(wave * CBLK * 16 / G, nq), wq1 = min(((wave + 1) * CBLK * 16 + G - 1) / G, nq);
+  const int wa0 = s_off[wq0], wa1 = s_off[wq1];
+
+  // m_run: running maximum (raw score units); thr = m_run + thr_gap; mb =
+  // m_run * scale * log2 e (0 while no score has been seen, m_run = -inf)
+  // l_run: this lane's share of the row sum (its keys); the column's l is
+  // the sum over the column's four lanes.  bf16 at head_dim 128 (LMMA): the
+  // row sum is one more matrix product per column block, a row of ones times
+  // P^T (acc_l, row 0 of a 16-row block: element 0 on the lanes with g = 0,
+  // zero elsewhere), so it is rescaled with O and costs no vector adds (the
+  // training shapes are bound by the softmax's vector work: 316 against 324
+  // us at N=4096; the decode shapes at head_dim 64 keep the adds).
+  constexpr bool LMMA = BF && DH == 128;
+  float m_run[CBLK], thr[CBLK], mb[CBLK], l_run[LMMA ? 1 : CBLK];
+  f32x4 acc[CBLK][NMB];
+  f32x4 acc_l[LMMA ? CBLK : 1];
+  int64_t dcnt[CBLK];
+  uint64_t dhsh[CBLK];
+#pragma unroll
+  for (int cb = 0; cb < CBLK; ++cb) {
+    m_run[cb] = -INFINITY;
+    thr[cb] = -INFINITY;
+    mb[cb] = 0.f;
+    if constexpr (LMMA) acc_l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    else l_run[cb] = 0.f;
+    dcnt[cb] = 0;
+    dhsh[cb] = 0;
+#pragma unroll
+    for (int i = 0; i < NMB; ++i) acc[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = p.scale_log2;
+  const float thr_gap = 8.0f / sl2;
 
   // ---- per-half steps.  A half is 32 keys; this lane holds keys
   // k0 + 16b + 4g + j (b = 2h, 2h+1; j < 4) of each of its columns.
@@ -629,12 +635,8 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   // steps are ordered so that the exponentials of one half run beside the
   // matrix products of the other:
   //   S0 | check0 (+rescale) | S1 + exp0 | check1 | PV0 + exp1 | (rescale) | PV1
-  const int n_iter = have_rows ? n_tiles : 0;
-  if (n_iter > 0) {
-    if constexpr (BF) {
-      dma_tile(0, 0);
-      if (NBUF > 2 && n_iter > 1) dma_tile(1, 1);
-    } else {
+  if constexpr (!BF) {
+    if (n_iter > 0) {
       load_tile(0);
       store_tile(0);
     }
