@@ -153,18 +153,23 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   const int qbase = seg * p.q_per_seg + tile * QPW;
   const int nq = min(QPW, p.q_per_seg - tile * QPW);
 
-  // ---- per-query metadata, chain lengths, exclusive scan of the lengths
-  int st = -1, cnt = 0, self = -1;
+  // ---- per-query metadata, chain lengths, exclusive scan of the lengths.
+  // The chain walk keeps its rows in the last K buffer (free until the tile
+  // loop), so the compacted list is built from LDS after the scan instead
+  // of walking the parents a second time.
+  static_assert(QMAX * MAXD * 4 <= KT * KPB, "chain walk rows fit one K buffer");
+  int* s_walk = reinterpret_cast<int*>(Ks[NBUF - 1]);
+  int st = -1, cnt = 0;
   if (tid < nq) {
     const int qi = qbase + tid;
     const int mi = (p.meta_by_row && p.q_rows) ? p.q_rows[qi] : qi;
     st = p.q_start[mi];
     if (p.q_depth) {
       const int dp = min(max(p.q_depth[mi], 0), maxd);
-      self = p.q_self_row[mi];
-      int row = self;
+      int row = p.q_self_row[mi];
       for (int e = 0; e < dp; ++e) {
         if (row < 0 || row >= p.num_kv_rows) break;
+        s_walk[tid * MAXD + cnt] = row;
         ++cnt;
         row = p.kv_parent[row];
       }
@@ -194,12 +199,10 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   if (tid < QMAX) s_off[tid] = wofs + incl - cnt;
   if (tid == 0) s_off[QMAX] = n_anc_all;
   if (cnt > 0) {
-    int row = self;
     const int o = wofs + incl - cnt;
     for (int e = 0; e < cnt; ++e) {
-      s_anc_row[o + e] = row;
+      s_anc_row[o + e] = s_walk[tid * MAXD + e];
       s_anc_own[o + e] = tid;
-      row = p.kv_parent[row];
     }
   }
   if (tid < KT) {  // pad the last chain tile (ANC_MAX is a multiple of KT)
