@@ -46,19 +46,31 @@ constexpr int BCOLK = 64;  // (query, head) columns per tile (dK, dV)
 constexpr int BMAXG = 16;  // groups a layout may have
 constexpr int BSPL = 4;    // dK/dV workgroups per key tile, each a share of its query tiles
 
-// First row in [lo, hi) whose start is >= s (rows sorted by start).
-__device__ int lower_row(const int32_t* start, int lo, int hi, int s) {
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (start[mid] < s) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-// First row in [lo, hi) whose start is > s.
-__device__ int upper_row(const int32_t* start, int lo, int hi, int s) {
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (start[mid] <= s) lo = mid + 1; else hi = mid;
+// First row in [lo, hi) whose start is >= s (GT: > s), or hi if there is
+// none; rows sorted by start.  All 64 lanes of the calling wave take part
+// (wave-uniform arguments): each round the lanes read the starts of 64
+// evenly spaced rows and the range shrinks to the gap between the last row
+// below the bound and the first one at or above it, so 4,096 rows take two
+// dependent reads instead of twelve.
+template <bool GT>
+__device__ int find_row_wave(const int32_t* start, int lo, int hi, int s) {
+  const int lane = threadIdx.x & 63;
+  while (hi > lo) {
+    const int n = hi - lo;
+    if (n <= 64) {
+      const bool below = lane < n && (GT ? start[lo + lane] <= s : start[lo + lane] < s);
+      return lo + __popcll(__ballot(below));
+    }
+    // probe i(l) = lo + n (l + 1) / 65, l = 0..63: increasing, inside [lo, hi)
+    auto probe = [&](int l) { return lo + (int)((int64_t)n * (l + 1) / 65); };
+    const int i = probe(lane);
+    const bool below = GT ? start[i] <= s : start[i] < s;
+    const int c = __popcll(__ballot(below));  // the rows below the bound are a prefix
+    const int nlo = c > 0 ? probe(c - 1) + 1 : lo;
+    const int nhi = c < 64 ? probe(c) : hi;
+    if (c < 64 && nhi == nlo) return nhi;  // the first probe at or above the bound is the answer
+    lo = nlo;
+    hi = nhi;
   }
   return lo;
 }
@@ -182,19 +194,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdParams p, in
   const int qs_min = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
   const int qs_max = max(max(s_red[4], s_red[5]), max(s_red[6], s_red[7]));
   const int qd_max = min(max(max(s_red[8], s_red[9]), max(s_red[10], s_red[11])), p.D - 1);
-  if (tid < BMAXG) {
+  // range of group e, one wave per group (e = wave, wave + 4, ...)
+  for (int e = wave; e < BMAXG; e += 4) {
     int a = 0, b = 0;
     if (qs_max >= 0) {
-      if (tid == 0) { a = 0; b = min(qs_max + 1, p.N); }
-      else if (tid <= qd_max) {
+      if (e == 0) { a = 0; b = min(qs_max + 1, p.N); }
+      else if (e <= qd_max) {
         int g0, g1;
-        group_rows(p, tid, g0, g1);
-        a = lower_row(p.start, g0, g1, qs_min);
-        b = upper_row(p.start, g0, g1, qs_max);
+        group_rows(p, e, g0, g1);
+        a = find_row_wave<false>(p.start, g0, g1, qs_min);
+        b = find_row_wave<true>(p.start, a, g1, qs_max);
       }
     }
-    s_rng[2 * tid] = a;
-    s_rng[2 * tid + 1] = b;
+    if (lane == 0) {
+      s_rng[2 * e] = a;
+      s_rng[2 * e + 1] = b;
+    }
   }
   __syncthreads();
 
@@ -442,19 +457,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(AttnBwdParams p, i
   }
 
   // query ranges per group that can see these keys, within [q_begin, q_end)
-  if (tid < BMAXG) {
+  // query rows of group e that can see these keys, one wave per group (e = wave, wave + 4, ...)
+  const int s_lo = p.start[kr0], s_hi = p.start[kr1 - 1];
+  for (int e = wave; e < BMAXG; e += 4) {
     int a = 0, b = 0;
-    if (tid < p.D && tid >= ke) {
+    if (e < p.D && e >= ke) {
       int g0, g1;
-      group_rows(p, tid, g0, g1);
-      const int s_lo = p.start[kr0], s_hi = p.start[kr1 - 1];
-      a = lower_row(p.start, g0, g1, s_lo);
-      b = ke == 0 ? g1 : upper_row(p.start, g0, g1, s_hi);
+      group_rows(p, e, g0, g1);
+      a = find_row_wave<false>(p.start, g0, g1, s_lo);
+      b = ke == 0 ? g1 : find_row_wave<true>(p.start, a, g1, s_hi);
       a = max(a, p.q_begin);
       b = min(b, p.q_end);
     }
-    s_rng[2 * tid] = a;
-    s_rng[2 * tid + 1] = max(a, b);
+    if (lane == 0) {
+      s_rng[2 * e] = a;
+      s_rng[2 * e + 1] = max(a, b);
+    }
   }
   __syncthreads();
   // this workgroup's share of the key tile's query tiles (in group order)
