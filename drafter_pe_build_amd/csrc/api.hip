@@ -752,8 +752,10 @@ pe_status run_lm_argmax(const pe_drafter_dims* dims, const pe_drafter_weights* w
   gp.epi.logits = logits;
   gp.epi.part_top2 = lw.top2;
   const int used = launch_gemm(gp, bf, stream);
-  // the two leading tokens of each row, scored again in fp32 from x
-  launch_argmax_rescore(lw.top2, used, n, x, d, w->final_gain, dims->eps, w->w_lm, d, bf, tokens, stream);
+  // the two leading tokens of each row scored again in fp32 from x, unless
+  // the logits came from the hi + lo operand (then the largest is the token)
+  const int rescore = lm_head_exact(n, d, bf, w->final_gain) ? 0 : 1;
+  launch_argmax_rescore(lw.top2, used, n, x, d, w->final_gain, dims->eps, w->w_lm, d, bf, tokens, rescore, stream);
   return launched();
 }
 

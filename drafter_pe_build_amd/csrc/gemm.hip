@@ -124,11 +124,12 @@ struct CopyStage {
 // barrier between the gain copy and its use.  With p.nrm.defer the rows are
 // written as x * g and each (row, segment)'s 1 / rms goes to the float array
 // after the gains (index row * segs + seg), for the contraction to apply.
-template <typename S, typename XT, int NC>
+template <typename S, typename XT, int NC, bool HL = false>
 struct NormStage {
   static constexpr int CI = 16 / sizeof(XT);  // elements per chunk
   static constexpr int GN = 3;                // gain chunks per thread per round
   static_assert(sizeof(S) <= sizeof(XT), "the operand type is never wider than the input");
+  static_assert(!HL || (sizeof(S) == 2 && sizeof(XT) == 4), "a remainder row: float input, bf16 operand");
   u32x4 raw[NC];
   f32x4 gt[GN];
   __device__ void load_pair(const GemmParams& p, int pr) {
@@ -197,6 +198,13 @@ struct NormStage {
         } else {
           u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
           *reinterpret_cast<u32x2*>(dst + e0 * 2) = w;
+          if constexpr (HL) {
+            // the remainder y - bf16(y) (exact in fp32) rounded to bf16, in row + 8
+            float lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lo[e] = y[e] - bf2f((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+            *reinterpret_cast<u32x2*>(dst + 8 * xp + e0 * 2) = u32x2{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+          }
         }
       }
     }
@@ -745,7 +753,7 @@ void lm_argmax_stream_kernel(GemmParams p) {
 // first weight batch is requested right after the rows' reads, so the
 // staging hides under its round trip.  Two waves per SIMD (256 registers per
 // lane), one workgroup per CU.
-template <typename S, int NWV, int UB, bool NORM, bool LSE>
+template <typename S, int NWV, int UB, bool NORM, bool LSE, bool HL>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2)))
 void lm_head_sweep_kernel(GemmParams p) {
   constexpr int CH = Storage<S>::CH;
@@ -764,6 +772,9 @@ void lm_head_sweep_kernel(GemmParams p) {
   const int nblk = (int)blockIdx.x < nfb ? (nfb - 1 - (int)blockIdx.x) / G + 1 : 0;
   const int nitems = nblk * nbat;
   const bool xr = r < M;
+  // HL (M <= 8): columns 8..15 of the activation operand hold the remainder
+  // of each normalised row, so every logit is the sum of two products
+  const bool xop = HL ? (r & 7) < M : xr;
   // this wave's last step (step 0 for a wave without steps): slots past the
   // end re-read it, so every load stays inside the block
   const int vlast = wave < nsteps ? wave + NWV * ((nsteps - 1 - wave) / NWV) : 0;
@@ -776,19 +787,21 @@ void lm_head_sweep_kernel(GemmParams p) {
   };
   u32x4 wa[UB], wb[UB];
   const int xp = K * (int)sizeof(S) + 16;  // LDS row pitch, bytes
+  const int nxr = HL ? 16 : M;             // staged rows (HL: the remainders in rows 8..)
   {
-    std::conditional_t<NORM, NormStage<S, float, norm_chunks<float>()>, CopyStage<S, 8>> stage;
+    static_assert(!HL || NORM, "the remainder rows come from the norm");
+    std::conditional_t<NORM, NormStage<S, float, norm_chunks<float>(), HL>, CopyStage<S, 8>> stage;
     if constexpr (NORM) stage.load(p, wave); else stage.load(p);
     if (nitems > 0) load(wa, 0);
-    // LDS: M rows at pitch xp, the zero chunk, then the gains of a norm
-    if constexpr (NORM) stage.finish(p, xs, xp, xs + M * xp + 16, wave, NWV); else stage.finish(p, xs, xp);
+    // LDS: the rows at pitch xp, the zero chunk, then the gains of a norm
+    if constexpr (NORM) stage.finish(p, xs, xp, xs + nxr * xp + 16, wave, NWV); else stage.finish(p, xs, xp);
   }
   clear_ints(p);
-  const char* xzero = xs + M * xp;
-  if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(xs + M * xp) = zero4();
+  const char* xzero = xs + nxr * xp;
+  if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(xs + nxr * xp) = zero4();
   __syncthreads();
-  const char* xrow = xr ? xs + r * xp + g * 16 : xzero;
-  const int xstep = xr ? STEP * (int)sizeof(S) : 0;
+  const char* xrow = xop ? xs + r * xp + g * 16 : xzero;
+  const int xstep = xop ? STEP * (int)sizeof(S) : 0;
 
   RowRed rr = RowRed::init();  // argmax or (LSE) log-sum-exp state of row r over this lane's features
   const int tgt = (LSE && p.epi.targets && xr) ? p.epi.targets[r] : -1;
@@ -809,6 +822,10 @@ void lm_head_sweep_kernel(GemmParams p) {
         f32x4 t = red[bi & 1][0][lane];
 #pragma unroll
         for (int w = 1; w < NWV; ++w) t += red[bi & 1][w][lane];
+        if constexpr (HL) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) t[j] += __shfl_down(t[j], 8, 64);  // + the remainder column r + 8
+        }
         if (xr) {
           const int b = (int)blockIdx.x + G * bi;
 #pragma unroll
@@ -1028,7 +1045,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p, int n_ft,
 template <typename S>
 __global__ __launch_bounds__(256) void argmax_rescore_kernel(const u32x4* part, int P, int M, const float* x,
                                                              int64_t ldx, const float* gain, float eps,
-                                                             const char* W, int K, int32_t* tokens) {
+                                                             const char* W, int K, int32_t* tokens, int rescore) {
   constexpr int CH = Storage<S>::CH;  // elements per 16-byte chunk
   constexpr int STEP = 4 * CH;        // elements per packed 1 KB step of a 16-row block
   constexpr int NPRE = 2;             // chunks per thread held from before the merge (K <= 512 CH)
@@ -1039,11 +1056,12 @@ __global__ __launch_bounds__(256) void argmax_rescore_kernel(const u32x4* part, 
   const int nch = K / CH;
   const float* xr = x + (int64_t)m * ldx;
   // the row and its gains first, so that their loads overlap the partials'
+  // (not when the logits were exact: the largest is then the token)
   f32x4 xv[NPRE][CH / 4], gv[NPRE][CH / 4];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < NPRE; ++c) {
-    const int ch = tid + 256 * c;
+    const int ch = rescore ? tid + 256 * c : nch;
 #pragma unroll
     for (int q = 0; q < CH / 4; ++q) {
       xv[c][q] = ch < nch ? *reinterpret_cast<const f32x4*>(xr + ch * CH + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1083,6 +1101,10 @@ __global__ __launch_bounds__(256) void argmax_rescore_kernel(const u32x4* part, 
   RowRed best = RowRed::init();
   for (int w = 0; w < 4; ++w) best.merge_packed(sw[w]);
   const int c1 = best.i, c2 = best.i2;
+  if (!rescore) {
+    if (tid == 0) tokens[m] = c1 == 0x7fffffff ? -1 : c1;
+    return;
+  }
   const bool has1 = c1 != 0x7fffffff, has2 = c2 != 0x7fffffff;
   // the two candidates' products with x * g
   const int steps = K / STEP;
@@ -1132,7 +1154,7 @@ __global__ __launch_bounds__(256) void argmax_rescore_kernel(const u32x4* part, 
 }
 
 void launch_argmax_rescore(const u32x4* part, int P, int M, const float* x, int64_t ldx, const float* gain,
-                           float eps, const void* W, int K, int w_bf16, int32_t* tokens, hipStream_t s) {
+                           float eps, const void* W, int K, int w_bf16, int32_t* tokens, int rescore, hipStream_t s) {
   const char* w = reinterpret_cast<const char*>(W);
   // workgroup b runs on XCD b % 8 and takes row (b % 8) * rpx + b / 8, so the
   // rows of one XCD are consecutive and share the lines of the tile-major
@@ -1140,10 +1162,10 @@ void launch_argmax_rescore(const u32x4* part, int P, int M, const float* x, int6
   const int rpx = (M + 7) / 8;
   if (w_bf16)
     hipLaunchKernelGGL(argmax_rescore_kernel<uint16_t>, dim3(8 * rpx), dim3(256), 0, s, part, P, M, x, ldx, gain, eps,
-                       w, K, tokens);
+                       w, K, tokens, rescore);
   else
     hipLaunchKernelGGL(argmax_rescore_kernel<float>, dim3(8 * rpx), dim3(256), 0, s, part, P, M, x, ldx, gain, eps,
-                       w, K, tokens);
+                       w, K, tokens, rescore);
 }
 
 // Log-sum-exp of each row from its P partial (maximum, sum of exp) pairs, merged
@@ -1522,26 +1544,47 @@ static GemmParams norm_first(const GemmParams& p, hipStream_t s, bool packed = f
 // The LM-head weight stream for M <= 16 rows (argmax or, LSE, log-sum-exp
 // partials): rows and their norm staged in LDS when they fit, else read from
 // global memory after a separate norm.  Returns the partial count.
+// Whether the LM head over M float rows normalised with `gain` (one segment
+// of K) runs with the remainder of the normalised rows as a second bf16
+// operand part (hi + lo, about 2^-17 relative): M <= 8, a row the norm
+// staging holds, a 16-byte aligned gain, and the 16 staged rows in LDS.
+// Those logits are exact to far below the argmax's 1e-2 gap, so the
+// argmax takes the largest without a re-score.
+bool lm_head_exact(int M, int K, int bf16, const float* gain) {
+  const size_t lds = (size_t)16 * ((size_t)K * 2 + 16) + 16 + (size_t)K * 4 + (size_t)M * 4;
+  return bf16 && M >= 1 && M <= 8 && K % 4 == 0 && K / 4 <= 64 * norm_chunks<float>() &&
+         (reinterpret_cast<uintptr_t>(gain) & 15) == 0 && lds <= (size_t)kLmSweepXLds;
+}
+
 template <typename S, bool LSE>
 static int launch_lm_stream(const GemmParams& p0, bool norm, bool norm_fits, bool xf32, size_t lds, hipStream_t s) {
   const int grid = gemm_argmax_partials(p0.M, p0.N);
+  if constexpr (sizeof(S) == 2) {
+    if (norm && xf32 && p0.nrm.segs == 1 && !p0.nrm.defer && lm_head_exact(p0.M, p0.K, 1, p0.nrm.gain)) {
+      const size_t lds_hl = (size_t)16 * ((size_t)p0.K * 2 + 16) + 16 + (size_t)p0.K * 4 + (size_t)p0.M * 4;
+      allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, true, LSE, true>>(kLmSweepXLds);
+      hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, true, LSE, true>), dim3(grid),
+                         dim3(64 * kLmSweepW), lds_hl, s, p0);
+      return grid;
+    }
+  }
   if (lds <= (size_t)kLmSweepXLds && norm_fits && (!norm || xf32)) {
     if (norm) {
-      allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, true, LSE>>(kLmSweepXLds);
-      hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, true, LSE>), dim3(grid), dim3(64 * kLmSweepW),
-                         lds, s, p0);
+      allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, true, LSE, false>>(kLmSweepXLds);
+      hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, true, LSE, false>), dim3(grid),
+                         dim3(64 * kLmSweepW), lds, s, p0);
     } else {
-      allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE>>(kLmSweepXLds);
-      hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE>), dim3(grid), dim3(64 * kLmSweepW),
-                         lds, s, p0);
+      allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE, false>>(kLmSweepXLds);
+      hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE, false>), dim3(grid),
+                         dim3(64 * kLmSweepW), lds, s, p0);
     }
     return grid;
   }
   const GemmParams p = norm ? norm_first<S>(p0, s, false) : p0;
   if (lds <= (size_t)kLmSweepXLds) {
-    allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE>>(kLmSweepXLds);
-    hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE>), dim3(grid), dim3(64 * kLmSweepW),
-                       lds, s, p);
+    allow_lds<&lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE, false>>(kLmSweepXLds);
+    hipLaunchKernelGGL((lm_head_sweep_kernel<S, kLmSweepW, kLmSweepU, false, LSE, false>), dim3(grid),
+                       dim3(64 * kLmSweepW), lds, s, p);
   } else {
     const dim3 block(64 * kLmNFB * kLmKS);
     hipLaunchKernelGGL((lm_argmax_stream_kernel<S, kLmNFB, kLmKS, kLmU, false, false, LSE>), dim3(grid), block, 0, s,

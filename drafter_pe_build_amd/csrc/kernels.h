@@ -180,9 +180,14 @@ int gemm_big_partials(int N);
 //   z = (sum_k W[c][k] x[m][k] g[k]) / sqrt(mean_k x[m][k]^2 + eps),
 // and the larger (lower index on a tie) is the token.  x: [M, K] float32
 // rows (stride ldx), W: packed [N, K] weights of storage type (bf16 when
-// w_bf16).
+// w_bf16).  rescore 0: the partials hold exact logits (lm_head_exact), and
+// the largest is the token as it is.
 void launch_argmax_rescore(const u32x4* part, int P, int M, const float* x, int64_t ldx, const float* gain,
-                           float eps, const void* W, int K, int w_bf16, int32_t* tokens, hipStream_t s);
+                           float eps, const void* W, int K, int w_bf16, int32_t* tokens, int rescore, hipStream_t s);
+// Whether the LM head over M float rows with a folded norm (gain, one
+// segment of K) runs on the bf16 hi + lo operand (logits exact to about
+// 2^-17 relative; see gemm.hip).
+bool lm_head_exact(int M, int K, int bf16, const float* gain);
 // lse[m] = log sum_v exp(y[m][v]) from the P partials of EPI_LSE, and
 // loss[m] = lse[m] - tgt[m] (0 where targets[m] is outside [0, N)); lse or
 // loss may be null.

@@ -410,10 +410,14 @@ pe_status pe_draft_layer_workspace(const pe_drafter_dims* dims, int32_t T, int32
  * drafting": the LM head predicts the draft tokens t_1..t_K of every request
  * in the same pass.  For each of the n rows of x [n, hidden] f32:
  *   z = w_lm RMSNorm(x, final_gain);  tokens[i] = lowest index of max(z)
- * The contraction runs on the normalised row rounded to the storage type;
- * the row's two leading logits are then computed again in fp32 from the
- * unrounded row, and the larger of those two (lower index on a tie) is the
- * token.  logits [n, vocab] f32 (the contraction's values) is written when
+ * bf16, n <= 8 (the decode step of one request): the contraction runs on
+ * the normalised row as two bf16 parts, the rounded row and its remainder,
+ * so every logit is within about 2^-17 of the unrounded row's, and the
+ * largest (lower index on a tie) is the token.  Otherwise the contraction
+ * runs on the normalised row rounded to the storage type, the row's two
+ * leading logits are computed again in fp32 from the unrounded row, and
+ * the larger of those two (lower index on a tie) is the token.
+ * logits [n, vocab] f32 (the contraction's values) is written when
  * non-NULL (validation runs); the fast path never materialises logits.
  * Uses weights->final_gain (16-byte aligned) and w_lm.
  * Workspace: pe_lm_head_argmax_workspace.
