@@ -152,6 +152,16 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   const int seg = lin / tps, tile = lin % tps;
   const int qbase = seg * p.q_per_seg + tile * QPW;
   const int nq = min(QPW, p.q_per_seg - tile * QPW);
+  // reads that depend on nothing below go out with the query metadata: the
+  // segment's first key row and each column's query row (an indexed list in
+  // the decode layer)
+  const int seg_base = p.seg_kv_base[seg];
+  int qrow_c[CBLK];
+#pragma unroll
+  for (int cb = 0; cb < CBLK; ++cb) {
+    const int cqc = (wave * (CBLK * 16) + cb * 16 + r) / G;
+    qrow_c[cb] = cqc < nq ? (p.q_rows ? p.q_rows[qbase + cqc] : qbase + cqc) : -1;
+  }
 
   // ---- per-query metadata, chain lengths, exclusive scan of the lengths.
   // The chain walk keeps its rows in the last K buffer (free until the tile
@@ -214,7 +224,6 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
   }
   __syncthreads();
   const int n_anc = (sp == 0) ? n_anc_all : 0;
-  const int seg_base = p.seg_kv_base[seg];
 
   // ---- this split's prefix range [kbeg, kend]: piece sp of ncut equal
   // pieces of the tile's own range (plan), or of split_len keys
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(256, (sizeof(S) == 2 || DH == 64) ? 2 : 1) void att
       lo = min(lo, climit[cb]);
       hi = max(hi, climit[cb]);
     }
-    const int qrow = cact[cb] ? (p.q_rows ? p.q_rows[qbase + cq[cb]] : qbase + cq[cb]) : -1;
+    const int qrow = qrow_c[cb];
 #pragma unroll
     for (int t = 0; t < NST; ++t)
       qreg[cb][t] = (qrow >= 0) ? ld16(Q + (int64_t)qrow * p.q_stride + (int64_t)hh[cb] * DH + t * STEP + g * CH)
