@@ -6,7 +6,8 @@
 // A workgroup of 2 x WN waves owns an output tile of BM activation rows x BN
 // features; each wave a (BM/2) x (BN/WN) sub-tile accumulated in registers
 // (112 or 128 rows x 64 features for the 224/256 x 128 tiles with four
-// waves: up to 128 accumulator registers per lane, two waves per SIMD).  Both
+// waves: up to 128 accumulator registers per lane; 112 x 80 and 140 for the
+// LM head's 224 x 160; two waves per SIMD).  Both
 // operands go through LDS in a ring of D stages, one 32-wide k-step each,
 // copied by global_load_lds_dwordx4 without passing through registers; D - 1
 // k-steps are in flight while one is multiplied:
@@ -50,11 +51,12 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   constexpr int WBYTES = WB * 1024;    // one weight matrix, one k-step
   constexpr int XOFF = WBYTES * (DUAL ? 2 : 1);
   constexpr int STAGE = XOFF + BM * 64;
-  constexpr int WI = WB / NW;          // weight copies per wave per k-step (per matrix)
+  constexpr int WI = (WB + NW - 1) / NW;  // weight copies per wave per k-step (per matrix; the
+                                         // last block repeats when NW does not divide WB)
   constexpr int XI = (BM / 16 + NW - 1) / NW;  // activation copies per wave per k-step (the
                                                // last group repeats when NW does not divide BM / 16)
   constexpr int PT = WI * (DUAL ? 2 : 1) + XI;  // vector-memory operations per wave per k-step
-  static_assert(BM % 32 == 0 && BN % 64 == 0 && WB % NW == 0, "tile shape");
+  static_assert(BM % 32 == 0 && BN % (16 * WN) == 0, "tile shape");
   static_assert(!ARGMAX || D * STAGE >= WN * BM * 16, "row-reduction lists fit in the ring");
   extern __shared__ __attribute__((aligned(16))) char lds[];  // D stages
 
@@ -82,7 +84,7 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   const char* w2src[DUAL ? WI : 1];
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
-    const int64_t off = ((int64_t)min(n0 / 16 + wave + NW * i, nfb - 1) * ksteps + kbeg) * 1024 + lane * 16;
+    const int64_t off = ((int64_t)min(n0 / 16 + min(wave + NW * i, WB - 1), nfb - 1) * ksteps + kbeg) * 1024 + lane * 16;
     wsrc[i] = reinterpret_cast<const char*>(p.W) + off;
     if constexpr (DUAL) w2src[i] = reinterpret_cast<const char*>(p.W2) + off;
   }
@@ -105,8 +107,8 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
     char* st = lds + (t % D) * STAGE;
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
-      copy16_to_lds(wsrc[i] + (int64_t)t * 1024, st + (wave + NW * i) * 1024);
-      if constexpr (DUAL) copy16_to_lds(w2src[i] + (int64_t)t * 1024, st + WBYTES + (wave + NW * i) * 1024);
+      copy16_to_lds(wsrc[i] + (int64_t)t * 1024, st + min(wave + NW * i, WB - 1) * 1024);
+      if constexpr (DUAL) copy16_to_lds(w2src[i] + (int64_t)t * 1024, st + WBYTES + min(wave + NW * i, WB - 1) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < XI; ++i)
@@ -297,7 +299,13 @@ static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
 
 // Tile shapes: 256 or 224 rows (whichever pads M less: 448 = 2 x 224,
 // 896 = 4 x 224) x 128 features, four waves and a three-stage ring, for
-// single contractions and the LM head.  The template also takes the gate/up
+// single contractions and the LM head.  The LM head on 224-row tiles takes
+// 160 features: the 448-row batch is then 2 x 1,257 workgroups, 4.91 rounds
+// of the 512 resident slots, where 128 features give 2 x 1,571 = 6.14
+// rounds whose last one runs 86 % empty (c=64 LM stage 539 -> 481 us).  Its
+// ten weight blocks per k-step take three copies per wave, waves 2 and 3
+// copying the last block again (the same bytes to the same place).  The
+// template also takes the gate/up
 // pair (DUAL: two weight streams, two accumulator sets), which measured
 // slower than the 128 x 64 register-fed tiles of gemm.hip and is not
 // dispatched.  Contractions with too few tiles to give every CU two
@@ -404,7 +412,7 @@ int launch_gemm_big(const GemmParams& p, hipStream_t s) {
                   : launch_big<256, 128, 2, 3, false, true, false, false, true>(p, 1, s);
     }
     if (p.x_packed)
-      return r224 ? launch_big<224, 128, 2, 3, false, true, false, true>(p, 1, s)
+      return r224 ? launch_big<224, 160, 2, 3, false, true, false, true>(p, 1, s)
                   : launch_big<256, 128, 2, 3, false, true, false, true>(p, 1, s);
     return r224 ? launch_big<224, 128, 2, 3, false, true, false>(p, 1, s)
                 : launch_big<256, 128, 2, 3, false, true, false>(p, 1, s);
@@ -424,8 +432,6 @@ int launch_gemm_big(const GemmParams& p, hipStream_t s) {
   hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, q, splits);
   return 0;
 }
-
-int gemm_big_partials(int N) { return (N + 127) / 128; }
 
 int64_t gemm_split_bytes(int T, int nmax) {
   if (T < 128) return 0;

@@ -160,7 +160,8 @@ int launch_gemm(const GemmParams& p, int bf16, hipStream_t s);
 // Upper bound of P for an argmax GEMM of this shape.
 int gemm_argmax_partials(int M, int N);
 // Large-M bf16 contraction through LDS-staged 256-row tiles (gemm_big.hip):
-// EPI_ARGMAX returns the partial count P = gemm_big_partials(N); other
+// EPI_ARGMAX returns the partial count P (one per feature tile, at most
+// gemm_argmax_partials(M, N)); other
 // epilogues return 0 when launched with a K split (p.split_ws), -1 when the
 // shape does not call for one (nothing launched).
 int launch_gemm_big(const GemmParams& p, hipStream_t s);
@@ -172,7 +173,6 @@ int gemm_big_splits(const GemmParams& p, int segs = 1);
 // Bytes of K-split workspace worth giving a large-M stage (T rows, widest
 // contraction output nmax).
 int64_t gemm_split_bytes(int T, int nmax);
-int gemm_big_partials(int N);
 
 // Greedy token of each row: the P partial top-2 lists merged into the row's
 // two largest logits (lowest index first among equal values), whose logits
