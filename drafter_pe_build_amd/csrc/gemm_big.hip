@@ -302,9 +302,12 @@ static int launch_big(const GemmParams& p, int splits, hipStream_t s) {
 // single contractions and the LM head.  The LM head on 224-row tiles takes
 // 160 features: the 448-row batch is then 2 x 1,257 workgroups, 4.91 rounds
 // of the 512 resident slots, where 128 features give 2 x 1,571 = 6.14
-// rounds whose last one runs 86 % empty (c=64 LM stage 539 -> 481 us).  Its
-// ten weight blocks per k-step take three copies per wave, waves 2 and 3
-// copying the last block again (the same bytes to the same place).  The
+// rounds whose last one runs 86 % empty (c=64 LM stage 539 -> 481 us); the
+// fused loss over 7,794 rows takes the same tile for its smaller L2->LDS
+// copy traffic per product (10.2 -> 9.3 ms).  Its ten weight blocks per
+// k-step take three copies per wave, waves 2 and 3 copying the last block
+// again (the same bytes to the same place).  The K-split projections keep
+// 128 features (160 measured slower: fewer workgroups).  The
 // template also takes the gate/up
 // pair (DUAL: two weight streams, two accumulator sets), which measured
 // slower than the 128 x 64 register-fed tiles of gemm.hip and is not
@@ -406,7 +409,7 @@ int launch_gemm_big(const GemmParams& p, hipStream_t s) {
   if (epi_rowred(p.epi.kind)) {
     if (p.epi.kind == EPI_LSE) {
       if (p.x_packed)
-        return r224 ? launch_big<224, 128, 2, 3, false, true, false, true, true>(p, 1, s)
+        return r224 ? launch_big<224, 160, 2, 3, false, true, false, true, true>(p, 1, s)
                     : launch_big<256, 128, 2, 3, false, true, false, true, true>(p, 1, s);
       return r224 ? launch_big<224, 128, 2, 3, false, true, false, false, true>(p, 1, s)
                   : launch_big<256, 128, 2, 3, false, true, false, false, true>(p, 1, s);
