@@ -627,14 +627,10 @@ void lm_argmax_stream_kernel(GemmParams p) {
   const int r = lane & 15, g = lane >> 4;
   const int M = p.M, N = p.N, K = p.K;
   const int nsteps = K / STEP;
-#ifndef PE_LM_INTERLEAVE
-#define PE_LM_INTERLEAVE 0
-#endif
-  // k-steps of this wave: a contiguous share, or (interleaved) every KS-th
-  // step from ks, so that a block's waves read one contiguous run together
-  const int s0 = PE_LM_INTERLEAVE ? ks : nsteps * ks / KS;
-  const int sst = PE_LM_INTERLEAVE ? KS : 1;
-  const int cnt = PE_LM_INTERLEAVE ? (nsteps - ks + KS - 1) / KS : nsteps * (ks + 1) / KS - s0;
+  // k-steps of this wave: a contiguous share
+  const int s0 = nsteps * ks / KS;
+  const int sst = 1;
+  const int cnt = nsteps * (ks + 1) / KS - s0;
   const int nfb = (N + 15) >> 4;
   const int ntiles = (nfb + NFB - 1) / NFB;
   const bool xr = r < M;

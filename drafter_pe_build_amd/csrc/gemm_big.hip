@@ -144,31 +144,21 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
                                                                     : R_ * 64 + 16 * (g ^ ((R_ >> 1) & 3)))); \
     }                                                                                                    \
   }
-#ifndef PE_BIG_SCHED
-#define PE_BIG_SCHED
-#endif
-#ifndef PE_BIG_SPLIT
-#define PE_BIG_SPLIT 0
-#endif
-  // FH: weight blocks whose products run before the barrier (the rest hide the
-  // operand reads of the next step)
-  constexpr int FH = PE_BIG_SPLIT ? FW / 2 : FW;
-#define PE_BIG_MMA(CUR, F0, F1)                                                                          \
-  _Pragma("unroll") for (int f = F0; f < F1; ++f)                                                        \
+#define PE_BIG_MMA(CUR)                                                                                  \
+  _Pragma("unroll") for (int f = 0; f < FW; ++f)                                                         \
     _Pragma("unroll") for (int q = 0; q < RW; ++q) {                                                     \
       mma16(acc[f][q], fa[CUR][f], fb[CUR][q], uint16_t());                                              \
       if constexpr (DUAL) mma16(acc2[f][q], fa2[CUR][f], fb[CUR][q], uint16_t());                        \
     }
 #define PE_BIG_ITER(T, CUR, NXT)                                                                         \
   {                                                                                                      \
-    PE_BIG_MMA(CUR, 0, FH)                                                                               \
+    PE_BIG_MMA(CUR)                                                                                      \
     if ((T) + 1 < nsteps) {                                                                              \
       if ((T) + D - 1 < nsteps) wait_vm<PT * (D - 2)>(); else wait_vm<0>();                              \
       __syncthreads();                                                                                   \
       if ((T) + D < nsteps) issue((T) + D);                                                              \
       PE_BIG_FRAGS((T) + 1, NXT)                                                                         \
     }                                                                                                    \
-    if constexpr (FH < FW) { PE_BIG_SCHED PE_BIG_MMA(CUR, FH, FW) }                                      \
   }
 #pragma unroll
   for (int t = 0; t < D; ++t)
