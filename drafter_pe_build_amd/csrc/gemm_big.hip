@@ -253,23 +253,142 @@ void gemm_big_kernel(GemmParams p, int n_ft, int n_mt) {
   }
 }
 
-// Sum of the K-split partial products in split order (deterministic), then
-// the contraction's epilogue; one thread per four features of one row.
-template <bool DUAL>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int splits) {
-  const int M = p.M, N = p.N;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)M * (N / 4)) return;
-  const int m = (int)(i / (N / 4)), n = (int)(i % (N / 4)) * 4;
-  f32x4 y = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    // a share of a deferred-scale operand lies in one segment: scale it by the row's 1 / rms there
-    const float sc = p.xinv ? p.xinv[(int64_t)m * p.xinv_segs + (p.nsplit_k ? p.split_seg[s] : 0)] : 1.f;
-    y += *reinterpret_cast<const f32x4*>(p.split_ws + ((int64_t)s * M + m) * N + n) * sc;
-    if constexpr (DUAL) y2 += *reinterpret_cast<const f32x4*>(p.split_ws + ((int64_t)(splits + s) * M + m) * N + n);
+// The epilogue of features n..n+3 of row m (n a multiple of 4) for the kinds
+// a K split finishes (fc, QKV, residual) with 8- or 16-byte accesses, in
+// three steps so that the reads go out early: the row's metadata (meta: the
+// token id, the residual row or the KV slot; skip: a rejected row), the
+// addend (embedding or residual elements, which depend on the metadata but
+// not on the sums), then the store.  The values equal epi_store's element by
+// element; other kinds and unaligned operands (vec false) take epi_store.
+struct Reduce4 {
+  int meta;
+  bool skip;
+  f32x4 add;
+};
+__device__ __forceinline__ void reduce_meta(const Epi& e, int m, Reduce4& t) {
+  t.meta = m;
+  t.skip = false;
+  t.add = f32x4{0.f, 0.f, 0.f, 0.f};
+  switch (e.kind) {
+    case EPI_FC:
+      t.skip = e.rejected && e.rejected[m];
+      t.meta = e.ids[m];
+      break;
+    case EPI_RESID:
+      t.meta = e.res_rows ? e.res_rows[m] : m;
+      break;
+    case EPI_QKV:
+      t.meta = e.slots[m];
+      break;
+    default:
+      break;
   }
+}
+__device__ __forceinline__ void reduce_addend(const Epi& e, int n, Reduce4& t) {
+  if (e.kind == EPI_FC) {
+    if (!t.skip && t.meta >= 0 && t.meta < e.embed_rows) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(e.embed) + (int64_t)t.meta * e.ld_out + n);
+      t.add = f32x4{bf2f((uint16_t)w.x), bf2f((uint16_t)(w.x >> 16)), bf2f((uint16_t)w.y), bf2f((uint16_t)(w.y >> 16))};
+    }
+  } else if (e.kind == EPI_RESID) {
+    t.add = *reinterpret_cast<const f32x4*>(e.res + (int64_t)t.meta * e.ld_res + n);
+  }
+}
+__device__ __forceinline__ void reduce_store4(const Epi& e, int m, int n, const f32x4& y, const Reduce4& t) {
+  switch (e.kind) {
+    case EPI_FC:
+      if (!t.skip) *reinterpret_cast<f32x4*>(e.out_f32 + (int64_t)m * e.ld_out + n) = y + t.add;
+      return;
+    case EPI_RESID:
+      *reinterpret_cast<f32x4*>(e.out_f32 + (int64_t)m * e.ld_out + n) = y + t.add;
+      return;
+    case EPI_QKV: {
+      const u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      if (n < e.q_cols) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(e.out_s) + (int64_t)m * e.q_cols + n) = w;
+        return;
+      }
+      const int slot = t.meta;
+      if (slot < 0 || slot >= e.kv_rows) return;
+      int c = n - e.q_cols;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(c < e.kv_cols ? e.k_cache : e.v_cache);
+      if (c >= e.kv_cols) c -= e.kv_cols;
+      *reinterpret_cast<u32x2*>(dst + (int64_t)slot * e.kv_cols + c) = w;
+      return;
+    }
+    default:
 #pragma unroll
-  for (int j = 0; j < 4; ++j) epi_store<uint16_t>(p.epi, m, n + j, y[j], y2[j]);
+      for (int j = 0; j < 4; ++j) epi_store<uint16_t>(e, m, n + j, y[j], 0.f);
+      return;
+  }
+}
+
+// Whether reduce_store4 may take the vector path for this epilogue.
+static bool reduce_vec_ok(const Epi& e) {
+  auto al = [](const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; };
+  switch (e.kind) {
+    case EPI_FC:
+      return e.ld_out % 4 == 0 && al(e.out_f32, 16) && al(e.embed, 8);
+    case EPI_RESID:
+      return e.ld_out % 4 == 0 && e.ld_res % 4 == 0 && al(e.out_f32, 16) && al(e.res, 16);
+    case EPI_QKV:
+      return e.q_cols % 4 == 0 && e.kv_cols % 4 == 0 && al(e.out_s, 8) && al(e.k_cache, 8) && al(e.v_cache, 8);
+    default:
+      return false;
+  }
+}
+
+// Sum of the K-split partial products in split order (deterministic), then
+// the contraction's epilogue; one thread per four features of one row.  The
+// share count is a template argument, so the partials of every share (and
+// their row scales) are loaded before the first add: one round trip for all
+// shares instead of one each.
+template <int NS>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p, int vec) {
+  const int M = p.M, N = p.N;
+  const int i = blockIdx.x * 256 + threadIdx.x;  // M * N / 4 < 2^31 (checked by big_split_plan)
+  if (i >= M * (N / 4)) return;
+  const int m = i / (N / 4), n = (i % (N / 4)) * 4;
+  Reduce4 t;
+  if (vec) reduce_meta(p.epi, m, t);
+  f32x4 part[NS];
+  float sc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    // a share of a deferred-scale operand lies in one segment: scale it by the row's 1 / rms there
+    sc[s] = p.xinv ? p.xinv[(int64_t)m * p.xinv_segs + (p.nsplit_k ? p.split_seg[s] : 0)] : 1.f;
+    part[s] = *reinterpret_cast<const f32x4*>(p.split_ws + ((int64_t)s * M + m) * N + n);
+  }
+  if (vec) reduce_addend(p.epi, n, t);
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) y += part[s] * sc[s];
+  if (vec) {
+    reduce_store4(p.epi, m, n, y, t);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) epi_store<uint16_t>(p.epi, m, n + j, y[j], 0.f);
+  }
+}
+
+template <int NS>
+static void launch_reduce_ns(const GemmParams& q, int64_t n4, hipStream_t s) {
+  hipLaunchKernelGGL((splitk_reduce_kernel<NS>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, q,
+                     reduce_vec_ok(q.epi) ? 1 : 0);
+}
+
+static void launch_splitk_reduce(const GemmParams& q, int splits, hipStream_t s) {
+  static_assert(kMaxSplitK == 8, "one instantiation per share count");
+  const int64_t n4 = (int64_t)q.M * (q.N / 4);
+  switch (splits) {
+    case 2: launch_reduce_ns<2>(q, n4, s); break;
+    case 3: launch_reduce_ns<3>(q, n4, s); break;
+    case 4: launch_reduce_ns<4>(q, n4, s); break;
+    case 5: launch_reduce_ns<5>(q, n4, s); break;
+    case 6: launch_reduce_ns<6>(q, n4, s); break;
+    case 7: launch_reduce_ns<7>(q, n4, s); break;
+    default: launch_reduce_ns<8>(q, n4, s); break;  // big_split_plan gives 2..kMaxSplitK
+  }
 }
 
 template <int BM, int BN, int WN, int STAGES, bool DUAL, bool ARGMAX, bool SPLIT, bool PX = false, bool LSE = false>
@@ -370,7 +489,7 @@ static int big_split_plan(const GemmParams& p, int segs, int* bb, int* be, int* 
   // the gate/up pair measured faster on the 128 x 64 register-fed tiles
   // (67.6 us against 76 us split at 448 rows)
   if (p.epi.kind == EPI_SWIGLU || epi_rowred(p.epi.kind)) return 0;
-  if (!p.split_ws || p.N % 4) return 0;
+  if (!p.split_ws || p.N % 4 || (int64_t)p.M * p.N >= ((int64_t)1 << 31)) return 0;  // the reduce indexes in 32 bits
   const int ksteps = p.K / 32;
   if (segs > 1 && (ksteps % segs || segs > kMaxSplitK)) return 0;  // segments of whole k-steps
   const int bm = rows224(p.M) ? 224 : 256;
@@ -421,8 +540,7 @@ int launch_gemm_big(const GemmParams& p, hipStream_t s) {
     if (r224) launch_big<224, 128, 2, PE_SPLIT_STAGES, false, false, true>(q, splits, s);
     else launch_big<256, 128, 2, PE_SPLIT_STAGES, false, false, true>(q, splits, s);
   }
-  const int64_t n4 = (int64_t)p.M * (p.N / 4);
-  hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, q, splits);
+  launch_splitk_reduce(q, splits, s);
   return 0;
 }
 
