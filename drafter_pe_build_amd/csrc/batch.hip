@@ -7,25 +7,47 @@
 // hidden rows (target rows to their new positions, h_shared into every MASK
 // slot).  Section "KV cache": rejected rows get PADDING_SLOT_ID (-1).
 //
-// One workgroup per draft row: thread 0 finds the row's request by binary
-// search over cu_window (row r's request segment starts at cu_window[r] + r*K),
-// writes the integer metadata, and the whole workgroup copies the row's
-// 3*hidden hidden values with 16-byte loads and stores.
+// One workgroup per draft row: the first wave finds the row's request (row
+// r's request segment starts at cu_window[r] + r*K), thread 0 writes the
+// integer metadata, and the whole workgroup copies the row's 3*hidden hidden
+// values with 16-byte loads and stores.
 #include "kernels.h"
 
 namespace pe {
 
+// First request whose segment starts after row t (the starts increase
+// strictly with r), by the first wave: 64 evenly spaced probes per round,
+// whose ballot leaves the answer between two neighbouring probes; up to 64
+// requests take one round (the c=64 batch: one dependent read instead of
+// six of a binary search).
+__device__ int first_segment_after(const BatchParams& p, int t) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = p.R;
+  while (hi > lo) {
+    const int n = hi - lo;
+    if (n <= 64) {
+      const bool le = lane < n && p.cu_window[lo + lane] + (lo + lane) * p.K <= t;
+      return lo + __popcll(__ballot(le));
+    }
+    // probe i(l) = lo + n (l + 1) / 65, l = 0..63: increasing, inside [lo, hi)
+    auto probe = [&](int l) { return lo + (int)((int64_t)n * (l + 1) / 65); };
+    const int i = probe(lane);
+    const int c = __popcll(__ballot(p.cu_window[i] + i * p.K <= t));  // a prefix of the probes
+    const int nlo = c > 0 ? probe(c - 1) + 1 : lo;
+    const int nhi = c < 64 ? probe(c) : hi;
+    if (c < 64 && nhi == nlo) return nhi;
+    lo = nlo;
+    hi = nhi;
+  }
+  return lo;
+}
+
 __global__ __launch_bounds__(256) void build_draft_batch_kernel(BatchParams p) {
   __shared__ int s_src;   // hidden source row, -1 = h_shared, -2 = none
   const int t = blockIdx.x;
+  // largest r with cu_window[r] + r*K <= t (0 when none: a malformed cu_window)
+  const int r = p.R > 1 && threadIdx.x < 64 ? max(first_segment_after(p, t) - 1, 0) : 0;
   if (threadIdx.x == 0) {
-    // largest r with cu_window[r] + r*K <= t
-    int lo = 0, hi = p.R - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.cu_window[mid] + mid * p.K <= t) lo = mid; else hi = mid - 1;
-    }
-    const int r = lo;
     // every per-request value in one round trip, whichever the row needs
     const int w0 = p.cu_window[r], w1 = p.cu_window[r + 1];
     const int nrej_in = p.n_rej[r], base = p.kv_base[r], kvl = p.kv_len[r];

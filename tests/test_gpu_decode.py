@@ -218,6 +218,29 @@ def test_hidden_of_one_k_step(dtype, hidden):
     check_case("hidden %d %s" % (hidden, dtype), dims, W, c)
 
 
+def test_batch_build_many_requests():
+    # 300 requests, some with empty windows: the row's request is found in
+    # several rounds of 64 probes (up to 64 requests take one); the batch is
+    # compared bit for bit, the later stages are covered by the other cases
+    from drafter_pe_build_amd.step import DraftStep
+    dims = small_dims("bf16")
+    W = si.drafter_weights(dims, 25)
+    g = np.random.default_rng(25)
+    R = 300
+    Wn = g.integers(0, 5, R)
+    n_rej = np.array([g.integers(0, w + 1) for w in Wn])
+    c = si.decode_case(dims, 25, R=R, K=3, W=Wn, kv_len=g.integers(0, 20, R), n_rej=n_rej)
+    say("[batch R=300 K=3] pe_build_draft_batch")
+    st = DraftStep(dims, W, c)
+    rb = oracle_batch(dims, W, c)
+    st.build_batch()
+    torch.cuda.synchronize()
+    for k in BATCH_KEYS:
+        np.testing.assert_array_equal(st.batch[k].cpu().numpy(), rb[k], err_msg=k)
+    hid = bits(st.batch["draft_hidden"])
+    np.testing.assert_array_equal(hid, rb["draft_hidden"].view(hid.dtype))
+
+
 def test_single_draft_slot():
     dims = small_dims("bf16", hq=16, hkv=2)
     W = si.drafter_weights(dims, 13)
