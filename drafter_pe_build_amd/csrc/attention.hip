@@ -839,36 +839,66 @@ __global__ __launch_bounds__(256) void attn_combine_few_kernel(AttnParams p, int
   };
   const int ns = qh < nqh ? pieces_of(qh / p.Hq) : 1;
   if (qh < nqh && ns > 1) {
-    // loads in batches of U pieces (independent, in flight together); the
-    // sums still run over the pieces in order
-    constexpr int U = 8;
     const float* ml = p.part_ml + qh * 2;
-    const int64_t sml = nqh * 2, spo = nqh * DH;
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < ns; s0 += U) {
-      float t[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) t[u] = s0 + u < ns ? ml[(int64_t)(s0 + u) * sml] : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < U; ++u) M = fmaxf(M, t[u]);
-    }
-    float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
     const float* po = p.part_o + qh * DH + d4;
-    for (int s0 = 0; s0 < ns; s0 += U) {
-      float2 t[U];
-      f32x4 v[U];
+    const int64_t sml = nqh * 2, spo = nqh * DH;
+    float M = -INFINITY, L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    // up to eight pieces: every piece's (m, l) and partial output loaded in
+    // one round trip, then the maximum and the sums over the pieces in order
+    auto merge = [&](auto nc) {
+      constexpr int NP = decltype(nc)::value;
+      float2 t[NP];
+      f32x4 v[NP];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int sc = min(s0 + u, ns - 1);  // clamped; pieces past ns get weight 0
-        t[u] = *reinterpret_cast<const float2*>(ml + (int64_t)sc * sml);
-        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)sc * spo);
+      for (int u = 0; u < NP; ++u) {
+        t[u] = *reinterpret_cast<const float2*>(ml + (int64_t)u * sml);
+        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)u * spo);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = (s0 + u >= ns || t[u].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((t[u].x - M) * sl2);
+      for (int u = 0; u < NP; ++u) M = fmaxf(M, t[u].x);
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const float w = t[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((t[u].x - M) * sl2);
         L += w * t[u].y;
         o += w * v[u];
+      }
+    };
+    switch (ns) {
+      case 2: merge(std::integral_constant<int, 2>{}); break;
+      case 3: merge(std::integral_constant<int, 3>{}); break;
+      case 4: merge(std::integral_constant<int, 4>{}); break;
+      case 5: merge(std::integral_constant<int, 5>{}); break;
+      case 6: merge(std::integral_constant<int, 6>{}); break;
+      case 7: merge(std::integral_constant<int, 7>{}); break;
+      case 8: merge(std::integral_constant<int, 8>{}); break;
+      default: {
+        // more pieces: loads in batches of U pieces (independent, in flight
+        // together); the sums still run over the pieces in order
+        constexpr int U = 8;
+        for (int s0 = 0; s0 < ns; s0 += U) {
+          float t[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) t[u] = s0 + u < ns ? ml[(int64_t)(s0 + u) * sml] : -INFINITY;
+#pragma unroll
+          for (int u = 0; u < U; ++u) M = fmaxf(M, t[u]);
+        }
+        for (int s0 = 0; s0 < ns; s0 += U) {
+          float2 t[U];
+          f32x4 v[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int sc = min(s0 + u, ns - 1);  // clamped; pieces past ns get weight 0
+            t[u] = *reinterpret_cast<const float2*>(ml + (int64_t)sc * sml);
+            v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)sc * spo);
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const float w = (s0 + u >= ns || t[u].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((t[u].x - M) * sl2);
+            L += w * t[u].y;
+            o += w * v[u];
+          }
+        }
       }
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
