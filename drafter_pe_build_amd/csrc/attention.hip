@@ -788,15 +788,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, int QPW
     const float L = wave_sum(w * l);
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     for (int dh = lane; dh < DH; dh += 64) {
+      // four sums over the pieces s = c mod 4; the loads of sixteen pieces
+      // are in flight together
       float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+      const float* po = p.part_o + qh * DH + dh;
+      const int64_t spo = nqh * DH;
       int s = 0;
-      for (; s + 4 <= ns; s += 4) {
-        o0 += __shfl(w, s, 64) * p.part_o[((int64_t)s * nqh + qh) * DH + dh];
-        o1 += __shfl(w, s + 1, 64) * p.part_o[((int64_t)(s + 1) * nqh + qh) * DH + dh];
-        o2 += __shfl(w, s + 2, 64) * p.part_o[((int64_t)(s + 2) * nqh + qh) * DH + dh];
-        o3 += __shfl(w, s + 3, 64) * p.part_o[((int64_t)(s + 3) * nqh + qh) * DH + dh];
+      for (; s + 16 <= ns; s += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = po[(int64_t)(s + u) * spo];
+#pragma unroll
+        for (int u = 0; u < 16; u += 4) {
+          o0 += __shfl(w, s + u, 64) * v[u];
+          o1 += __shfl(w, s + u + 1, 64) * v[u + 1];
+          o2 += __shfl(w, s + u + 2, 64) * v[u + 2];
+          o3 += __shfl(w, s + u + 3, 64) * v[u + 3];
+        }
       }
-      for (; s < ns; ++s) o0 += __shfl(w, s, 64) * p.part_o[((int64_t)s * nqh + qh) * DH + dh];
+      for (; s + 4 <= ns; s += 4) {
+        o0 += __shfl(w, s, 64) * po[(int64_t)s * spo];
+        o1 += __shfl(w, s + 1, 64) * po[(int64_t)(s + 1) * spo];
+        o2 += __shfl(w, s + 2, 64) * po[(int64_t)(s + 2) * spo];
+        o3 += __shfl(w, s + 3, 64) * po[(int64_t)(s + 3) * spo];
+      }
+      for (; s < ns; ++s) o0 += __shfl(w, s, 64) * po[(int64_t)s * spo];
       reinterpret_cast<S*>(p.out)[qh * DH + dh] = Storage<S>::from_f32(((o0 + o1) + (o2 + o3)) * inv);
     }
     if (lane == 0 && p.lse) p.lse[qh] = L > 0.f ? M * p.scale + logf(L) : -INFINITY;
